@@ -1,0 +1,457 @@
+/*
+ * zq_ref.c -- plain, slow CPU oracle for the W8A8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library, and the HIP library never
+ * calls it.
+ *
+ * Pages cited (title, then the section used):
+ *   [ZQN]  "[2022 NeurIPS] ZeroQuant: Efficient and Affordable Post-Training
+ *          Quantization for Large-Scale Transformers" (reading notes):
+ *          group-wise weight quantization; token-wise activation quantization;
+ *          the kernel-fusion flowcharts (LN/GeLU + Quantize, GeMM + DeQuantize).
+ *   [T36]  "探秘Transformer系列之（36）--- 大模型量化方案":
+ *          1.1.2 "8位数据类型和量化" (absmax quantization to [-127,127]),
+ *          1.1.2 "逐向量量化" (outer-product denormalisation of an int GEMM),
+ *          1.2.2 "用于激活的按token量化" (dynamic per-token scales; scaling the
+ *          INT32 accumulation before the FP16 write), 1.2.2 "用于权重矩阵的分组量化".
+ *   [IQ]   "Integer Quantization: Deep Dive": "乘加单元" (accumulator initialised
+ *          with the bias), "如何进行量化？" (x_int = clamp(round(x/s + z))),
+ *          "量化模拟" (dequant s*(x_int - z)), "量化误差" (rounding error <= s/2).
+ *   [SQ]   "SmoothQuant技术解析：大模型INT8量化的突破与实践": 2.1 (naive absmax
+ *          quantizer, torch.round), 2.2 (Y = (X diag(s)^-1)(diag(s) W)),
+ *          3.2 (offline: scale and quantize W; online: X diag(s)^-1, quantize).
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - rounding is round-half-to-even (the SQ 2.1 quantizer uses torch.round);
+ *   - the code range is symmetric [-127, 127], zero-point 0;
+ *   - s = fl32(absmax / 127); q = clamp(rne(fl32(y / s)), -127, 127); an
+ *     all-zero token or group gets s = 0 and all codes 0;
+ *   - a weight group is G consecutive output rows by all K input columns;
+ *   - LayerNorm is the textbook affine form with biased variance; GeLU is the
+ *     exact erf form;
+ *   - the bias is added in float after dequantization and before the
+ *     optional GeLU epilogue;
+ *   - the SmoothQuant factor is s_j = sqrt(max_m |LN(X)_mj| / max_n |W_nj|)
+ *     with gamma = 1, beta = 0 for the statistics; s_j = 1 if either max is 0.
+ *
+ * Arithmetic: fp64 everywhere the pages do not fix a precision.  The two
+ * places where float decides an integer (the code q and, through it, the
+ * scale) are taken in fp32, the precision of the stored scale.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ZQREF_OK 0
+#define ZQREF_ERR_ARG 1
+#define ZQREF_ERR_OVERFLOW 2
+
+#define PRE_NONE 0
+#define PRE_LAYERNORM 1
+#define PRE_GELU 2
+#define ACT_NONE 0
+#define ACT_GELU 1
+
+/* ---- IEEE binary16 <-> binary32/64, written from the format definition ---- */
+
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+float zqref_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);               /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);   /* (1 + f/1024) * 2^(e-15) */
+    return (float)(sign ? -v : v);                /* exact: fits in binary32 */
+}
+
+/* One correctly rounded (nearest, ties to even) conversion from binary64. */
+uint16_t zqref_f64_to_f16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v))
+        return 0x7e00;
+    if (a >= 65520.0)                 /* halfway between 65504 and 2^16 rounds up */
+        return sign | 0x7c00;
+    if (a < ldexp(1.0, -14)) {        /* subnormal range: multiples of 2^-24 */
+        double q = nearbyint(ldexp(a, 24));   /* exact scaling, one rounding */
+        return sign | (uint16_t)q;            /* q == 1024 encodes 2^-14 */
+    }
+    int e;
+    frexp(a, &e);                     /* a = m * 2^e, m in [0.5, 1) */
+    e -= 1;                           /* a = m' * 2^e, m' in [1, 2) */
+    double q = nearbyint(ldexp(a, 10 - e));   /* 11-bit significand, in [1024, 2048] */
+    if (q >= 2048.0) {
+        q = 1024.0;
+        e += 1;
+    }
+    if (e > 15)
+        return sign | 0x7c00;
+    return sign | (uint16_t)(((e + 15) << 10) | ((int)q - 1024));
+}
+
+static double load_x(const void *X, int x_is_f16, int64_t idx)
+{
+    if (x_is_f16)
+        return (double)zqref_f16_to_f32(((const uint16_t *)X)[idx]);
+    return (double)((const float *)X)[idx];
+}
+
+/* Exact-erf GeLU in fp64: 0.5 x (1 + erf(x / sqrt 2)). */
+static double gelu64(double x)
+{
+    return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+}
+
+/* ---- Step: the elementwise / reduction op that precedes quantization ---- */
+
+/*
+ * [ZQN] kernel-fusion flowchart: LN/GeLU runs before Quantize.
+ * LayerNorm: mean and biased variance in fp64 (two passes), then
+ * y_k = fl32((x_k - mu) * r * gamma_k + beta_k) with r = 1/sqrt(var + eps).
+ * GeLU: y_k = fl32(gelu(x_k)).  NONE: y_k = x_k.
+ * gamma/beta NULL mean 1 and 0.
+ */
+int zqref_preop(const void *X, int x_is_f16, int64_t M, int64_t K, int pre,
+                const float *gamma, const float *beta, float eps, float *Y)
+{
+    if (!X || !Y || M < 0 || K < 1)
+        return ZQREF_ERR_ARG;
+    if (pre != PRE_NONE && pre != PRE_LAYERNORM && pre != PRE_GELU)
+        return ZQREF_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        const int64_t row = m * K;
+        if (pre == PRE_LAYERNORM) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; k++)
+                sum += load_x(X, x_is_f16, row + k);
+            double mu = sum / (double)K;
+            double ss = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double d = load_x(X, x_is_f16, row + k) - mu;
+                ss += d * d;
+            }
+            double var = ss / (double)K;
+            double r = 1.0 / sqrt(var + (double)eps);
+            for (int64_t k = 0; k < K; k++) {
+                double g = gamma ? (double)gamma[k] : 1.0;
+                double b = beta ? (double)beta[k] : 0.0;
+                Y[row + k] = (float)((load_x(X, x_is_f16, row + k) - mu) * r * g + b);
+            }
+        } else if (pre == PRE_GELU) {
+            for (int64_t k = 0; k < K; k++)
+                Y[row + k] = (float)gelu64(load_x(X, x_is_f16, row + k));
+        } else {
+            for (int64_t k = 0; k < K; k++)
+                Y[row + k] = (float)load_x(X, x_is_f16, row + k);
+        }
+    }
+    return ZQREF_OK;
+}
+
+/* ---- Step: symmetric absmax quantization of one vector ---- */
+
+/*
+ * [T36] 1.1.2 absmax quantization; [IQ] "如何进行量化？" with z = 0.
+ * a = max |v|; s = fl32(a / 127); q = clamp(rne(fl32(v / s)), -127, 127).
+ * Returns s.  a = 0 gives s = 0 and all-zero codes.
+ */
+static float absmax_quantize(const float *v, int64_t n, int8_t *q)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; i++) {
+        float t = fabsf(v[i]);
+        if (t > a)
+            a = t;
+    }
+    float s = a / 127.0f;
+    for (int64_t i = 0; i < n; i++) {
+        if (s == 0.0f) {
+            q[i] = 0;
+            continue;
+        }
+        float t = v[i] / s;                  /* fp32 division, correctly rounded */
+        float r = nearbyintf(t);             /* ties to even (default mode) */
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        q[i] = (int8_t)r;
+    }
+    return s;
+}
+
+/* Quantize each row of Y [M x K] with its own scale (dynamic per-token). */
+int zqref_quantize_rows(const float *Y, int64_t M, int64_t K, int8_t *Xq, float *s_x)
+{
+    if (!Y || !Xq || !s_x || M < 0 || K < 1)
+        return ZQREF_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        s_x[m] = absmax_quantize(Y + m * K, K, Xq + m * K);
+    return ZQREF_OK;
+}
+
+/*
+ * The fused prologue's result: y = preop(x), then per-token quantization
+ * ([T36] 1.2.2 token-wise activation quantization; [ZQN] fused LN/GeLU +
+ * Quantize).  Y_out (optional, [M x K] fp32) receives y.
+ */
+int zqref_prologue(const void *X, int x_is_f16, int64_t M, int64_t K, int pre,
+                   const float *gamma, const float *beta, float eps,
+                   int8_t *Xq, float *s_x, float *Y_out)
+{
+    if (!Xq || !s_x)
+        return ZQREF_ERR_ARG;
+    float *Y = Y_out ? Y_out : (float *)malloc(sizeof(float) * (size_t)(M * K > 0 ? M * K : 1));
+    if (!Y)
+        return ZQREF_ERR_ARG;
+    int rc = zqref_preop(X, x_is_f16, M, K, pre, gamma, beta, eps, Y);
+    if (rc == ZQREF_OK)
+        rc = zqref_quantize_rows(Y, M, K, Xq, s_x);
+    if (!Y_out)
+        free(Y);
+    return rc;
+}
+
+/* ---- Step: group-wise weight quantization (offline) ---- */
+
+/*
+ * [ZQN] group-wise quantization of W; [T36] 1.2.2 group-wise weight
+ * quantization.  Group g = rows [g*G, (g+1)*G) by all K columns; one scale
+ * per group, computed exactly as the per-token scale.
+ */
+int zqref_quantize_groups(const float *W, int64_t N, int64_t K, int64_t G,
+                          int8_t *Wq, float *s_w)
+{
+    if (!W || !Wq || !s_w || N < 1 || K < 1 || G < 1 || N % G)
+        return ZQREF_ERR_ARG;
+    const int64_t ng = N / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < ng; g++)
+        s_w[g] = absmax_quantize(W + g * G * K, G * K, Wq + g * G * K);
+    return ZQREF_OK;
+}
+
+/* ---- Step: SmoothQuant factors and the offline fold ---- */
+
+/*
+ * [SQ] 2.2 / 3.2: s is a per-input-channel vector; the activation side is
+ * divided by s, the weight side multiplied by it.  The statistics use the
+ * linear's actual input LN(X) with gamma = 1, beta = 0:
+ *   a_j = max_m |LN(X)_mj|, w_j = max_n |W_nj|, s_j = fl32(sqrt(a_j / w_j)),
+ * with s_j = 1 when a_j or w_j is 0.  (The square root is the even split of
+ * the range between the two sides.)
+ */
+int zqref_smooth_factors(const void *X, int x_is_f16, int64_t M, int64_t K, float eps,
+                         const float *W, int64_t N, float *s)
+{
+    if (!X || !W || !s || M < 1 || K < 1 || N < 1)
+        return ZQREF_ERR_ARG;
+    float *Y = (float *)malloc(sizeof(float) * (size_t)(M * K));
+    if (!Y)
+        return ZQREF_ERR_ARG;
+    int rc = zqref_preop(X, x_is_f16, M, K, PRE_LAYERNORM, NULL, NULL, eps, Y);
+    if (rc != ZQREF_OK) {
+        free(Y);
+        return rc;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < K; j++) {
+        double a = 0.0, w = 0.0;
+        for (int64_t m = 0; m < M; m++) {
+            double t = fabs((double)Y[m * K + j]);
+            if (t > a) a = t;
+        }
+        for (int64_t n = 0; n < N; n++) {
+            double t = fabs((double)W[n * K + j]);
+            if (t > w) w = t;
+        }
+        s[j] = (a > 0.0 && w > 0.0) ? (float)sqrt(a / w) : 1.0f;
+    }
+    free(Y);
+    return ZQREF_OK;
+}
+
+/* LN(x; gamma/s, beta/s) = LN(x; gamma, beta) / s: the activation side of the fold. */
+int zqref_fold_ln(const float *gamma, const float *beta, const float *s, int64_t K,
+                  float *gamma_out, float *beta_out)
+{
+    if (!s || !gamma_out || !beta_out || K < 1)
+        return ZQREF_ERR_ARG;
+    for (int64_t j = 0; j < K; j++) {
+        double g = gamma ? (double)gamma[j] : 1.0;
+        double b = beta ? (double)beta[j] : 0.0;
+        gamma_out[j] = (float)(g / (double)s[j]);
+        beta_out[j] = (float)(b / (double)s[j]);
+    }
+    return ZQREF_OK;
+}
+
+/* W'_{n,j} = fl32(W_{n,j} * s_j): the weight side of the fold (columns of [N x K]). */
+int zqref_fold_weights(const float *W, const float *s, int64_t N, int64_t K, float *W_out)
+{
+    if (!W || !s || !W_out || N < 1 || K < 1)
+        return ZQREF_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t j = 0; j < K; j++)
+            W_out[n * K + j] = (float)((double)W[n * K + j] * (double)s[j]);
+    return ZQREF_OK;
+}
+
+/* ---- Step: the integer GEMM ---- */
+
+/*
+ * [IQ] "乘加单元": each output accumulates products W_nm * x_m; [T36] 1.2.2:
+ * the INT8 product accumulates in INT32.  acc[m,n] = sum_k Xq[m,k] * Wq[n,k],
+ * exact in int64, then checked to fit int32.
+ */
+int zqref_gemm_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t N, int64_t K,
+                   int32_t *acc)
+{
+    if (!Xq || !Wq || !acc || M < 0 || N < 1 || K < 1)
+        return ZQREF_ERR_ARG;
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            int64_t sum = 0;
+            for (int64_t k = 0; k < K; k++)
+                sum += (int64_t)Xq[m * K + k] * (int64_t)Wq[n * K + k];
+            if (sum > INT32_MAX || sum < INT32_MIN)
+                overflow = 1;
+            acc[m * N + n] = (int32_t)sum;
+        }
+    }
+    return overflow ? ZQREF_ERR_OVERFLOW : ZQREF_OK;
+}
+
+/* ---- Step: dequantization epilogue ---- */
+
+/*
+ * [T36] 1.1.2 vector-wise: the int product is denormalised by the outer
+ * product of the row scales and the column scales; [T36] 1.2.2: the INT32
+ * accumulation is scaled by the activation and weight scales before the
+ * FP16 write; [IQ] "乘加单元": the bias joins the accumulation.
+ *   v = s_x[m] * s_w[n / G] * acc[m,n] + b[n]   (fp64)
+ *   v = gelu(v) if act == GELU                  (fp64)
+ *   Y = fp16(v), one rounding, ties to even.
+ * Y_f64 (optional) receives v before the fp16 rounding.
+ */
+int zqref_epilogue(const int32_t *acc, const float *s_x, const float *s_w, int64_t G,
+                   const float *bias, int act, int64_t M, int64_t N,
+                   uint16_t *Y, double *Y_f64)
+{
+    if (!acc || !s_x || !s_w || !Y || G < 1 || N % G || M < 0 || N < 1)
+        return ZQREF_ERR_ARG;
+    if (act != ACT_NONE && act != ACT_GELU)
+        return ZQREF_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            double v = (double)s_x[m] * (double)s_w[n / G] * (double)acc[m * N + n];
+            if (bias)
+                v += (double)bias[n];
+            if (act == ACT_GELU)
+                v = gelu64(v);
+            if (Y_f64)
+                Y_f64[m * N + n] = v;
+            Y[m * N + n] = zqref_f64_to_f16(v);
+        }
+    }
+    return ZQREF_OK;
+}
+
+/* ---- The whole layer on a subset of tokens ---- */
+
+/*
+ * The fused layer ([ZQN] flowchart after fusion: (LN/GeLU + Quantize) then
+ * (GeMM + DeQuantize)) evaluated for the tokens listed in rows[0..R).
+ * Each token is independent, so a subset gives exactly the rows of the full
+ * result.  Outputs are [R x K] codes, [R] scales and [R x N] fp16.
+ */
+int zqref_linear_rows(const void *X, int x_is_f16, int64_t M, int64_t K, int pre,
+                      const float *gamma, const float *beta, float eps,
+                      const int8_t *Wq, const float *s_w, int64_t G, const float *bias,
+                      int act, int64_t N, const int64_t *rows, int64_t R,
+                      int8_t *Xq_out, float *s_x_out, uint16_t *Y_out)
+{
+    if (!X || !Wq || !s_w || !rows || !Xq_out || !s_x_out || !Y_out || R < 0)
+        return ZQREF_ERR_ARG;
+    for (int64_t r = 0; r < R; r++)
+        if (rows[r] < 0 || rows[r] >= M)
+            return ZQREF_ERR_ARG;
+    const size_t esz = x_is_f16 ? 2 : 4;
+    char *Xs = (char *)malloc(esz * (size_t)(R * K > 0 ? R * K : 1));
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(R * N > 0 ? R * N : 1));
+    if (!Xs || !acc) {
+        free(Xs);
+        free(acc);
+        return ZQREF_ERR_ARG;
+    }
+    for (int64_t r = 0; r < R; r++)
+        memcpy(Xs + esz * (size_t)(r * K), (const char *)X + esz * (size_t)(rows[r] * K), esz * (size_t)K);
+    int rc = zqref_prologue(Xs, x_is_f16, R, K, pre, gamma, beta, eps, Xq_out, s_x_out, NULL);
+    if (rc == ZQREF_OK)
+        rc = zqref_gemm_i32(Xq_out, Wq, R, N, K, acc);
+    if (rc == ZQREF_OK)
+        rc = zqref_epilogue(acc, s_x_out, s_w, G, bias, act, R, N, Y_out, NULL);
+    free(Xs);
+    free(acc);
+    return rc;
+}
+
+/*
+ * The unquantized layer act(preop(X) W^T + b) in fp64, for a subset of
+ * tokens.  Informational only (quantization error with and without the
+ * SmoothQuant fold); it is not what the integer path is compared with.
+ */
+int zqref_linear_float_rows(const void *X, int x_is_f16, int64_t M, int64_t K, int pre,
+                            const float *gamma, const float *beta, float eps,
+                            const float *W, const float *bias, int act, int64_t N,
+                            const int64_t *rows, int64_t R, double *Y_out)
+{
+    if (!X || !W || !rows || !Y_out || R < 0)
+        return ZQREF_ERR_ARG;
+    for (int64_t r = 0; r < R; r++)
+        if (rows[r] < 0 || rows[r] >= M)
+            return ZQREF_ERR_ARG;
+    const size_t esz = x_is_f16 ? 2 : 4;
+    char *Xs = (char *)malloc(esz * (size_t)(R * K > 0 ? R * K : 1));
+    float *Y = (float *)malloc(sizeof(float) * (size_t)(R * K > 0 ? R * K : 1));
+    if (!Xs || !Y) {
+        free(Xs);
+        free(Y);
+        return ZQREF_ERR_ARG;
+    }
+    for (int64_t r = 0; r < R; r++)
+        memcpy(Xs + esz * (size_t)(r * K), (const char *)X + esz * (size_t)(rows[r] * K), esz * (size_t)K);
+    int rc = zqref_preop(Xs, x_is_f16, R, K, pre, gamma, beta, eps, Y);
+    if (rc == ZQREF_OK) {
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < R; r++) {
+            for (int64_t n = 0; n < N; n++) {
+                double v = 0.0;
+                for (int64_t k = 0; k < K; k++)
+                    v += (double)Y[r * K + k] * (double)W[n * K + k];
+                if (bias)
+                    v += (double)bias[n];
+                if (act == ACT_GELU)
+                    v = gelu64(v);
+                Y_out[r * N + n] = v;
+            }
+        }
+    }
+    free(Xs);
+    free(Y);
+    return rc;
+}

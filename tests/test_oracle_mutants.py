@@ -1,0 +1,74 @@
+"""Planted mistakes in copies of the CPU oracle must each fail some pin.
+
+Each mutant replaces one fragment of oracle/zq_ref.c (a dropped term, a wrong
+sign, rounding mode, index or operand), builds the copy with gcc into a
+temporary directory, routes the oracle wrapper through it and runs every
+pin from test_oracle_pins.py.  The test passes when at least one pin fails.
+Everything here runs on the CPU.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+import pytest
+
+from oracle import build as obuild
+from oracle import ref
+from tests import test_oracle_pins as pins
+
+MUTANTS = {
+    "round_half_away": ("float r = nearbyintf(t);", "float r = roundf(t);"),
+    "scale_over_128": ("float s = a / 127.0f;", "float s = a / 128.0f;"),
+    "unbiased_variance": ("double var = ss / (double)K;", "double var = ss / (double)(K - 1);"),
+    "eps_dropped": ("double r = 1.0 / sqrt(var + (double)eps);", "double r = 1.0 / sqrt(var);"),
+    "beta_sign": ("* r * g + b);", "* r * g - b);"),
+    "gelu_wrong_scale": ("return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));",
+                         "return 0.5 * x * (1.0 + erf(x / 2.0));"),
+    "gemm_transposed_w": ("(int64_t)Wq[n * K + k]", "(int64_t)Wq[k * N + n]"),
+    "group_index_modulo": ("(double)s_w[n / G]", "(double)s_w[n % (N / G)]"),
+    "bias_dropped": ("                v += (double)bias[n];\n            if (act == ACT_GELU)\n                v = gelu64(v);\n            if (Y_f64)",
+                     "                v += 0.0;\n            if (act == ACT_GELU)\n                v = gelu64(v);\n            if (Y_f64)"),
+    "fp16_truncates": ("double q = nearbyint(ldexp(a, 10 - e));", "double q = floor(ldexp(a, 10 - e));"),
+    "smooth_inverted": ("(float)sqrt(a / w)", "(float)sqrt(w / a)"),
+    "fold_weight_divides": ("(double)W[n * K + j] * (double)s[j]", "(double)W[n * K + j] / (double)s[j]"),
+    "group_absmax_first_row": ("s_w[g] = absmax_quantize(W + g * G * K, G * K, Wq + g * G * K);",
+                               "{ s_w[g] = absmax_quantize(W + g * G * K, K, Wq + g * G * K);\n"
+                               "        for (int64_t i = K; i < G * K; i++) {\n"
+                               "            float t = nearbyintf(W[g * G * K + i] / s_w[g]);\n"
+                               "            Wq[g * G * K + i] = (int8_t)(t > 127 ? 127 : t < -127 ? -127 : t);\n"
+                               "        } }"),
+}
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(obuild.SRC, encoding="utf-8").read()
+    assert src.count(old) == 1, f"mutant {name}: fragment not found exactly once"
+    mpath = tmp_path / f"{name}.c"
+    mpath.write_text(src.replace(old, new), encoding="utf-8")
+    lib = tmp_path / f"lib_{name}.so"
+    subprocess.run(["gcc", *obuild.CFLAGS, str(mpath), "-o", str(lib), "-lm"], check=True,
+                   capture_output=True)
+    return str(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    lib = _build_mutant(tmp_path, name, old, new)
+    caught = []
+    with ref.using_library(lib):
+        for pin in pins.ALL_PINS:
+            try:
+                pin()
+            except (AssertionError, ref.OracleError):
+                caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
+
+
+def test_pins_pass_on_unmodified_copy(tmp_path):
+    """The same machinery on an unmodified copy catches nothing."""
+    lib = _build_mutant(tmp_path, "identity", "#include <math.h>", "#include <math.h>")
+    with ref.using_library(lib):
+        for pin in pins.ALL_PINS:
+            pin()

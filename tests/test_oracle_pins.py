@@ -1,0 +1,332 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each `pin_*` function raises AssertionError when the oracle disagrees with a
+hand-worked example (tests/golden), a closed form, an invariant, a library
+routine that the case reduces to, or brute force.  The tests below run every
+pin against the oracle; test_oracle_mutants.py runs them against copies of
+the oracle with planted mistakes and checks that each mistake is caught.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import brute, ref
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line
+
+
+def _golden_kv(name):
+    out = {}
+    for line in _golden_lines(name):
+        k, v = line.split(":", 1)
+        out[k.strip()] = [float(t) for t in v.split()]
+    return out
+
+
+# --------------------------------------------------------------------------
+# Hand-worked examples (tests/golden, each file cites its passage)
+# --------------------------------------------------------------------------
+
+def pin_golden_absmax():
+    for line in _golden_lines("absmax_quantize.txt"):
+        xs, s, qs = (p.strip() for p in line.split("|"))
+        x = np.array([[float(t) for t in xs.split()]], dtype=np.float32)
+        q, sc = ref.quantize_rows(x)
+        assert sc[0] == np.float32(float(s)), (line, sc)
+        assert q[0].tolist() == [int(t) for t in qs.split()], (line, q)
+
+
+def pin_golden_layernorm():
+    for line in _golden_lines("layernorm_quantize.txt"):
+        xs, qs = (p.strip() for p in line.split("|"))
+        x = np.array([[float(t) for t in xs.split()]], dtype=np.float32)
+        q, _ = ref.prologue(x, ref.PRE_LAYERNORM, eps=0.0)
+        assert q[0].tolist() == [int(t) for t in qs.split()], (line, q)
+
+
+def pin_golden_gelu():
+    for line in _golden_lines("gelu_values.txt"):
+        xs, ys = (p.strip() for p in line.split("|"))
+        y = ref.preop(np.array([[float(xs)]], dtype=np.float32), ref.PRE_GELU)[0, 0]
+        assert abs(float(y) - float(ys)) <= 1e-7 * max(1.0, abs(float(ys))), (line, y)
+
+
+def pin_golden_fp16():
+    for line in _golden_lines("fp16_rounding.txt"):
+        vs, hs = (p.strip() for p in line.split("|"))
+        got = int(ref.f64_to_f16_bits([float(vs)])[0])
+        assert got == int(hs, 16), (line, hex(got))
+
+
+def pin_golden_linear_integer():
+    g = _golden_kv("linear_integer.txt")
+    X = np.array([g["x"]], dtype=np.float32)
+    W = np.array([g["w0"], g["w1"]], dtype=np.float32)
+    bias = np.array(g["bias"], dtype=np.float32)
+    Wq, s_w = ref.quantize_groups(W, 2)
+    assert s_w.tolist() == [1.0]
+    assert np.array_equal(Wq, W.astype(np.int8))
+    Y, Xq, s_x = ref.linear(X, ref.PRE_NONE, None, None, 1e-5, Wq, s_w, 2, bias, ref.ACT_NONE)
+    assert s_x.tolist() == [1.0]
+    assert ref.gemm_i32(Xq, Wq)[0].tolist() == [int(v) for v in g["acc"]]
+    assert Y.astype(np.float64)[0].tolist() == g["y"], Y
+
+
+def pin_golden_smooth():
+    g = _golden_kv("smooth_factors.txt")
+    X = np.array([g["x0"], g["x1"]], dtype=np.float32)
+    W = np.array([g["w0"]], dtype=np.float32)
+    s = ref.smooth_factors(X, W, eps=0.0)
+    np.testing.assert_allclose(s, g["s"], rtol=2e-7)
+
+
+# --------------------------------------------------------------------------
+# Format facts, brute force and library routines
+# --------------------------------------------------------------------------
+
+def pin_fp16_matches_numpy():
+    """One RNE rounding binary64 -> binary16, against numpy's own conversion,
+    on random values across the range and on exact midpoints."""
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.standard_normal(3000) * 10.0 ** rng.integers(-9, 6, 3000),
+        # exact midpoints between consecutive fp16 values (ties)
+        (np.arange(-2000, 2000, dtype=np.float64) + 0.5) * 2.0 ** -24,
+        (np.arange(1024, 2048, dtype=np.float64) + 0.5) * 2.0 ** -10,
+        (np.arange(1024, 2048, dtype=np.float64) + 0.5) * 2.0 ** 5,
+    ])
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float16).view(np.uint16)
+    got = ref.f64_to_f16_bits(v)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(v[i], hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def pin_f16_decode_all_codes():
+    h = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    want = h.view(np.float16).astype(np.float32)
+    got = ref.f16_bits_to_f32(h)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+    assert np.array_equal(np.signbit(got[~np.isnan(got)]), np.signbit(want[~np.isnan(want)]))
+
+
+def _brute_case(seed, M, K, N, G, pre, act, x_dtype, affine, with_bias):
+    rng = np.random.default_rng(seed)
+    X = (rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))).astype(x_dtype)
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    gamma = beta = None
+    if affine:
+        gamma = (1 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+        beta = (0.1 * rng.standard_normal(K)).astype(np.float32)
+    bias = (0.01 * rng.standard_normal(N)).astype(np.float32) if with_bias else None
+    return X, W, gamma, beta, bias
+
+
+BRUTE_CASES = [
+    # seed, M, K, N, G, pre, act, x dtype, affine LN, bias
+    (0, 3, 16, 4, 2, ref.PRE_LAYERNORM, ref.ACT_NONE, np.float32, False, True),
+    (1, 4, 32, 6, 3, ref.PRE_LAYERNORM, ref.ACT_GELU, np.float16, True, True),
+    (2, 2, 48, 4, 4, ref.PRE_GELU, ref.ACT_NONE, np.float16, False, False),
+    (3, 5, 16, 8, 1, ref.PRE_NONE, ref.ACT_GELU, np.float32, False, True),
+    (4, 1, 64, 2, 2, ref.PRE_LAYERNORM, ref.ACT_NONE, np.float16, True, False),
+]
+
+
+def pin_brute_force():
+    """The C oracle and the pure-Python brute force agree bit for bit on
+    codes, scales and accumulators, and on the fp16 output."""
+    for seed, M, K, N, G, pre, act, dt, affine, with_bias in BRUTE_CASES:
+        X, W, gamma, beta, bias = _brute_case(seed, M, K, N, G, pre, act, dt, affine, with_bias)
+        bq, bs, bwq, bsw, bacc, bY = brute.linear(X, pre, gamma, beta, 1e-5, W, G, bias, act)
+        Wq, s_w = ref.quantize_groups(W, G)
+        Xq, s_x = ref.prologue(X, pre, gamma, beta, 1e-5)
+        acc = ref.gemm_i32(Xq, Wq)
+        Y = ref.epilogue(acc, s_x, s_w, G, bias, act)
+        assert np.array_equal(Xq, bq) and np.array_equal(s_x, bs), seed
+        assert np.array_equal(Wq, bwq) and np.array_equal(s_w, bsw), seed
+        assert np.array_equal(acc.astype(np.int64), bacc), seed
+        assert np.array_equal(Y.view(np.uint16), bY.view(np.uint16)), seed
+
+
+def pin_layernorm_matches_torch():
+    """LayerNorm reduces to torch.nn.functional.layer_norm evaluated in fp64."""
+    import torch
+    rng = np.random.default_rng(5)
+    for K, affine in [(256, False), (768, True), (1000, True)]:
+        X = (rng.standard_normal((8, K)) * np.exp(rng.standard_normal((8, 1)))).astype(np.float32)
+        g = (1 + 0.1 * rng.standard_normal(K)).astype(np.float32) if affine else None
+        b = (0.1 * rng.standard_normal(K)).astype(np.float32) if affine else None
+        want = torch.nn.functional.layer_norm(
+            torch.from_numpy(X.astype(np.float64)), (K,),
+            None if g is None else torch.from_numpy(g.astype(np.float64)),
+            None if b is None else torch.from_numpy(b.astype(np.float64)), eps=1e-5).numpy()
+        got = ref.preop(X, ref.PRE_LAYERNORM, g, b, 1e-5).astype(np.float64)
+        ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - want) <= ulp), np.max(np.abs(got - want) / ulp)
+
+
+def pin_gelu_matches_torch():
+    """GeLU reduces to torch.nn.functional.gelu(approximate='none') in fp64."""
+    import torch
+    rng = np.random.default_rng(6)
+    X = (3.0 * rng.standard_normal((4, 512))).astype(np.float32)
+    want = torch.nn.functional.gelu(torch.from_numpy(X.astype(np.float64)), approximate="none").numpy()
+    got = ref.preop(X, ref.PRE_GELU).astype(np.float64)
+    ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - want) <= ulp + 1e-30)
+
+
+# --------------------------------------------------------------------------
+# Closed forms and invariants
+# --------------------------------------------------------------------------
+
+def pin_rounding_error_bound():
+    """|y - s q| <= s/2 up to the fp32 rounding of y/s, and no clipping:
+    absmax scaling covers the range, so each nonzero row has a code of +-127."""
+    rng = np.random.default_rng(7)
+    Y = (rng.standard_normal((64, 300)) * np.exp(2 * rng.standard_normal((64, 1)))).astype(np.float32)
+    q, s = ref.quantize_rows(Y)
+    err = np.abs(Y.astype(np.float64) - s[:, None].astype(np.float64) * q)
+    assert np.all(err <= s[:, None] * (0.5 + 2.0 ** -17))
+    assert np.all(np.max(np.abs(q.astype(np.int32)), axis=1) == 127)
+    a = np.max(np.abs(Y), axis=1)
+    assert np.array_equal(s, (a / np.float32(127)).astype(np.float32))
+
+
+def pin_power_of_two_scaling():
+    """Scaling a token by 2^k scales s by 2^k and leaves codes unchanged;
+    LayerNorm with eps = 0 removes the factor exactly."""
+    rng = np.random.default_rng(8)
+    Y = rng.standard_normal((16, 96)).astype(np.float32)
+    q1, s1 = ref.quantize_rows(Y)
+    q2, s2 = ref.quantize_rows(Y * np.float32(2.0 ** 7))
+    assert np.array_equal(q1, q2) and np.array_equal(s2, s1 * np.float32(2.0 ** 7))
+    l1, _ = ref.prologue(Y, ref.PRE_LAYERNORM, eps=0.0)
+    l2, _ = ref.prologue(Y * np.float32(2.0 ** -5), ref.PRE_LAYERNORM, eps=0.0)
+    assert np.array_equal(l1, l2)
+
+
+def _numpy_absmax(v: np.ndarray, axis):
+    a = np.max(np.abs(v), axis=axis, keepdims=True)
+    s = (a / np.float32(127)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.clip(np.rint(v / s), -127, 127), 0).astype(np.int8)
+    return q, s
+
+
+def pin_group_special_cases():
+    """G = N is per-tensor quantization; G = 1 is per-row (vector-wise)
+    quantization; an intermediate G takes each block of G output rows."""
+    rng = np.random.default_rng(9)
+    W = (0.02 * rng.standard_normal((12, 40)) * np.exp(rng.standard_normal((12, 1)))).astype(np.float32)
+    q, s = ref.quantize_groups(W, 12)
+    qt, st = _numpy_absmax(W, None)
+    assert np.array_equal(q, qt) and s[0] == st.ravel()[0]
+    q, s = ref.quantize_groups(W, 1)
+    qr, sr = _numpy_absmax(W, 1)
+    assert np.array_equal(q, qr) and np.array_equal(s, sr.ravel())
+    q, s = ref.quantize_groups(W, 4)
+    for g in range(3):
+        qg, sg = _numpy_absmax(W[4 * g:4 * g + 4], None)
+        assert np.array_equal(q[4 * g:4 * g + 4], qg) and s[g] == sg.ravel()[0]
+
+
+def pin_gemm_exact():
+    """The int GEMM equals numpy's int64 matmul (non-square, so a transposed
+    operand shows), and overflow past int32 is reported."""
+    rng = np.random.default_rng(10)
+    Xq = rng.integers(-127, 128, (9, 200)).astype(np.int8)
+    Wq = rng.integers(-127, 128, (13, 200)).astype(np.int8)
+    acc = ref.gemm_i32(Xq, Wq)
+    assert np.array_equal(acc.astype(np.int64), Xq.astype(np.int64) @ Wq.astype(np.int64).T)
+    big = np.full((1, 140000), 127, dtype=np.int8)
+    try:
+        ref.gemm_i32(big, big)
+    except ref.OracleError:
+        pass
+    else:
+        raise AssertionError("int32 overflow not reported")
+
+
+def pin_epilogue_outer_product():
+    """v = s_x[m] s_w[n // G] acc + b equals the fake-quant form
+    sum_k (s_x q)(s_w w) + b, and Y is v rounded once to fp16."""
+    rng = np.random.default_rng(11)
+    M, N, K, G = 6, 512, 64, 128
+    Xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    Wq = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    s_x = np.exp(rng.standard_normal(M)).astype(np.float32) * np.float32(0.01)
+    s_w = np.exp(rng.standard_normal(N // G)).astype(np.float32) * np.float32(1e-3)
+    bias = (0.01 * rng.standard_normal(N)).astype(np.float32)
+    acc = ref.gemm_i32(Xq, Wq)
+    for act in (ref.ACT_NONE, ref.ACT_GELU):
+        Y, Y64 = ref.epilogue(acc, s_x, s_w, G, bias, act, return_f64=True)
+        fq = (s_x[:, None].astype(np.float64) * Xq) @ (np.repeat(s_w, G)[:, None].astype(np.float64) * Wq).T
+        v = fq + bias.astype(np.float64)
+        if act == ref.ACT_GELU:
+            v = 0.5 * v * (1.0 + np.vectorize(math.erf)(v / math.sqrt(2.0)))
+        np.testing.assert_allclose(Y64, v, rtol=1e-12, atol=1e-15)
+        assert np.array_equal(Y.view(np.uint16), Y64.astype(np.float16).view(np.uint16))
+
+
+def pin_zero_token():
+    """An all-zero token (pre-op NONE) gets scale 0, codes 0 and output = bias."""
+    X = np.zeros((2, 32), dtype=np.float32)
+    X[1, 3] = 1.0
+    Xq, s_x = ref.prologue(X, ref.PRE_NONE)
+    assert s_x[0] == 0 and not Xq[0].any() and s_x[1] > 0
+    Wq = np.ones((2, 32), dtype=np.int8)
+    bias = np.array([0.25, -0.5], dtype=np.float32)
+    Y = ref.epilogue(ref.gemm_i32(Xq, Wq), s_x, np.array([1.0], np.float32), 2, bias)
+    assert Y[0].astype(np.float32).tolist() == [0.25, -0.5]
+
+
+def pin_smoothquant_identity():
+    """(X diag(s)^-1)(diag(s) W) = X W to 1e-5 relative (max norm) with the
+    factors rounded to fp32; after the fold each channel's activation and
+    weight maxima are both sqrt(a_j w_j); LN with gamma/s, beta/s is LN / s."""
+    rng = np.random.default_rng(12)
+    M, K, N = 64, 128, 96
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    X[:, [5, 77]] *= np.float32(100.0)
+    X = X.astype(np.float16)
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    s = ref.smooth_factors(X, W)
+    Xt = ref.preop(X, ref.PRE_LAYERNORM)
+    Xh = (Xt / s).astype(np.float32)
+    Wh = ref.fold_weights(W, s)
+    Y0 = Xt.astype(np.float64) @ W.astype(np.float64).T
+    Y1 = Xh.astype(np.float64) @ Wh.astype(np.float64).T
+    assert np.max(np.abs(Y1 - Y0)) <= 1e-5 * np.max(np.abs(Y0))
+    a = np.max(np.abs(Xt), axis=0).astype(np.float64)
+    w = np.max(np.abs(W), axis=0).astype(np.float64)
+    target = np.sqrt(a * w)
+    np.testing.assert_allclose(np.max(np.abs(Xh), axis=0), target, rtol=1e-6)
+    np.testing.assert_allclose(np.max(np.abs(Wh), axis=0), target, rtol=1e-6)
+    gamma = (1 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(K)).astype(np.float32)
+    g2, b2 = ref.fold_ln(gamma, beta, s)
+    lhs = ref.preop(X, ref.PRE_LAYERNORM, g2, b2).astype(np.float64)
+    rhs = ref.preop(X, ref.PRE_LAYERNORM, gamma, beta).astype(np.float64) / s
+    assert np.max(np.abs(lhs - rhs)) <= 1e-6 * np.max(np.abs(rhs))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(pin):
+    pin()
