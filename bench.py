@@ -1,0 +1,305 @@
+"""Benchmark of the W8A8 linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the per-token hot path over one batch: the fused
+LayerNorm/GeLU + per-token quantization kernel, then the int8 MFMA GEMM with
+the fused dequant (+bias, +GeLU) epilogue, through zq_linear_w8a8.  Weights
+are quantized offline (by the library) before timing, as the method
+prescribes.  Inputs are seeded synthetic data resident in HBM; several
+independent input/weight/output sets are rotated so that the 256 MB
+Infinity Cache cannot serve a step from the previous one.
+
+The steps are captured in a HIP graph (on torch's stream, which is the
+stream the library launches on) so that host-side call overhead does not
+leave the GPU idle between the ~10 us layers; the timed region is one replay
+of a graph of exactly K steps, bracketed by device synchronisations.
+
+Printed: ONE JSON line with the throughput (TOPS for prefill workloads, GB/s
+for the decode workload), the dominant kernel's roofline figures measured
+with HIP events, and the CPU oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W8A8 fused linear TOPS (% int8 MFMA peak) prefill; GB/s (% HBM) decode"
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+PRE_NAMES = {0: "none", 1: "layernorm", 2: "gelu"}
+ACT_NAMES = {0: "none", 1: "gelu"}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="bert_ffn_up")
+    ap.add_argument("--rotate-mb", type=float, default=600.0,
+                    help="total bytes of the rotated input sets (beyond the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=5.0,
+                    help="repeat full oracle passes until this much wall time has passed")
+    ap.add_argument("--calib-copy-mb", type=float, default=0.0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "post_w8a8_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def graph_of(torch, fn, n):
+    """Capture n calls fn(i) into one graph (after two eager warm calls on a side stream)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+        fn(1 % max(n, 1))
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g):
+    """Milliseconds for one replay, bracketed by device synchronisations."""
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return e0.elapsed_time(e1), wall
+
+
+def calib_copy(torch, mb):
+    n = int(mb * 1024 * 1024)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n, "launches": 5}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import post_w8a8_quantized_amd as zq
+    from zq_workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    zq.library()
+    if args.calib_copy_mb > 0:
+        calib_copy(torch, args.calib_copy_mb)
+        return
+
+    w = WORKLOADS[args.workload]
+    decode = w.M <= 32
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    Xd = torch.from_numpy(inp.X).to(dev)
+    Wd = torch.from_numpy(inp.W).to(dev)
+    gamma = torch.from_numpy(inp.gamma).to(dev)
+    beta = torch.from_numpy(inp.beta).to(dev)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
+
+    # ---- offline (untimed): SmoothQuant fold and group-wise weight quantization
+    smooth = None
+    if w.smooth:
+        smooth, gamma, beta = zq.smoothquant_factors(Xd, Wd, w.eps, gamma, beta)
+    Wq, s_w = zq.quantize_weights_grouped(Wd, w.group_rows, smooth)
+    del Wd
+    torch.cuda.synchronize()
+    g_arg = gamma if w.pre == zq.PRE_LAYERNORM else None
+    b_arg = beta if w.pre == zq.PRE_LAYERNORM else None
+
+    # ---- rotated sets
+    M, N, K, G = w.M, w.N, w.K, w.group_rows
+    ws_bytes = zq.linear_workspace_bytes(M, K)
+    x_el = 2 if w.x_dtype == "f16" else 4
+    set_bytes = M * K * x_el + N * K + M * N * 2 + ws_bytes + 4 * N // G
+    nsets = max(2, math.ceil(args.rotate_mb * 1e6 / set_bytes))
+    sets = []
+    for i in range(nsets):
+        sets.append(dict(
+            X=Xd if i == 0 else Xd.clone(),
+            Wq=Wq if i == 0 else Wq.clone(),
+            s_w=s_w if i == 0 else s_w.clone(),
+            ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
+            Y=torch.empty((M, N), dtype=torch.float16, device=dev),
+        ))
+    xq_off = 0
+    sx_off = (M * K + 255) // 256 * 256
+
+    def layer(i):
+        s = sets[i % nsets]
+        zq.linear_w8a8(s["X"], s["Wq"], s["s_w"], G, w.pre, g_arg, b_arg, w.eps, bias, w.act,
+                       workspace=s["ws"], out=s["Y"])
+
+    def prologue(i):
+        s = sets[i % nsets]
+        xq = s["ws"][xq_off:xq_off + M * K].view(torch.int8).view(M, K)
+        sx = s["ws"][sx_off:sx_off + 4 * M].view(torch.float32)
+        zq.ln_quant_per_token(s["X"], w.pre, g_arg, b_arg, w.eps, out=(xq, sx))
+
+    def gemm(i):
+        s = sets[i % nsets]
+        xq = s["ws"][xq_off:xq_off + M * K].view(torch.int8).view(M, K)
+        sx = s["ws"][sx_off:sx_off + 4 * M].view(torch.float32)
+        zq.w8a8_gemm_dequant(xq, sx, s["Wq"], s["s_w"], G, bias, w.act, out=s["Y"])
+
+    # eager pass over every set (fills every workspace with valid codes)
+    for i in range(nsets):
+        layer(i)
+    torch.cuda.synchronize()
+
+    # ---- timed layer steps
+    g_warm = graph_of(torch, layer, max(args.warmup, 1))
+    g_steps = graph_of(torch, layer, args.steps)
+    time_graph(torch, g_warm)
+    ms_ev, ms_wall = time_graph(torch, g_steps)
+    ms_step = ms_ev / args.steps
+
+    # ---- per-kernel averages over graphs of the same launches (HIP events)
+    g_pro = graph_of(torch, prologue, args.steps)
+    g_gemm = graph_of(torch, gemm, args.steps)
+    time_graph(torch, g_pro)
+    time_graph(torch, g_gemm)
+    pro_ms = time_graph(torch, g_pro)[0] / args.steps
+    gemm_ms = time_graph(torch, g_gemm)[0] / args.steps
+    del g_warm, g_steps, g_pro, g_gemm
+    torch.cuda.synchronize()
+
+    ops = 2.0 * M * N * K
+    bytes_pro = M * K * x_el + M * K + 4 * M
+    bytes_gemm = M * K + 4 * M + N * K + 4 * (N // G) + (4 * N if bias is not None else 0) + 2 * M * N
+    bytes_layer = bytes_pro + bytes_gemm
+    gemm_kernel = "gemm_skinny" if decode else "gemm_tiled"
+    src_hash = kernel_source_hash([f"{gemm_kernel}.hip", "zq_device.h"])
+    traffic = read_traffic(gemm_kernel, w.name, src_hash)
+
+    if decode:
+        value = bytes_layer / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+        g_ach = bytes_gemm / (gemm_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(g_ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(g_ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "kernel": gemm_kernel, "avg_launch_us": round(gemm_ms * 1e3, 3),
+                    "algorithmic_bytes_per_launch": bytes_gemm}
+    else:
+        value = ops / (ms_step * 1e-3) / 1e12
+        unit = "TOPS"
+        g_ach = ops / (gemm_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(g_ach, 1), "peak": PEAK_INT8_TOPS,
+                    "unit": "TOP/s", "frac": round(g_ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                    "kernel": gemm_kernel, "avg_launch_us": round(gemm_ms * 1e3, 3),
+                    "algorithmic_ops_per_launch": ops}
+
+    # ---- CPU oracle on the host cores (a reported baseline, not the target)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ref
+        Wq_h, sw_h = ref.quantize_groups(
+            ref.fold_weights(inp.W, smooth.cpu().numpy()) if smooth is not None else inp.W, G)
+        g_h = gamma.cpu().numpy() if w.pre == 1 else None
+        b_h = beta.cpu().numpy() if w.pre == 1 else None
+        rows = np.arange(M, dtype=np.int64)
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            ref.linear_rows(inp.X, w.pre, g_h, b_h, w.eps, Wq_h, sw_h, G, inp.bias, w.act, rows)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        per = el / passes
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        cpu = {"value": round((bytes_layer / per / 1e9) if decode else (ops / per / 1e12), 4),
+               "unit": unit, "cores": cores, "kind": "oracle",
+               "sample": f"all {M} tokens of the workload (prologue + int GEMM + epilogue), "
+                         f"{passes} passes, {per:.3f} s each"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "K": K, "N": N, "group_rows": G,
+                   "x_dtype": w.x_dtype, "pre": PRE_NAMES[w.pre], "act": ACT_NAMES[w.act],
+                   "bias": bias is not None, "smoothquant": w.smooth,
+                   "rotated_sets": nsets, "graph_steps": args.steps},
+        "frac_of_peak": round(value / (PEAK_HBM_GBS if decode else PEAK_INT8_TOPS), 4),
+        "breakdown_us": {"layer_step": round(ms_step * 1e3, 3), "prologue": round(pro_ms * 1e3, 3),
+                         "gemm": round(gemm_ms * 1e3, 3),
+                         "prologue_GBps": round(bytes_pro / (pro_ms * 1e-3) / 1e9, 1),
+                         "timed_region_wall_ms": round(ms_wall, 3)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * zq.h -- C ABI of libzq: ZeroQuant-style W8A8 inference for one linear layer
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, then section):
+ *   [ZQN] "[2022 NeurIPS] ZeroQuant: Efficient and Affordable Post-Training
+ *         Quantization for Large-Scale Transformers" (reading notes): group-wise
+ *         weight quantization; token-wise activation quantization; the
+ *         kernel-fusion flowcharts ("LN/GeLU + Quantize" then "GeMM + DeQuantize").
+ *   [T36] "探秘Transformer系列之（36）--- 大模型量化方案": 1.1.2 absmax quantization
+ *         and vector-wise (outer-product) denormalisation; 1.2.2 token-wise
+ *         activation quantization fused with the preceding LayerNorm, INT32
+ *         accumulation scaled by both scales before the FP16 write, group-wise
+ *         weight quantization; 1.3 granularity (scales only along the outer
+ *         dimensions of an INT8 GEMM).
+ *   [IQ]  "Integer Quantization: Deep Dive": MAC unit (accumulator plus bias);
+ *         quantize / dequantize formulas with zero-point z = 0 here.
+ *   [SQ]  "SmoothQuant技术解析：大模型INT8量化的突破与实践": 2.2 the smoothing
+ *         identity Y = (X diag(s)^-1)(diag(s) W); 3.2 offline weight scaling and
+ *         quantization, online activation division and quantization.
+ *
+ * Conventions for every call
+ *   - Data pointers are DEVICE pointers owned by the caller; the library keeps
+ *     no reference after the call returns and allocates no memory.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default stream);
+ *     results are ready when the stream is synchronised.
+ *   - Matrices are row-major and dense: X [M x K], Xq [M x K], W / Wq [N x K]
+ *     (output rows, input columns, so both GEMM operands are K-contiguous),
+ *     Y [M x N].  M = tokens, K = input features, N = output features.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and a non-zero zq_status is returned.  A
+ *     launch failure reported by the HIP runtime returns ZQ_ERR_HIP.  Faults
+ *     during execution surface at the caller's next synchronisation.
+ *   - Calls never abort and never throw.  The library keeps no mutable global
+ *     state: calls are reentrant; calls on different streams that write the
+ *     same buffers race, as any two kernels would.
+ *   - Quantization is symmetric absmax: s = fl32(max|v| / 127),
+ *     q = clamp(round_half_even(fl32(v / s)), -127, 127), and an all-zero
+ *     vector gets s = 0 with all codes 0 ([T36] 1.1.2; [IQ] with z = 0).
+ */
+#ifndef ZQ_H
+#define ZQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum zq_status {
+    ZQ_OK = 0,
+    ZQ_ERR_NULL = 1,        /* a required pointer is NULL */
+    ZQ_ERR_SHAPE = 2,       /* a size is out of range or not a required multiple */
+    ZQ_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+    ZQ_ERR_DTYPE = 4,       /* a dtype / op enum is not one this argument accepts */
+    ZQ_ERR_WORKSPACE = 5,   /* the workspace is NULL or smaller than required */
+    ZQ_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+    ZQ_ERR_UNSUPPORTED = 7  /* a valid request this build does not implement */
+} zq_status;
+
+typedef enum zq_dtype {
+    ZQ_F32 = 0,
+    ZQ_F16 = 1,
+    ZQ_I8 = 2,
+    ZQ_I32 = 3
+} zq_dtype;
+
+/* The op fused in front of the per-token quantizer ([ZQN] flowchart). */
+typedef enum zq_pre {
+    ZQ_PRE_NONE = 0,
+    ZQ_PRE_LAYERNORM = 1,   /* y = (x - mean) / sqrt(var + eps) * gamma + beta, biased var */
+    ZQ_PRE_GELU = 2         /* y = x * Phi(x), the exact (erf) GeLU */
+} zq_pre;
+
+/* The op fused after the dequantization in the GEMM epilogue. */
+typedef enum zq_act {
+    ZQ_ACT_NONE = 0,
+    ZQ_ACT_GELU = 1
+} zq_act;
+
+/* Which GEMM kernel zq_w8a8_gemm_dequant_ex runs. */
+typedef enum zq_gemm_path {
+    ZQ_PATH_AUTO = 0,       /* skinny kernel for M <= 32, tiled MFMA kernel otherwise */
+    ZQ_PATH_TILED = 1,      /* LDS-tiled MFMA kernel (prefill shapes), any M */
+    ZQ_PATH_SKINNY = 2      /* weight-streaming kernel (decode shapes), M <= 32 only */
+} zq_gemm_path;
+
+/* Largest K accepted: with codes in [-127, 127], |acc| <= 16129 K < 2^31. */
+#define ZQ_MAX_K 131072
+
+/*
+ * zq_quantize_weights_grouped -- offline group-wise weight quantization.
+ * [ZQN] group-wise weight quantization; [T36] 1.2.2 "用于权重矩阵的分组量化";
+ * [SQ] 3.2 (weights are scaled by s, then quantized, offline).
+ *
+ *   W         [N x K], w_dtype ZQ_F32 or ZQ_F16, 16-byte aligned.
+ *   smooth    [K] fp32 or NULL.  If given, the quantized matrix is
+ *             W'[n, j] = fl32(W[n, j] * smooth[j]) (the weight side of the
+ *             SmoothQuant fold); otherwise W' = W.
+ *   group_rows G: group g is rows [g G, (g+1) G) by all K columns.
+ *   Wq        [N x K] int8 out, 16-byte aligned.
+ *   w_scales  [N / G] fp32 out: s_w[g] = fl32(max |W'| over the group / 127).
+ *             The call also uses this array as its reduction scratch.
+ * Requires N >= 1, 1 <= K <= ZQ_MAX_K, K % 16 == 0, G >= 1, N % G == 0.
+ * W' must be finite.
+ */
+zq_status zq_quantize_weights_grouped(const void *W, zq_dtype w_dtype, const float *smooth,
+                                      int64_t N, int64_t K, int64_t group_rows,
+                                      int8_t *Wq, float *w_scales, hipStream_t stream);
+
+/*
+ * zq_ln_quant_per_token -- the fused prologue: LayerNorm or GeLU (or nothing)
+ * in fp32 registers, then dynamic per-token absmax quantization.
+ * [ZQN] kernel fusion "LN/GeLU + Quantize"; [T36] 1.2.2 token-wise
+ * quantization with run-time ranges, fused with the preceding LayerNorm.
+ *
+ *   X         [M x K], x_dtype ZQ_F16 or ZQ_F32, 16-byte aligned.
+ *   pre       ZQ_PRE_NONE / ZQ_PRE_LAYERNORM / ZQ_PRE_GELU.
+ *   gamma, beta [K] fp32, used only for ZQ_PRE_LAYERNORM; NULL means 1 / 0.
+ *   eps       LayerNorm epsilon (e.g. 1e-5).
+ *   Xq        [M x K] int8 out, 16-byte aligned.
+ *   x_scales  [M] fp32 out: s_x[m] = fl32(max_k |y[m, k]| / 127).
+ * Requires M >= 1, 1 <= K <= ZQ_MAX_K, K % 16 == 0.
+ */
+zq_status zq_ln_quant_per_token(const void *X, zq_dtype x_dtype, int64_t M, int64_t K,
+                                zq_pre pre, const float *gamma, const float *beta, float eps,
+                                int8_t *Xq, float *x_scales, hipStream_t stream);
+
+/*
+ * zq_w8a8_gemm_dequant -- int8 x int8 -> int32 GEMM with the dequantization
+ * fused into its epilogue.
+ * [T36] 1.2.2: the INT32 accumulation is scaled by the activation and weight
+ * scales before the FP16 write; [T36] 1.1.2 vector-wise: that scaling is the
+ * outer product of the per-row and per-column scales; [IQ] MAC unit: the
+ * bias joins the accumulation; [ZQN] kernel fusion "GeMM + DeQuantize".
+ *
+ *   acc[m, n] = sum_k Xq[m, k] Wq[n, k]                      (exact int32)
+ *   v = s_x[m] * s_w[n / G] * acc[m, n] + bias[n]            (fp32)
+ *   v = gelu(v) if act == ZQ_ACT_GELU
+ *   Y[m, n] = fp16(v), round to nearest even                  (y_dtype ZQ_F16)
+ *
+ *   Xq [M x K], Wq [N x K] int8, 16-byte aligned; x_scales [M]; w_scales [N / G];
+ *   bias [N] fp32 or NULL; Y [M x N], 16-byte aligned.
+ *   y_dtype ZQ_F16 is the product path.  ZQ_I32 is a test mode: Y receives
+ *   the raw int32 accumulators and x_scales, w_scales, bias and act are
+ *   ignored (they may be NULL).
+ * Requires M, N >= 1, 1 <= K <= ZQ_MAX_K, K % 16 == 0, G >= 1, N % G == 0,
+ * N % 4 == 0.
+ */
+zq_status zq_w8a8_gemm_dequant(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                               const float *w_scales, int64_t group_rows, const float *bias,
+                               zq_act act, int64_t M, int64_t N, int64_t K,
+                               void *Y, zq_dtype y_dtype, hipStream_t stream);
+
+/* As zq_w8a8_gemm_dequant, with the kernel chosen explicitly (tests, tuning).
+ * ZQ_PATH_SKINNY with M > 32 returns ZQ_ERR_SHAPE. */
+zq_status zq_w8a8_gemm_dequant_ex(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                  const float *w_scales, int64_t group_rows, const float *bias,
+                                  zq_act act, int64_t M, int64_t N, int64_t K,
+                                  void *Y, zq_dtype y_dtype, zq_gemm_path path,
+                                  hipStream_t stream);
+
+/*
+ * zq_linear_w8a8 -- the whole layer: prologue then GEMM + dequant, both on
+ * `stream` with no host synchronisation in between ([ZQN] flowchart after
+ * fusion).  The int8 codes and per-token scales pass through `workspace`.
+ *
+ *   Arguments as in the two calls above; Y is fp16 [M x N].
+ *   workspace  device memory of at least zq_linear_workspace_bytes(M, K)
+ *              bytes, 256-byte aligned, owned by the caller, overwritten.
+ * Dispatches to the skinny (weight-streaming) GEMM when M <= 32.
+ */
+zq_status zq_linear_w8a8(const void *X, zq_dtype x_dtype, zq_pre pre, const float *gamma,
+                         const float *beta, float eps, const int8_t *Wq, const float *w_scales,
+                         int64_t group_rows, const float *bias, zq_act act,
+                         int64_t M, int64_t N, int64_t K,
+                         void *workspace, size_t workspace_bytes, void *Y, hipStream_t stream);
+
+/* Bytes of workspace zq_linear_w8a8 needs: M*K rounded up to 256, plus 4*M.
+ * Returns 0 for sizes that zq_linear_w8a8 would reject. */
+size_t zq_linear_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * zq_smoothquant_factors -- offline SmoothQuant calibration and LayerNorm fold.
+ * [SQ] 2.2: Y = (X diag(s)^-1)(diag(s) W), s per input channel; [SQ] 3.2:
+ * the factors are computed offline from activation statistics.
+ *
+ *   Statistics: a_j = max_m |LN(X)[m, j]| with gamma = 1, beta = 0 (the
+ *   linear's actual input), w_j = max_n |W[n, j]|;
+ *   smooth[j] = fl32(sqrt(a_j / w_j)), or 1 when a_j or w_j is 0.
+ *   Fold: gamma_out[j] = fl32(gamma[j] / smooth[j]), beta_out[j] = fl32(beta[j] / smooth[j])
+ *   (gamma / beta NULL mean 1 / 0), so that LN with gamma_out, beta_out equals
+ *   LN(X) diag(smooth)^-1.  The weight side is applied by passing `smooth`
+ *   to zq_quantize_weights_grouped.
+ *
+ *   X [M x K] (ZQ_F16 / ZQ_F32), W [N x K] (ZQ_F32 / ZQ_F16), both 16-byte aligned.
+ *   smooth, gamma_out, beta_out [K] fp32 out.
+ *   workspace  at least zq_smoothquant_workspace_bytes(M, K) bytes, 256-byte aligned.
+ * Requires M, N >= 1, 1 <= K <= ZQ_MAX_K, K % 16 == 0; X and W finite.
+ */
+zq_status zq_smoothquant_factors(const void *X, zq_dtype x_dtype, int64_t M, int64_t K, float eps,
+                                 const void *W, zq_dtype w_dtype, int64_t N,
+                                 const float *gamma, const float *beta,
+                                 float *smooth, float *gamma_out, float *beta_out,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace zq_smoothquant_factors needs (8*M + 8*K, rounded up to 256). */
+size_t zq_smoothquant_workspace_bytes(int64_t M, int64_t K);
+
+/* A static, human-readable name for a status code. */
+const char *zq_status_str(zq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZQ_H */

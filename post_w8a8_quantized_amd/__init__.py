@@ -1,0 +1,46 @@
+"""post_w8a8_quantized_amd -- ZeroQuant-style W8A8 linear layers on MI355X (gfx950).
+
+A thin Python binding over the C ABI of libzq.so (include/zq.h).  Each
+function has the name of the C entry point it calls, takes torch tensors that
+live on the GPU, checks their device, dtype, shape and contiguity, and passes
+raw device pointers plus torch's current HIP stream.  All arithmetic runs in
+the library's HIP kernels; there is no fallback.  If the library is missing
+or cannot be loaded, every call raises.
+
+    import torch, post_w8a8_quantized_amd as zq
+    Wq, s_w = zq.quantize_weights_grouped(W, group_rows=128)       # offline
+    Y = zq.linear_w8a8(X, Wq, s_w, 128, pre=zq.PRE_LAYERNORM, bias=b)
+
+Offline weight preparation and the SmoothQuant fold are also exposed
+(`smoothquant_factors`, `quantize_weights_grouped(..., smooth=s)`).
+"""
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    ACT_GELU,
+    ACT_NONE,
+    PATH_AUTO,
+    PATH_SKINNY,
+    PATH_TILED,
+    PRE_GELU,
+    PRE_LAYERNORM,
+    PRE_NONE,
+    ZQError,
+    exported_symbols,
+    library,
+    library_path,
+    linear_w8a8,
+    linear_workspace_bytes,
+    ln_quant_per_token,
+    quantize_weights_grouped,
+    smoothquant_factors,
+    smoothquant_workspace_bytes,
+    w8a8_gemm_dequant,
+)
+
+__all__ = [
+    "ACT_GELU", "ACT_NONE", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "PRE_GELU",
+    "PRE_LAYERNORM", "PRE_NONE", "ZQError", "exported_symbols", "library", "library_path",
+    "linear_w8a8", "linear_workspace_bytes", "ln_quant_per_token", "quantize_weights_grouped",
+    "smoothquant_factors", "smoothquant_workspace_bytes", "w8a8_gemm_dequant",
+]

@@ -1,0 +1,243 @@
+"""ctypes marshalling for libzq.so.  No arithmetic of the method happens here."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch  # imported first: libzq then binds to the HIP runtime torch already loaded
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libzq.so")
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "zq.h")
+
+# zq.h enums
+ZQ_OK = 0
+_STATUS = {0: "ZQ_OK", 1: "ZQ_ERR_NULL", 2: "ZQ_ERR_SHAPE", 3: "ZQ_ERR_ALIGN", 4: "ZQ_ERR_DTYPE",
+           5: "ZQ_ERR_WORKSPACE", 6: "ZQ_ERR_HIP", 7: "ZQ_ERR_UNSUPPORTED"}
+F32, F16, I8, I32 = 0, 1, 2, 3
+PRE_NONE, PRE_LAYERNORM, PRE_GELU = 0, 1, 2
+ACT_NONE, ACT_GELU = 0, 1
+PATH_AUTO, PATH_TILED, PATH_SKINNY = 0, 1, 2
+
+
+class ZQError(RuntimeError):
+    def __init__(self, call: str, status: int, msg: str = ""):
+        self.status = status
+        super().__init__(f"{call} failed: {_STATUS.get(status, status)} {msg}".rstrip())
+
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "zq_quantize_weights_grouped": (_i, [_p, _i, _p, _i64, _i64, _i64, _p, _p, _p]),
+    "zq_ln_quant_per_token": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _p, _p, _p]),
+    "zq_w8a8_gemm_dequant": (_i, [_p, _p, _p, _p, _i64, _p, _i, _i64, _i64, _i64, _p, _i, _p]),
+    "zq_w8a8_gemm_dequant_ex": (_i, [_p, _p, _p, _p, _i64, _p, _i, _i64, _i64, _i64, _p, _i, _i, _p]),
+    "zq_linear_w8a8": (_i, [_p, _i, _i, _p, _p, _f, _p, _p, _i64, _p, _i, _i64, _i64, _i64, _p, _sz,
+                           _p, _p]),
+    "zq_linear_workspace_bytes": (_sz, [_i64, _i64]),
+    "zq_smoothquant_factors": (_i, [_p, _i, _i64, _i64, _f, _p, _i, _i64, _p, _p, _p, _p, _p, _p,
+                                   _sz, _p]),
+    "zq_smoothquant_workspace_bytes": (_sz, [_i64, _i64]),
+    "zq_status_str": (ctypes.c_char_p, [_i]),
+}
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return set()
+    return {os.path.realpath(p) for p in paths if p.startswith("/")}
+
+
+def library():
+    """Load libzq.so (raises if it is not built).  Torch is imported before the
+    library so both share torch's HIP runtime; loading a second runtime into
+    the process would make torch's device pointers and streams meaningless to
+    libzq, so that case raises too."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ZQError("load", 7, f"{_LIB_PATH} is not built; run "
+                          "`python -m post_w8a8_quantized_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        runtimes = _hip_runtimes_mapped()
+        if len(runtimes) > 1:
+            raise ZQError("load", 6, f"more than one HIP runtime mapped: {sorted(runtimes)}")
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    """Names of the entry points zq.h declares."""
+    text = open(_HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"^\s*(?:zq_status|size_t|const char \*)\s*(zq_\w+)\s*\(", text,
+                                 re.M)))
+
+
+def _call(name: str, *args):
+    st = getattr(library(), name)(*args)
+    if st != ZQ_OK:
+        raise ZQError(name, st)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtypes, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _fdtype(t: torch.Tensor) -> int:
+    return F16 if t.dtype == torch.float16 else F32
+
+
+def quantize_weights_grouped(W: torch.Tensor, group_rows: int, smooth: Optional[torch.Tensor] = None,
+                             out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Offline group-wise int8 quantization of W [N, K] (optionally W * diag(smooth)).
+    Returns (Wq int8 [N, K], w_scales fp32 [N / group_rows])."""
+    _need(W, "W", (torch.float32, torch.float16))
+    N, K = W.shape
+    if smooth is not None:
+        _need(smooth, "smooth", (torch.float32,), (K,), W.device)
+    if out is None:
+        Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+        s_w = torch.empty((max(N // group_rows, 1),), dtype=torch.float32, device=W.device)
+    else:
+        Wq, s_w = out
+    _call("zq_quantize_weights_grouped", _ptr(W), _fdtype(W), _ptr(smooth), N, K, group_rows,
+          _ptr(Wq), _ptr(s_w), _stream(W))
+    return Wq, s_w
+
+
+def ln_quant_per_token(X: torch.Tensor, pre: int = PRE_LAYERNORM, gamma=None, beta=None,
+                       eps: float = 1e-5, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Fused LN/GeLU + per-token quantization of X [M, K] -> (Xq int8 [M, K], s_x fp32 [M])."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    if out is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+        s_x = torch.empty((M,), dtype=torch.float32, device=X.device)
+    else:
+        Xq, s_x = out
+    _call("zq_ln_quant_per_token", _ptr(X), _fdtype(X), M, K, pre, _ptr(gamma), _ptr(beta), eps,
+          _ptr(Xq), _ptr(s_x), _stream(X))
+    return Xq, s_x
+
+
+def w8a8_gemm_dequant(Xq: torch.Tensor, x_scales: Optional[torch.Tensor], Wq: torch.Tensor,
+                      w_scales: Optional[torch.Tensor], group_rows: int, bias=None,
+                      act: int = ACT_NONE, out_dtype: torch.dtype = torch.float16,
+                      path: int = PATH_AUTO, out: Optional[torch.Tensor] = None):
+    """Y = dequant(Xq Wq^T) [+ bias] [GeLU], fp16.  out_dtype=torch.int32 returns the raw
+    int32 accumulators (test mode)."""
+    _need(Xq, "Xq", (torch.int8,))
+    M, K = Xq.shape
+    _need(Wq, "Wq", (torch.int8,), None, Xq.device)
+    N = Wq.shape[0]
+    if Wq.shape[1] != K:
+        raise ValueError(f"Wq has K={Wq.shape[1]}, Xq has K={K}")
+    if out_dtype == torch.float16:
+        _need(x_scales, "x_scales", (torch.float32,), (M,), Xq.device)
+        _need(w_scales, "w_scales", (torch.float32,), (N // group_rows,), Xq.device)
+        ydt = F16
+    elif out_dtype == torch.int32:
+        ydt = I32
+    else:
+        raise TypeError("out_dtype must be torch.float16 or torch.int32")
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), (N,), Xq.device)
+    Y = torch.empty((M, N), dtype=out_dtype, device=Xq.device) if out is None else out
+    _call("zq_w8a8_gemm_dequant_ex", _ptr(Xq), _ptr(x_scales), _ptr(Wq), _ptr(w_scales),
+          group_rows, _ptr(bias), act, M, N, K, _ptr(Y), ydt, path, _stream(Xq))
+    return Y
+
+
+def linear_workspace_bytes(M: int, K: int) -> int:
+    return int(library().zq_linear_workspace_bytes(M, K))
+
+
+def linear_w8a8(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor, group_rows: int,
+                pre: int = PRE_LAYERNORM, gamma=None, beta=None, eps: float = 1e-5, bias=None,
+                act: int = ACT_NONE, workspace: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None):
+    """The fused layer: prologue (LN/GeLU + per-token quant) then GEMM + dequant -> fp16 [M, N]."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    _need(Wq, "Wq", (torch.int8,), None, X.device)
+    N = Wq.shape[0]
+    _need(w_scales, "w_scales", (torch.float32,), (N // group_rows,), X.device)
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), (N,), X.device)
+    need = linear_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _call("zq_linear_w8a8", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps, _ptr(Wq),
+          _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
+    return Y
+
+
+def smoothquant_workspace_bytes(M: int, K: int) -> int:
+    return int(library().zq_smoothquant_workspace_bytes(M, K))
+
+
+def smoothquant_factors(X: torch.Tensor, W: torch.Tensor, eps: float = 1e-5, gamma=None, beta=None):
+    """Offline SmoothQuant calibration on X [M, K] and W [N, K].
+    Returns (smooth [K], gamma_out [K], beta_out [K]), all fp32."""
+    _need(X, "X", (torch.float32, torch.float16))
+    _need(W, "W", (torch.float32, torch.float16), None, X.device)
+    M, K = X.shape
+    N = W.shape[0]
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    s = torch.empty((K,), dtype=torch.float32, device=X.device)
+    g = torch.empty_like(s)
+    b = torch.empty_like(s)
+    need = smoothquant_workspace_bytes(M, K)
+    ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    _call("zq_smoothquant_factors", _ptr(X), _fdtype(X), M, K, eps, _ptr(W), _fdtype(W), N,
+          _ptr(gamma), _ptr(beta), _ptr(s), _ptr(g), _ptr(b), _ptr(ws), need, _stream(X))
+    return s, g, b

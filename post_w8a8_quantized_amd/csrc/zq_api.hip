@@ -1,0 +1,252 @@
+// C ABI of libzq (declared in include/zq.h): host-side validation, dispatch
+// to the gfx950 kernels, and HIP error mapping.  Every argument is checked
+// before anything is enqueued; on error nothing is enqueued.
+#include "zq.h"
+#include "zq_kernels.h"
+
+#define ZQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kSkinnyMaxM = 32;
+
+bool aligned16(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+bool aligned16_or_null(const void *p)
+{
+    return p == nullptr || aligned16(p);
+}
+
+size_t round_up(size_t v, size_t a)
+{
+    return (v + a - 1) / a * a;
+}
+
+zq_status map_hip(hipError_t e)
+{
+    return e == hipSuccess ? ZQ_OK : ZQ_ERR_HIP;
+}
+
+// Drop an error left by earlier, unrelated work so that it is not reported
+// as this call's launch failure.
+void clear_stale_error()
+{
+    (void)hipGetLastError();
+}
+
+bool k_ok(int64_t K)
+{
+    return K >= 1 && K <= ZQ_MAX_K && K % 16 == 0;
+}
+
+zq_status check_gemm(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                     const float *w_scales, int64_t G, zq_act act, int64_t M, int64_t N,
+                     int64_t K, const void *Y, zq_dtype y_dtype, const float *bias)
+{
+    if (!Xq || !Wq || !Y)
+        return ZQ_ERR_NULL;
+    if (y_dtype != ZQ_F16 && y_dtype != ZQ_I32)
+        return ZQ_ERR_DTYPE;
+    if (act != ZQ_ACT_NONE && act != ZQ_ACT_GELU)
+        return ZQ_ERR_DTYPE;
+    if (y_dtype == ZQ_F16 && (!x_scales || !w_scales))
+        return ZQ_ERR_NULL;
+    if (M < 1 || N < 1 || !k_ok(K) || G < 1 || N % G != 0 || N % 4 != 0)
+        return ZQ_ERR_SHAPE;
+    if (M > INT32_MAX || N > INT32_MAX || M * K > (int64_t)1 << 40 || N * K > (int64_t)1 << 40)
+        return ZQ_ERR_SHAPE;
+    if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(Y))
+        return ZQ_ERR_ALIGN;
+    (void)bias;
+    return ZQ_OK;
+}
+
+zq_status check_prologue(const void *X, zq_dtype x_dtype, int64_t M, int64_t K, zq_pre pre,
+                         const float *gamma, const float *beta, const int8_t *Xq,
+                         const float *x_scales)
+{
+    if (!X || !Xq || !x_scales)
+        return ZQ_ERR_NULL;
+    if (x_dtype != ZQ_F16 && x_dtype != ZQ_F32)
+        return ZQ_ERR_DTYPE;
+    if (pre != ZQ_PRE_NONE && pre != ZQ_PRE_LAYERNORM && pre != ZQ_PRE_GELU)
+        return ZQ_ERR_DTYPE;
+    if (M < 1 || !k_ok(K) || M > INT32_MAX || M * K > (int64_t)1 << 40)
+        return ZQ_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(Xq))
+        return ZQ_ERR_ALIGN;
+    if (pre == ZQ_PRE_LAYERNORM && (!aligned16_or_null(gamma) || !aligned16_or_null(beta)))
+        return ZQ_ERR_ALIGN;
+    return ZQ_OK;
+}
+
+zq_status gemm_dispatch(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                        const float *w_scales, int64_t G, const float *bias, zq_act act,
+                        int64_t M, int64_t N, int64_t K, void *Y, zq_dtype y_dtype,
+                        zq_gemm_path path, hipStream_t stream)
+{
+    const bool i32 = y_dtype == ZQ_I32;
+    const bool skinny = path == ZQ_PATH_SKINNY || (path == ZQ_PATH_AUTO && M <= kSkinnyMaxM);
+    hipError_t e;
+    if (skinny)
+        e = zq::launch_gemm_skinny(Xq, x_scales, Wq, w_scales, G, bias, (int)act, M, N, K, Y, i32,
+                                   stream);
+    else
+        e = zq::launch_gemm_tiled(Xq, x_scales, Wq, w_scales, G, bias, (int)act, M, N, K, Y, i32,
+                                  stream);
+    return map_hip(e);
+}
+
+}  // namespace
+
+ZQ_API const char *zq_status_str(zq_status s)
+{
+    switch (s) {
+    case ZQ_OK: return "ZQ_OK";
+    case ZQ_ERR_NULL: return "ZQ_ERR_NULL: a required pointer is NULL";
+    case ZQ_ERR_SHAPE: return "ZQ_ERR_SHAPE: a size is out of range or not a required multiple";
+    case ZQ_ERR_ALIGN: return "ZQ_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case ZQ_ERR_DTYPE: return "ZQ_ERR_DTYPE: unsupported dtype or op";
+    case ZQ_ERR_WORKSPACE: return "ZQ_ERR_WORKSPACE: workspace missing or too small";
+    case ZQ_ERR_HIP: return "ZQ_ERR_HIP: the HIP runtime reported an error";
+    case ZQ_ERR_UNSUPPORTED: return "ZQ_ERR_UNSUPPORTED: not implemented";
+    }
+    return "unknown zq_status";
+}
+
+ZQ_API zq_status zq_quantize_weights_grouped(const void *W, zq_dtype w_dtype, const float *smooth,
+                                             int64_t N, int64_t K, int64_t group_rows, int8_t *Wq,
+                                             float *w_scales, hipStream_t stream)
+{
+    if (!W || !Wq || !w_scales)
+        return ZQ_ERR_NULL;
+    if (w_dtype != ZQ_F32 && w_dtype != ZQ_F16)
+        return ZQ_ERR_DTYPE;
+    if (N < 1 || !k_ok(K) || group_rows < 1 || N % group_rows != 0 || N > INT32_MAX ||
+        N * K > (int64_t)1 << 40)
+        return ZQ_ERR_SHAPE;
+    if (!aligned16(W) || !aligned16(Wq))
+        return ZQ_ERR_ALIGN;
+    clear_stale_error();
+    return map_hip(zq::launch_quantize_weights(W, w_dtype == ZQ_F16, smooth, N, K, group_rows, Wq,
+                                               w_scales, stream));
+}
+
+ZQ_API zq_status zq_ln_quant_per_token(const void *X, zq_dtype x_dtype, int64_t M, int64_t K,
+                                       zq_pre pre, const float *gamma, const float *beta,
+                                       float eps, int8_t *Xq, float *x_scales, hipStream_t stream)
+{
+    zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta, Xq, x_scales);
+    if (st != ZQ_OK)
+        return st;
+    clear_stale_error();
+    return map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
+                                       pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
+                                       pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, Xq,
+                                       x_scales, stream));
+}
+
+ZQ_API zq_status zq_w8a8_gemm_dequant_ex(const int8_t *Xq, const float *x_scales,
+                                         const int8_t *Wq, const float *w_scales,
+                                         int64_t group_rows, const float *bias, zq_act act,
+                                         int64_t M, int64_t N, int64_t K, void *Y,
+                                         zq_dtype y_dtype, zq_gemm_path path, hipStream_t stream)
+{
+    zq_status st = check_gemm(Xq, x_scales, Wq, w_scales, group_rows, act, M, N, K, Y, y_dtype,
+                              bias);
+    if (st != ZQ_OK)
+        return st;
+    if (path != ZQ_PATH_AUTO && path != ZQ_PATH_TILED && path != ZQ_PATH_SKINNY)
+        return ZQ_ERR_DTYPE;
+    if (path == ZQ_PATH_SKINNY && M > kSkinnyMaxM)
+        return ZQ_ERR_SHAPE;
+    clear_stale_error();
+    return gemm_dispatch(Xq, x_scales, Wq, w_scales, group_rows, bias, act, M, N, K, Y, y_dtype,
+                         path, stream);
+}
+
+ZQ_API zq_status zq_w8a8_gemm_dequant(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                      const float *w_scales, int64_t group_rows,
+                                      const float *bias, zq_act act, int64_t M, int64_t N,
+                                      int64_t K, void *Y, zq_dtype y_dtype, hipStream_t stream)
+{
+    return zq_w8a8_gemm_dequant_ex(Xq, x_scales, Wq, w_scales, group_rows, bias, act, M, N, K, Y,
+                                   y_dtype, ZQ_PATH_AUTO, stream);
+}
+
+ZQ_API size_t zq_linear_workspace_bytes(int64_t M, int64_t K)
+{
+    if (M < 1 || !k_ok(K) || M > INT32_MAX || M * K > (int64_t)1 << 40)
+        return 0;
+    return round_up((size_t)(M * K), 256) + 4 * (size_t)M;
+}
+
+ZQ_API zq_status zq_linear_w8a8(const void *X, zq_dtype x_dtype, zq_pre pre, const float *gamma,
+                                const float *beta, float eps, const int8_t *Wq,
+                                const float *w_scales, int64_t group_rows, const float *bias,
+                                zq_act act, int64_t M, int64_t N, int64_t K, void *workspace,
+                                size_t workspace_bytes, void *Y, hipStream_t stream)
+{
+    if (!X || !Wq || !w_scales || !Y)
+        return ZQ_ERR_NULL;
+    if (!workspace)
+        return ZQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return ZQ_ERR_ALIGN;
+    const size_t need = zq_linear_workspace_bytes(M, K);
+    int8_t *Xq = static_cast<int8_t *>(workspace);
+    float *x_scales = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                                round_up((size_t)(M > 0 && K > 0 ? M * K : 0), 256));
+    zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta, Xq, x_scales);
+    if (st != ZQ_OK)
+        return st;
+    st = check_gemm(Xq, x_scales, Wq, w_scales, group_rows, act, M, N, K, Y, ZQ_F16, bias);
+    if (st != ZQ_OK)
+        return st;
+    if (workspace_bytes < need)
+        return ZQ_ERR_WORKSPACE;
+    clear_stale_error();
+    st = map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
+                                     pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
+                                     pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, Xq, x_scales,
+                                     stream));
+    if (st != ZQ_OK)
+        return st;
+    return gemm_dispatch(Xq, x_scales, Wq, w_scales, group_rows, bias, act, M, N, K, Y, ZQ_F16,
+                         ZQ_PATH_AUTO, stream);
+}
+
+ZQ_API size_t zq_smoothquant_workspace_bytes(int64_t M, int64_t K)
+{
+    if (M < 1 || !k_ok(K) || M > INT32_MAX)
+        return 0;
+    return round_up(8 * (size_t)M + 8 * (size_t)K, 256);
+}
+
+ZQ_API zq_status zq_smoothquant_factors(const void *X, zq_dtype x_dtype, int64_t M, int64_t K,
+                                        float eps, const void *W, zq_dtype w_dtype, int64_t N,
+                                        const float *gamma, const float *beta, float *smooth,
+                                        float *gamma_out, float *beta_out, void *workspace,
+                                        size_t workspace_bytes, hipStream_t stream)
+{
+    if (!X || !W || !smooth || !gamma_out || !beta_out)
+        return ZQ_ERR_NULL;
+    if ((x_dtype != ZQ_F16 && x_dtype != ZQ_F32) || (w_dtype != ZQ_F16 && w_dtype != ZQ_F32))
+        return ZQ_ERR_DTYPE;
+    if (M < 1 || N < 1 || !k_ok(K) || M > INT32_MAX || N > INT32_MAX ||
+        M * K > (int64_t)1 << 40 || N * K > (int64_t)1 << 40)
+        return ZQ_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(W))
+        return ZQ_ERR_ALIGN;
+    if (!workspace || workspace_bytes < zq_smoothquant_workspace_bytes(M, K))
+        return ZQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return ZQ_ERR_ALIGN;
+    clear_stale_error();
+    return map_hip(zq::launch_smooth_factors(X, x_dtype == ZQ_F16, M, K, eps, W, w_dtype == ZQ_F16,
+                                             N, gamma, beta, smooth, gamma_out, beta_out,
+                                             workspace, stream));
+}

@@ -1,0 +1,42 @@
+// Internal launcher interface between the C ABI (zq_api.hip) and the gfx950
+// kernels.  Not installed, not part of the ABI.  Every launcher assumes the
+// arguments were validated by the caller and returns the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zq {
+
+// Prologue: LN / GeLU / none in fp32, then per-token absmax quantization.
+hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
+                           const float *gamma, const float *beta, float eps,
+                           int8_t *Xq, float *x_scales, hipStream_t stream);
+
+// Tiled MFMA GEMM (prefill shapes) with the fused dequant epilogue.
+// out_i32 selects the raw-accumulator test mode.
+hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                             const float *w_scales, int64_t G, const float *bias, int act,
+                             int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
+                             hipStream_t stream);
+
+// Weight-streaming MFMA GEMM for M <= 32 (decode shapes), same epilogue.
+hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                              const float *w_scales, int64_t G, const float *bias, int act,
+                              int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
+                              hipStream_t stream);
+
+// Offline group-wise weight quantization (optionally W * diag(smooth)).
+hipError_t launch_quantize_weights(const void *W, bool w_f16, const float *smooth,
+                                   int64_t N, int64_t K, int64_t G, int8_t *Wq,
+                                   float *w_scales, hipStream_t stream);
+
+// Offline SmoothQuant factors and LayerNorm fold.  ws holds 2*M floats of
+// per-token statistics followed by 2*K uint32 channel maxima.
+hipError_t launch_smooth_factors(const void *X, bool x_f16, int64_t M, int64_t K, float eps,
+                                 const void *W, bool w_f16, int64_t N,
+                                 const float *gamma, const float *beta, float *smooth,
+                                 float *gamma_out, float *beta_out, void *ws,
+                                 hipStream_t stream);
+
+}  // namespace zq

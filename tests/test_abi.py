@@ -1,0 +1,166 @@
+"""The C ABI: the library loads, exports every entry point zq.h declares, and
+rejects bad arguments on the host before touching the GPU.  Runs on the CPU
+(fake, never-dereferenced pointers; validation happens before any HIP call)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import post_w8a8_quantized_amd as zq
+from post_w8a8_quantized_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 1 << 20          # a fake 16-byte-aligned address; never dereferenced
+UNALIGNED = A + 4
+
+OK, NULL, SHAPE, ALIGN, DTYPE, WS, HIP = 0, 1, 2, 3, 4, 5, 6
+
+
+@pytest.fixture(scope="module")
+def L():
+    return zq.library()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = zq.exported_symbols()
+    assert len(names) == 9
+    out = subprocess.run(["nm", "-D", "--defined-only", zq.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+    # Nothing beyond the declared API is exported.
+    assert {n for n in exported if n.startswith("zq")} == set(names)
+
+
+def test_single_hip_runtime_mapped(L):
+    assert len(B._hip_runtimes_mapped()) <= 1
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.zq_status_str(s).decode().startswith(B._STATUS[s])
+    assert L.zq_status_str(99) == b"unknown zq_status"
+
+
+def test_workspace_sizes(L):
+    assert L.zq_linear_workspace_bytes(4096, 768) == 4096 * 768 + 4 * 4096
+    assert L.zq_linear_workspace_bytes(3, 16) == 256 + 12
+    assert L.zq_linear_workspace_bytes(0, 16) == 0
+    assert L.zq_linear_workspace_bytes(4, 17) == 0
+    assert L.zq_smoothquant_workspace_bytes(4096, 5120) == 8 * 4096 + 8 * 5120
+    assert L.zq_smoothquant_workspace_bytes(1, 16) == 256
+
+
+def gemm(L, Xq=A, sx=A, Wq=A, sw=A, G=128, bias=None, act=0, M=16, N=256, K=256, Y=A, ydt=1,
+         path=0):
+    return L.zq_w8a8_gemm_dequant_ex(Xq, sx, Wq, sw, G, bias, act, M, N, K, Y, ydt, path, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Xq=None), NULL), (dict(Wq=None), NULL), (dict(Y=None), NULL),
+    (dict(sx=None), NULL), (dict(sw=None), NULL),
+    (dict(M=0), SHAPE), (dict(N=0), SHAPE), (dict(K=0), SHAPE), (dict(K=24), SHAPE),
+    (dict(K=131072 + 16), SHAPE), (dict(G=0), SHAPE), (dict(G=96), SHAPE),
+    (dict(N=250, G=2), SHAPE), (dict(M=33, path=2), SHAPE),
+    (dict(Xq=UNALIGNED), ALIGN), (dict(Wq=UNALIGNED), ALIGN), (dict(Y=UNALIGNED), ALIGN),
+    (dict(ydt=0), DTYPE), (dict(ydt=2), DTYPE), (dict(act=2), DTYPE), (dict(path=3), DTYPE),
+])
+def test_gemm_validation(L, kw, want):
+    assert gemm(L, **kw) == want
+
+
+def test_gemm_i32_mode_does_not_need_scales(L):
+    # Valid in test mode without scales: passes validation and reaches the launch,
+    # which fails only where there is no GPU.
+    st = gemm(L, sx=None, sw=None, ydt=3)
+    assert st in (OK, HIP) and (st == HIP) == (not os.path.exists("/dev/kfd"))
+
+
+def prologue(L, X=A, dt=1, M=8, K=256, pre=1, g=None, b=None, Xq=A, sx=A):
+    return L.zq_ln_quant_per_token(X, dt, M, K, pre, g, b, 1e-5, Xq, sx, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(X=None), NULL), (dict(Xq=None), NULL), (dict(sx=None), NULL),
+    (dict(dt=2), DTYPE), (dict(dt=3), DTYPE), (dict(pre=3), DTYPE),
+    (dict(M=0), SHAPE), (dict(K=8), SHAPE), (dict(K=0), SHAPE), (dict(K=262144), SHAPE),
+    (dict(X=UNALIGNED), ALIGN), (dict(Xq=UNALIGNED), ALIGN), (dict(g=UNALIGNED), ALIGN),
+])
+def test_prologue_validation(L, kw, want):
+    assert prologue(L, **kw) == want
+
+
+def test_prologue_ignores_gamma_alignment_without_layernorm(L):
+    st = prologue(L, pre=2, g=UNALIGNED)
+    assert st in (OK, HIP)
+
+
+def linear(L, X=A, dt=1, pre=1, Wq=A, sw=A, G=128, M=16, N=256, K=256, ws=A, wsb=1 << 30, Y=A,
+           act=0):
+    return L.zq_linear_w8a8(X, dt, pre, None, None, 1e-5, Wq, sw, G, None, act, M, N, K, ws, wsb, Y,
+                            None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(X=None), NULL), (dict(Wq=None), NULL), (dict(sw=None), NULL), (dict(Y=None), NULL),
+    (dict(ws=None), WS), (dict(wsb=16 * 256), WS), (dict(ws=A + 16), ALIGN),
+    (dict(K=40), SHAPE), (dict(G=100), SHAPE), (dict(M=0), SHAPE), (dict(dt=3), DTYPE),
+    (dict(act=5), DTYPE), (dict(X=UNALIGNED), ALIGN),
+])
+def test_linear_validation(L, kw, want):
+    assert linear(L, **kw) == want
+
+
+def test_linear_workspace_exact_size_accepted(L):
+    need = L.zq_linear_workspace_bytes(16, 256)
+    assert linear(L, wsb=need) in (OK, HIP)
+    assert linear(L, wsb=need - 1) == WS
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(W=None), NULL), (dict(Wq=None), NULL), (dict(s=None), NULL), (dict(dt=2), DTYPE),
+    (dict(N=0), SHAPE), (dict(G=3), SHAPE), (dict(K=20), SHAPE), (dict(W=UNALIGNED), ALIGN),
+])
+def test_weight_quant_validation(L, kw, want):
+    a = dict(W=A, dt=0, smooth=None, N=256, K=256, G=64, Wq=A, s=A)
+    a.update(kw)
+    assert L.zq_quantize_weights_grouped(a["W"], a["dt"], a["smooth"], a["N"], a["K"], a["G"],
+                                         a["Wq"], a["s"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(X=None), NULL), (dict(W=None), NULL), (dict(s=None), NULL), (dict(xdt=2), DTYPE),
+    (dict(wdt=3), DTYPE), (dict(K=12), SHAPE), (dict(N=0), SHAPE), (dict(ws=None), WS),
+    (dict(wsb=10), WS), (dict(X=UNALIGNED), ALIGN), (dict(ws=A + 64), ALIGN),
+])
+def test_smooth_validation(L, kw, want):
+    a = dict(X=A, xdt=1, M=64, K=128, W=A, wdt=0, N=32, s=A, ws=A, wsb=1 << 20)
+    a.update(kw)
+    assert L.zq_smoothquant_factors(a["X"], a["xdt"], a["M"], a["K"], 1e-5, a["W"], a["wdt"],
+                                    a["N"], None, None, a["s"], A, A, a["ws"], a["wsb"],
+                                    None) == want
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="checks the no-GPU error path")
+def test_valid_call_without_gpu_reports_hip_error(L):
+    assert gemm(L) == HIP
+    assert prologue(L) == HIP
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    X = torch.zeros((4, 16), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        zq.ln_quant_per_token(X)
+
+
+def test_missing_library_raises(tmp_path, monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "_LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(zq.ZQError, match="not built"):
+        B.library()

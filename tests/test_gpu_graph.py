@@ -1,0 +1,57 @@
+"""The layer captured in a HIP graph (as the benchmark runs it) gives, on every
+replay, the same bits as the eager call, with unrelated eager work and
+synchronisations between the replays."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from tests._match import say
+from zq_workloads import random_affine, random_int8
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_graph_replays_match_eager(M):
+    import post_w8a8_quantized_amd as zq
+    say("graph replay", M)
+    rng = np.random.default_rng(M)
+    K, N, G = 768, 512, 128
+    X = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float16)).cuda()
+    g, b = (torch.from_numpy(a).cuda() for a in random_affine(rng, K))
+    Wq = torch.from_numpy(random_int8(rng, (N, K))).cuda()
+    s_w = torch.from_numpy(np.full(N // G, 2e-3, np.float32)).cuda()
+    bias = torch.from_numpy((0.01 * rng.standard_normal(N)).astype(np.float32)).cuda()
+    ws = torch.empty(zq.linear_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+
+    def call():
+        zq.linear_w8a8(X, Wq, s_w, G, zq.PRE_LAYERNORM, g, b, 1e-5, bias, zq.ACT_GELU,
+                       workspace=ws, out=Y)
+
+    call()
+    torch.cuda.synchronize()
+    eager = Y.cpu().numpy().view(np.uint16).copy()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(4):
+        Y.fill_(0)
+        ws.fill_(0)
+        junk = torch.randn(1 << 20, device="cuda").sum()   # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = Y.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, eager), f"replay {r} differs"
+        del junk

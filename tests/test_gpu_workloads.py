@@ -1,0 +1,126 @@
+"""End-to-end parity at the five workload sizes, through zq_linear_w8a8 as the
+benchmark calls it, with the offline steps (SmoothQuant fold, group-wise
+weight quantization) run by the HIP library too.
+
+The oracle computes the prologue and the weight quantization in full, and the
+layer's output for a sample of tokens (each token is independent, so a
+sampled row of the oracle is exactly that row of the full result): the
+first and last tokens, tokens either side of every 128-token tile edge in
+range, and evenly spaced tokens in between.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import ref
+from tests._match import assert_codes, assert_scales, assert_y, say, y_errors
+from zq_workloads import WORKLOAD_ORDER, WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def zq():
+    import post_w8a8_quantized_amd as m
+    assert torch.cuda.is_available(), "a GPU device node exists but torch sees no GPU"
+    m.library()
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def sample_rows(M: int, n: int = 48) -> np.ndarray:
+    if M <= n:
+        return np.arange(M, dtype=np.int64)
+    rows = {0, 1, M - 2, M - 1}
+    for e in range(128, M, 128 * max(1, M // (128 * 8))):
+        rows.update({e - 1, e})
+    rows.update(np.linspace(0, M - 1, n).astype(np.int64).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < M), dtype=np.int64)
+
+
+def run_workload(zq, name, smooth_override=None):
+    w = WORKLOADS[name]
+    smooth = w.smooth if smooth_override is None else smooth_override
+    inp = make_inputs(w)
+    X, W, bias = inp.X, inp.W, inp.bias
+    G, eps = w.group_rows, w.eps
+
+    # ---- oracle: offline steps in full
+    gamma, beta = inp.gamma, inp.beta
+    Wsrc = W
+    if smooth:
+        s_ref = ref.smooth_factors(X, W, eps)
+        gamma, beta = ref.fold_ln(inp.gamma, inp.beta, s_ref)
+        Wsrc = ref.fold_weights(W, s_ref)
+    Wq_ref, sw_ref = ref.quantize_groups(Wsrc, G)
+
+    # ---- HIP library: offline steps
+    Xd, Wd = dev(X), dev(W)
+    gd, bd = dev(inp.gamma), dev(inp.beta)
+    sd = None
+    if smooth:
+        sd, gd, bd = zq.smoothquant_factors(Xd, Wd, eps, gd, bd)
+        assert_scales(host(sd), s_ref, "smoothing factors", ulps=8)
+    Wq, s_w = zq.quantize_weights_grouped(Wd, G, sd)
+    del Wd
+    if smooth:
+        assert_codes(host(Wq), Wq_ref, "weight codes")
+        assert_scales(host(s_w), sw_ref, "weight scales")
+    else:
+        assert np.array_equal(host(s_w), sw_ref)
+        assert_codes(host(Wq), Wq_ref, "weight codes", exact=True)
+
+    # ---- prologue on every token
+    xq_ref, sx_ref = ref.prologue(X, w.pre, gamma, beta, eps)
+    xq, sx = zq.ln_quant_per_token(Xd, w.pre, gd if w.pre == 1 else None,
+                                   bd if w.pre == 1 else None, eps)
+    flips = assert_codes(host(xq), xq_ref, "activation codes")
+    assert_scales(host(sx), sx_ref, "activation scales")
+
+    # ---- the fused layer, as the benchmark runs it
+    biasd = None if bias is None else dev(bias)
+    Y = zq.linear_w8a8(Xd, Wq, s_w, G, w.pre, gd if w.pre == 1 else None,
+                       bd if w.pre == 1 else None, eps, biasd, w.act)
+    rows = sample_rows(w.M)
+    Yg = host(Y)[rows]
+    Yref, _, _ = ref.linear_rows(X, w.pre, gamma, beta, eps, Wq_ref, sw_ref, G, bias, w.act, rows)
+    max_rel, mean_rel = assert_y(Yg, Yref, f"{name} Y")
+    say(f"{name}: smooth={smooth} rows={len(rows)} code flips={flips} "
+        f"max|dY|/max|Y|={max_rel:.2e} sum|dY|/sum|Y|={mean_rel:.2e}")
+    return dict(X=X, W=W, bias=bias, rows=rows, Y=Yg, inp=inp)
+
+
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_workload_end_to_end(zq, name):
+    say("workload", name)
+    run_workload(zq, name)
+    torch.cuda.empty_cache()
+
+
+def test_smoothing_lowers_quantization_error(zq):
+    """Reported, and checked in direction only: on the outlier workload the
+    SmoothQuant fold brings the W8A8 result closer to the unquantized layer.
+    The pages describe smoothing as moving the outliers' difficulty from the
+    activations into the weights; the size of the gain is not pinned."""
+    name = "outlier_smooth"
+    w = WORKLOADS[name]
+    plain = run_workload(zq, name, smooth_override=False)
+    smooth = run_workload(zq, name, smooth_override=True)
+    rows = plain["rows"]
+    inp = plain["inp"]
+    yf = ref.linear_float_rows(inp.X, w.pre, inp.gamma, inp.beta, w.eps, inp.W, inp.bias, w.act, rows)
+    e_plain = y_errors(plain["Y"], yf)[1]
+    e_smooth = y_errors(smooth["Y"], yf)[1]
+    say(f"W8A8 vs unquantized (sum|dY|/sum|Y|): no smoothing {e_plain:.3e}, smoothing {e_smooth:.3e}")
+    assert e_smooth < e_plain
