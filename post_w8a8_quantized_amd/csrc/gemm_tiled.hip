@@ -10,71 +10,129 @@
 // Y[m, n] = fp16( s_x[m] * s_w[n / G] * sum_k Xq[m, k] Wq[n, k] + bias[n] ), optional GeLU.
 //
 // Design for CDNA4:
-//  - v_mfma_i32_32x32x32_i8: one instruction multiplies a 32x32 block of
-//    W rows by a 32x32 block of X rows over 32 k.  W is the A operand and X
-//    the B operand, so each lane's 16 accumulators hold 4 runs of 4
-//    consecutive output columns n of one token m: the epilogue writes 8-byte
+//  - v_mfma_i32_32x32x32_i8 (32 cycles per SIMD, the full int8 rate; the
+//    16x16x64 form issues at half that rate on gfx950).  W is the A operand
+//    and X the B operand, so each lane's 16 accumulators hold 4 runs of 4
+//    consecutive output columns of one token: the epilogue writes 8-byte
 //    fp16 groups straight from registers.
-//  - Both operands are K-contiguous in HBM, so every lane's MFMA operand is
-//    one 16-byte run of k; tiles are staged through LDS with 16-byte global
-//    loads and ds_read_b128, double-buffered so that the next k-slab's global
-//    loads are in flight while the current slab feeds the MFMAs.
-//  - LDS rows are 64 bytes (one k-slab); the 16-byte chunk index is XORed
-//    with (row / 4) % 4, which makes both the row-wise writes and the
-//    column-wise MFMA operand reads free of bank conflicts.
-//  - Output tiles are ordered so that consecutive workgroups, which the
-//    dispatcher spreads round-robin over the 8 XCDs, land on the same XCD in
-//    groups that share W (and X) panels in that XCD's L2.
+//  - Four waves, one per SIMD, each owning a (BM/2) x (BN/2) output block
+//    (128 x 128 at the largest tile): one 16-byte LDS read per lane feeds up
+//    to four MFMAs, 0.5 KB of LDS traffic per MFMA.
+//  - k slabs of BK bytes move HBM -> LDS with global_load_lds_dwordx4 (no
+//    VGPR staging, no ds_write): lane l of a wave-wide load lands at
+//    LDS[base + 16 l], so the bank swizzle is applied by choosing which
+//    16-byte chunk of its row each lane fetches.  NSTAGE slabs are in flight;
+//    one barrier per slab.  Lanes past the end of K fetch a 16-byte zero block.
+//  - LDS rows are BK bytes; chunk c of row r sits at position c ^ f(r)
+//    (f = (r/4)%4 for 64-byte rows, (r/2)%8 for 128-byte rows), which keeps
+//    the MFMA operand reads (32 rows, one chunk) free of bank conflicts.
+//  - MFMA fragments are double-buffered: the reads for k-step s+1 are issued
+//    before the MFMAs of k-step s.
+//  - Per-column weight scales and biases of the tile are staged once in LDS;
+//    per-row activation scales sit in registers.
+//  - Workgroup b runs on XCD b % 8.  Tiles are ordered in groups of 8
+//    M-tiles (N next) and each XCD takes a contiguous run, so the ~32 tiles
+//    an XCD runs at once share 8 X panels and 4 W panels in its L2.
 #include "zq_device.h"
 #include "zq_kernels.h"
 
+#include <stdlib.h>
+
+#include <type_traits>
+
 namespace zq {
+
+// 16 zero bytes: the DMA source for lanes whose k chunk lies past the end of K.
+__device__ __attribute__((aligned(16))) int8_t g_zero16[16];
+
 namespace {
 
-constexpr int BK = 64;  // k bytes per LDS slab
-
-__device__ __forceinline__ int swz(int row, int chunk)
+template <int BK>
+__device__ __forceinline__ int swz(int row)
 {
-    return chunk ^ ((row >> 2) & 3);
+    return BK == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
 }
 
-template <int BM, int BN, int WM, int WN>
-struct TileCfg {
-    static constexpr int NT = WM * WN * kWave;        // threads per block
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void dma16(const int8_t *src, int8_t *lds_base)
+{
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NSTAGE>
+struct Cfg {
+    static constexpr int NW = WM * WN;                // waves per workgroup
+    static constexpr int NT = NW * 64;
     static constexpr int TWM = BM / WM;               // tokens per wave
     static constexpr int TWN = BN / WN;               // output columns per wave
     static constexpr int FM = TWM / 32;               // X fragments per wave
     static constexpr int FN = TWN / 32;               // W fragments per wave
-    static constexpr int LX = BM * 4 / NT;            // 16-byte X loads per thread per slab
-    static constexpr int LW = BN * 4 / NT;            // 16-byte W loads per thread per slab
-    static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be 32-aligned");
-    static_assert((BM * 4) % NT == 0 && (BN * 4) % NT == 0, "loads must divide evenly");
+    static constexpr int RPI = 1024 / BK;             // rows filled by one wave-wide DMA
+    static constexpr int CPR = BK / 16;               // 16-byte chunks per row
+    static constexpr int LX = BM / RPI / NW;          // DMAs per wave per slab, X
+    static constexpr int LW = BN / RPI / NW;          // DMAs per wave per slab, W
+    static constexpr int STAGE = (BM + BN) * BK;      // bytes per slab
+    static constexpr int KS = BK / 32;                // MFMA k-steps per slab
+    static_assert(BK == 64 || BK == 128, "slab depth");
+    static_assert(TWM % 32 == 0 && TWN % 32 == 0, "wave tile must be 32-aligned");
+    static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "DMAs must divide evenly");
+    static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
+    static_assert(NSTAGE >= 2 && NSTAGE <= 4, "pipeline depth");
+    static_assert(BN <= NT, "column parameters are staged one per thread");
 };
 
-// Map the linear workgroup id to an output tile.  Workgroup b runs on XCD
-// b % 8; regrouping makes workgroups that share an XCD take neighbouring
-// tiles along M within one N column band, so they reuse the same W panel.
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
 {
     const int total = tiles_m * tiles_n;
     int t = bid;
-    if ((total & 7) == 0) {
-        const int per_xcd = total >> 3;
-        t = (bid & 7) * per_xcd + (bid >> 3);
-    }
-    tn = t / tiles_m;
-    tm = t % tiles_m;
+    if ((total & 7) == 0)
+        t = (bid & 7) * (total >> 3) + (bid >> 3);
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int g = t / per_group;
+    const int gm = min(GM, tiles_m - g * GM);
+    const int r = t - g * per_group;
+    tm = g * GM + r % gm;
+    tn = r / gm;
 }
 
-template <int BM, int BN, int WM, int WN, bool OUT_I32>
-__global__ __launch_bounds__(WM *WN *kWave) void k_gemm_tiled(
-    const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
-    const float *__restrict__ sw, int G, const float *__restrict__ bias, int act, int M, int N,
-    int K, void *__restrict__ Y, int tiles_m, int tiles_n)
+// Waves per SIMD the register budget is planned for: the two-waves-per-SIMD
+// layouts and the small tile (two workgroups per CU) get 256 registers, the
+// large one-wave-per-SIMD tiles 512.
+template <int BM, int BN, int WM, int WN>
+constexpr int waves_per_simd()
 {
-    using C = TileCfg<BM, BN, WM, WN>;
-    __shared__ __attribute__((aligned(16))) int8_t lds_x[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) int8_t lds_w[2][BN * BK];
+    return (WM * WN == 8 || BM * BN < 256 * 128) ? 2 : 1;
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool OUT_I32, int ACT>
+__global__ __launch_bounds__(WM *WN * 64)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
+                                   waves_per_simd<BM, BN, WM, WN>()))) void k_gemm_tiled(
+    const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
+    const float *__restrict__ sw, int G, const float *__restrict__ bias, int M, int N, int K,
+    void *__restrict__ Y, int tiles_m, int tiles_n)
+{
+    using C = Cfg<BM, BN, WM, WN, BK, NSTAGE>;
+    // One LDS object per slab buffer, referenced statically from an unrolled
+    // main loop, so the compiler can tell a read of one buffer from the
+    // in-flight DMAs into the others and need not wait for all of them.
+    __shared__ __attribute__((aligned(1024))) int8_t lds0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t lds1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t lds2[NSTAGE > 2 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t lds3[NSTAGE > 3 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(16))) float col_scale[BN];
+    __shared__ __attribute__((aligned(16))) float col_bias[BN];
 
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -86,47 +144,56 @@ __global__ __launch_bounds__(WM *WN *kWave) void k_gemm_tiled(
     const int wm = wave % WM;
     const int wn = wave / WM;
 
-    // Global load assignment: chunk u = tid + NT*j covers row u/4, 16-byte chunk u%4.
-    const int8_t *gx[C::LX];
-    const int8_t *gw[C::LW];
-    int lds_off_x[C::LX], lds_off_w[C::LW];
-    int kchunk_x[C::LX], kchunk_w[C::LW];
+    if (!OUT_I32 && tid < BN) {
+        const int n = min(n0 + tid, N - 1);
+        col_scale[tid] = sw[n / G];
+        col_bias[tid] = bias ? bias[n] : 0.0f;
+    }
+    float sxm[C::FM];
+#pragma unroll
+    for (int b = 0; b < C::FM; b++)
+        sxm[b] = OUT_I32 ? 0.0f : sx[min(m0 + wm * C::TWM + b * 32 + (lane & 31), M - 1)];
+
+    // DMA sources: wave-wide load j of this wave fills rows gi*RPI .. gi*RPI + RPI - 1
+    // (gi = wave + NW j); lane l writes position l % CPR of row gi*RPI + l / CPR and
+    // therefore fetches chunk (l % CPR) ^ f(row) of that row.
+    const int8_t *src_x[C::LX];
+    const int8_t *src_w[C::LW];
+    int kc_x[C::LX], kc_w[C::LW];
 #pragma unroll
     for (int j = 0; j < C::LX; j++) {
-        const int u = tid + C::NT * j;
-        const int r = u >> 2, c = u & 3;
-        const int m = min(m0 + r, M - 1);  // ragged M: re-read the last row, never stored
-        gx[j] = Xq + (int64_t)m * K + c * 16;
-        kchunk_x[j] = c * 16;
-        lds_off_x[j] = r * BK + swz(r, c) * 16;
+        const int row = (wave + C::NW * j) * C::RPI + lane / C::CPR;
+        const int c = (lane % C::CPR) ^ swz<BK>(row);
+        src_x[j] = Xq + (int64_t)min(m0 + row, M - 1) * K + 16 * c;  // ragged M: never stored
+        kc_x[j] = 16 * c;
     }
 #pragma unroll
     for (int j = 0; j < C::LW; j++) {
-        const int u = tid + C::NT * j;
-        const int r = u >> 2, c = u & 3;
-        const int n = min(n0 + r, N - 1);
-        gw[j] = Wq + (int64_t)n * K + c * 16;
-        kchunk_w[j] = c * 16;
-        lds_off_w[j] = r * BK + swz(r, c) * 16;
+        const int row = (wave + C::NW * j) * C::RPI + lane / C::CPR;
+        const int c = (lane % C::CPR) ^ swz<BK>(row);
+        src_w[j] = Wq + (int64_t)min(n0 + row, N - 1) * K + 16 * c;
+        kc_w[j] = 16 * c;
     }
+    // Lanes whose 16-byte chunk lies past K fetch zeros instead (branch-free select).
+    auto issue = [&](int slab, int8_t *bx) {
+        const int k0 = slab * BK;
+        int8_t *bw = bx + BM * BK;
+#pragma unroll
+        for (int j = 0; j < C::LX; j++)
+            dma16(k0 + kc_x[j] < K ? src_x[j] + k0 : g_zero16, bx + (wave + C::NW * j) * 1024);
+#pragma unroll
+        for (int j = 0; j < C::LW; j++)
+            dma16(k0 + kc_w[j] < K ? src_w[j] + k0 : g_zero16, bw + (wave + C::NW * j) * 1024);
+    };
 
-    v4i rx[C::LX], rw[C::LW];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int j = 0; j < C::LX; j++)
-            rx[j] = (k0 + kchunk_x[j] < K) ? *reinterpret_cast<const v4i *>(gx[j] + k0) : v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < C::LW; j++)
-            rw[j] = (k0 + kchunk_w[j] < K) ? *reinterpret_cast<const v4i *>(gw[j] + k0) : v4i{0, 0, 0, 0};
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < C::LX; j++)
-            *reinterpret_cast<v4i *>(&lds_x[buf][lds_off_x[j]]) = rx[j];
-#pragma unroll
-        for (int j = 0; j < C::LW; j++)
-            *reinterpret_cast<v4i *>(&lds_w[buf][lds_off_w[j]]) = rw[j];
-    };
+    // MFMA operand reads: lane (frow, fhalf) reads row frow of each 32-row
+    // fragment at chunk 2*ks + fhalf.  Fragment rows are multiples of 32 apart,
+    // so the swizzle depends on frow only.
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+    const int sw_l = swz<BK>(frow);
+    const int xbase = (wm * C::TWM + frow) * BK;
+    const int wbase = BM * BK + (wn * C::TWN + frow) * BK;
 
     v16i acc[C::FN][C::FM];
 #pragma unroll
@@ -135,46 +202,86 @@ __global__ __launch_bounds__(WM *WN *kWave) void k_gemm_tiled(
         for (int b = 0; b < C::FM; b++)
             acc[a][b] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-    // MFMA operand rows of this lane.
-    const int frow = lane & 31;
-    const int fhalf = lane >> 5;
-    int xrow[C::FM], wrow[C::FN];
+    auto load_frags = [&](const int8_t *stage, int ks, v4i (&fx)[C::FM], v4i (&fw)[C::FN]) {
+        const int off = ((2 * ks + fhalf) ^ sw_l) << 4;
 #pragma unroll
-    for (int b = 0; b < C::FM; b++)
-        xrow[b] = wm * C::TWM + b * 32 + frow;
+        for (int b = 0; b < C::FM; b++)
+            fx[b] = *reinterpret_cast<const v4i *>(stage + xbase + b * 32 * BK + off);
 #pragma unroll
-    for (int a = 0; a < C::FN; a++)
-        wrow[a] = wn * C::TWN + a * 32 + frow;
+        for (int a = 0; a < C::FN; a++)
+            fw[a] = *reinterpret_cast<const v4i *>(stage + wbase + a * 32 * BK + off);
+    };
 
+    int8_t *const bufs[4] = {lds0, lds1, lds2, lds3};
+    // The slab count is padded to a multiple of NSTAGE: padding slabs lie past
+    // K, every lane of their DMAs fetches the zero block, and their MFMAs add
+    // exactly 0.  This keeps the unrolled slab loop free of branches, so the
+    // count of in-flight DMAs at every wait is the same constant.
     const int nk = (K + BK - 1) / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    const int nkp = (nk + NSTAGE - 1) / NSTAGE * NSTAGE;
+    constexpr int PER_SLAB = C::LX + C::LW;  // DMAs per wave per slab
 
-    for (int kt = 0; kt < nk; kt++) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk)
-            gload((kt + 1) * BK);
+    // lgkmcnt(0) then s_barrier: this wave's LDS reads have returned and every
+    // wave has passed this point.  (A plain s_barrier: __syncthreads would also
+    // wait for the slab DMAs still in flight.)
+    auto barrier = [] {
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_barrier();
+    };
+
+    // Slab j lives in buffer j % NSTAGE.  All NSTAGE buffers start filled.
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ks++) {
-            const int chunk = ks * 2 + fhalf;
-            v4i fx[C::FM], fw[C::FN];
+    for (int j = 0; j < NSTAGE; j++)
+        issue(j, bufs[j]);
+    wait_vmcnt<(NSTAGE - 1) * PER_SLAB>();
+    barrier();
+
+    v4i fx[2][C::FM], fw[2][C::FN];
+    load_frags(bufs[0], 0, fx[0], fw[0]);
+
+    // One slab: KS MFMA k-steps.  The LDS reads for the next k-step are issued
+    // before the current k-step's MFMAs.  Before the last k-step's MFMAs the
+    // slab hands over: wait for slab kt+1, barrier (after which this slab's
+    // buffer is free), refill it with slab kt+NSTAGE, read slab kt+1's first
+    // fragments.
+    auto slab = [&](int kt, auto S) {
+        constexpr int s = decltype(S)::value;
 #pragma unroll
-            for (int b = 0; b < C::FM; b++)
-                fx[b] = *reinterpret_cast<const v4i *>(&lds_x[cur][xrow[b] * BK + swz(xrow[b], chunk) * 16]);
-#pragma unroll
-            for (int a = 0; a < C::FN; a++)
-                fw[a] = *reinterpret_cast<const v4i *>(&lds_w[cur][wrow[a] * BK + swz(wrow[a], chunk) * 16]);
+        for (int ks = 0; ks < C::KS; ks++) {
+            if (ks + 1 < C::KS) {
+                // The reads feeding this k-step were issued a k-step ago and have
+                // returned; waiting for them here, before the next reads go out,
+                // lets the MFMAs below start without an LDS wait.
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                load_frags(bufs[s], ks + 1, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
+            } else {
+                wait_vmcnt<(NSTAGE - 2) * PER_SLAB>();
+                barrier();
+                issue(kt + NSTAGE, bufs[s]);
+                load_frags(bufs[(s + 1) % NSTAGE], 0, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int a = 0; a < C::FN; a++)
 #pragma unroll
                 for (int b = 0; b < C::FM; b++)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[a], fx[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[ks & 1][a], fx[ks & 1][b],
+                                                                      acc[a][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < nk)
-            lstore(cur ^ 1);
-        __syncthreads();
+    };
+    static_assert(C::KS % 2 == 0, "fragment buffers alternate within a slab");
+    for (int kt = 0; kt < nkp; kt += NSTAGE) {
+        slab(kt, std::integral_constant<int, 0>{});
+        slab(kt + 1, std::integral_constant<int, 1>{});
+        if constexpr (NSTAGE > 2)
+            slab(kt + 2, std::integral_constant<int, 2>{});
+        if constexpr (NSTAGE > 3)
+            slab(kt + 3, std::integral_constant<int, 3>{});
     }
+    // The refills issued by the last slabs read past K (zeros) into buffers
+    // nobody reads again; drain them before the workgroup's LDS is released.
+    wait_vmcnt<0>();
 
     // Epilogue.  Accumulator register r of fragment (a, b) holds
     // token  m = m0 + wm*TWM + b*32 + lane%32 and
@@ -184,12 +291,12 @@ __global__ __launch_bounds__(WM *WN *kWave) void k_gemm_tiled(
         const int m = m0 + wm * C::TWM + b * 32 + frow;
         if (m >= M)
             continue;
-        const float sxm = OUT_I32 ? 0.0f : sx[m];
 #pragma unroll
         for (int a = 0; a < C::FN; a++) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const int n = n0 + wn * C::TWN + a * 32 + 8 * q + 4 * fhalf;
+                const int nl = wn * C::TWN + a * 32 + 8 * q + 4 * fhalf;  // column within tile
+                const int n = n0 + nl;
                 if (n >= N)
                     continue;
                 if constexpr (OUT_I32) {
@@ -197,14 +304,15 @@ __global__ __launch_bounds__(WM *WN *kWave) void k_gemm_tiled(
                              acc[a][b][4 * q + 3]};
                     *reinterpret_cast<v4i *>(static_cast<int32_t *>(Y) + (int64_t)m * N + n) = o;
                 } else {
+                    const float4 cs = *reinterpret_cast<const float4 *>(&col_scale[nl]);
+                    const float4 cb = *reinterpret_cast<const float4 *>(&col_bias[nl]);
+                    const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
+                    const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
                     h4 o;
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
-                        const float scale = sxm * sw[(n + i) / G];
-                        float v = (float)acc[a][b][4 * q + i] * scale;
-                        if (bias)
-                            v += bias[n + i];
-                        if (act == 1)
+                        float v = fmaf((float)acc[a][b][4 * q + i], sxm[b] * csv[i], cbv[i]);
+                        if constexpr (ACT == 1)
                             v = gelu_erf(v);
                         o[i] = (_Float16)v;
                     }
@@ -215,7 +323,7 @@ __global__ __launch_bounds__(WM *WN *kWave) void k_gemm_tiled(
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int NSTAGE>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
                       void *Y, bool out_i32, hipStream_t stream)
@@ -223,14 +331,61 @@ hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)(tiles_m * tiles_n));
-    const dim3 block(WM * WN * kWave);
+    const dim3 block(WM * WN * 64);
+#define ZQ_GEMM_LAUNCH(I32, A)                                                                    \
+    hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, BK, NSTAGE, I32, A>), grid, block, 0, stream, \
+                       Xq, sx, \
+                       Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y, tiles_m, tiles_n)
     if (out_i32)
-        hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, true>), grid, block, 0, stream, Xq, sx,
-                           Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y, tiles_m, tiles_n);
+        ZQ_GEMM_LAUNCH(true, 0);
+    else if (act == 1)
+        ZQ_GEMM_LAUNCH(false, 1);
     else
-        hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, false>), grid, block, 0, stream, Xq, sx,
-                           Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y, tiles_m, tiles_n);
+        ZQ_GEMM_LAUNCH(false, 0);
+#undef ZQ_GEMM_LAUNCH
     return hipGetLastError();
+}
+
+struct Shape {
+    int bm, bn;
+};
+// Tile configurations (waves: WM x WN; slab: BK bytes, NSTAGE deep):
+//  0: 256x256, 2x2 waves, 64 B x4     1: 256x256, 2x2 waves, 128 B x2
+//  2: 256x192, 2x2 waves, 64 B x4     3: 128x128, 2x2 waves, 64 B x4
+//  4: 256x128, 2x2 waves, 64 B x4     5: 256x256, 2x4 waves, 64 B x4
+//  6: 256x256, 2x4 waves, 128 B x2    7: 256x192, 4x2 waves, 128 B x2
+constexpr int kNumShapes = 8;
+constexpr Shape kShapes[kNumShapes] = {{256, 256}, {256, 256}, {256, 192}, {128, 128},
+                                       {256, 128}, {256, 256}, {256, 256}, {256, 192}};
+
+// Bigger tiles move fewer bytes from L2 per MFMA; the choice trades that
+// against how evenly the tiles fill 256 CUs.  ZQ_GEMM_TILE=0..7 forces one.
+int pick_tile(int64_t M, int64_t N)
+{
+    static const int forced = [] {
+        const char *e = getenv("ZQ_GEMM_TILE");
+        return e ? atoi(e) : -1;
+    }();
+    if (forced >= 0 && forced < kNumShapes)
+        return forced;
+    const double cus = 256.0;
+    // Measured on MI355X: the two-waves-per-SIMD 256x192 and 256x256 tiles are
+    // the fastest on every prefill shape tried; 128x128 covers small problems.
+    const int cand[3] = {7, 6, 3};
+    const double weight[3] = {1.0, 1.0, 0.7};
+    int best = 3;
+    double best_score = -1.0;
+    for (int i = 0; i < 3; i++) {
+        const Shape s = kShapes[cand[i]];
+        const double tiles = (double)((M + s.bm - 1) / s.bm) * (double)((N + s.bn - 1) / s.bn);
+        const double rounds = ceil(tiles / cus);
+        const double score = weight[i] * tiles / (rounds * cus);
+        if (score > best_score + 1e-9) {
+            best_score = score;
+            best = cand[i];
+        }
+    }
+    return best;
 }
 
 }  // namespace
@@ -240,8 +395,20 @@ hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8
                              int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
                              hipStream_t stream)
 {
-    return launch_cfg<128, 128, 2, 2>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,
-                                      out_i32, stream);
+#define ZQ_CFG(BM, BN, WM, WN, BK, NS)                                                           \
+    launch_cfg<BM, BN, WM, WN, BK, NS>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,      \
+                                       out_i32, stream)
+    switch (pick_tile(M, N)) {
+    case 0: return ZQ_CFG(256, 256, 2, 2, 64, 4);
+    case 1: return ZQ_CFG(256, 256, 2, 2, 128, 2);
+    case 2: return ZQ_CFG(256, 192, 2, 2, 64, 4);
+    case 4: return ZQ_CFG(256, 128, 2, 2, 64, 4);
+    case 5: return ZQ_CFG(256, 256, 2, 4, 64, 4);
+    case 6: return ZQ_CFG(256, 256, 2, 4, 128, 2);
+    case 7: return ZQ_CFG(256, 192, 4, 2, 128, 2);
+    default: return ZQ_CFG(128, 128, 2, 2, 64, 4);
+    }
+#undef ZQ_CFG
 }
 
 }  // namespace zq
