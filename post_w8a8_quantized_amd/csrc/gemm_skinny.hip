@@ -7,129 +7,199 @@
 // ("Integer Quantization: Deep Dive": decoding is memory-bandwidth bound).
 //
 // Design for CDNA4:
-//  - v_mfma_i32_16x16x64_i8 with W as the A operand (16 output rows) and X as
-//    the B operand (16 tokens): one instruction consumes 16 rows x 64 bytes
-//    of W, so the matrix cores absorb the whole 16-token product and the VALU
-//    stays idle.
-//  - W is read straight from HBM into registers (no LDS): each lane loads
-//    16 bytes of one row; a wave's UNROLL loads cover 16 rows x 64*UNROLL
-//    contiguous bytes, i.e. whole cache lines.  X (M x K int8, at most
-//    896 KB) is re-read from L2.
-//  - A workgroup owns 16 output rows; its NWAVE waves split K into contiguous
-//    ranges so that many 16-byte loads per CU are in flight.  Partial int32
-//    sums are combined through LDS in a fixed order (deterministic, no atomics).
+//  - A workgroup owns 16*RG output rows over all of K (one workgroup per CU
+//    at the decode shape).  Slabs of BKB bytes of those rows (and of the
+//    <= 32 token rows of X) move HBM -> LDS with global_load_lds_dwordx4;
+//    every wave-wide DMA reads 1 KB of ONE row, i.e. fully contiguous,
+//    streaming memory, which is what HBM rewards.  Two slabs are in flight.
+//  - In LDS, 16-byte chunk c of row r sits at slot c ^ (r % 16) (the DMA
+//    lane fetching a slot picks the matching chunk), so the MFMA operand
+//    reads -- 16 rows, one chunk each -- hit 16 different bank groups.
+//  - v_mfma_i32_16x16x64_i8 with W as the A operand (16 rows) and X as the
+//    B operand (16 tokens) absorbs the whole product; the four waves take
+//    alternate 64-byte k blocks of each slab and their int32 partial sums
+//    are added through LDS in a fixed order (deterministic, no atomics).
 #include "zq_device.h"
 #include "zq_kernels.h"
 
 namespace zq {
 namespace {
 
-template <int MT, int NWAVE, int UNROLL, bool OUT_I32>
-__global__ __launch_bounds__(NWAVE *kWave) void k_gemm_skinny(
+// 16 zero bytes: the DMA source for lanes whose chunk lies past the end of K.
+__device__ __attribute__((aligned(16))) int8_t zero16[16];
+
+constexpr int kThreads = 256;  // 4 waves
+
+__device__ __forceinline__ void dma16(const int8_t *src, int8_t *lds_base)
+{
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MT, int RG, int BKB, bool OUT_I32>
+__global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int act, int M, int N,
     int K, void *__restrict__ Y)
 {
-    __shared__ v4i part[NWAVE][MT][kWave];
+    constexpr int WR = 16 * RG;            // weight rows per workgroup
+    constexpr int XR = 16 * MT;            // token rows (padded to 16s)
+    constexpr int ROWS = WR + XR;
+    constexpr int PIECES = BKB / 1024;     // 1 KB DMA pieces per row per slab
+    constexpr int DMAS = ROWS * PIECES;    // wave-wide DMAs per slab
+    static_assert(DMAS % 4 == 0, "DMAs split evenly over the four waves");
+    constexpr int PER_WAVE = DMAS / 4;
+    constexpr int STAGE = ROWS * BKB;
+    constexpr int KB = BKB / 64;           // 64-byte MFMA k blocks per slab
+
+    __shared__ __attribute__((aligned(1024))) int8_t buf0[STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t buf1[STAGE];
+    __shared__ v4i part[4][RG][MT][kWave];
 
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    const int n0 = blockIdx.x * 16;
-    const int r16 = lane & 15;   // operand row within the 16-row block
-    const int kq = lane >> 4;    // which 16-byte quarter of a 64-byte k block
+    const int n0 = blockIdx.x * WR;
 
-    const int n = min(n0 + r16, N - 1);  // ragged N: re-read the last row, never stored
-    const int8_t *wrow = Wq + (int64_t)n * K + kq * 16;
-    const int8_t *xrow[MT];
+    // DMA j of this wave: row (wave + 4 j) / PIECES, piece (wave + 4 j) % PIECES.
+    // Row index < WR is a weight row, otherwise a token row.
+    const int8_t *src[PER_WAVE];
+    int kc[PER_WAVE];          // byte offset of this lane's chunk within the slab
+    int slot_bytes[PER_WAVE];  // LDS destination of the DMA
 #pragma unroll
-    for (int t = 0; t < MT; t++)
-        xrow[t] = Xq + (int64_t)min(16 * t + r16, M - 1) * K + kq * 16;
-
-    // Contiguous k-block range of this wave (64-byte blocks, last one may be partial).
-    const int nkb = (K + 63) / 64;
-    const int per = (nkb + NWAVE - 1) / NWAVE;
-    const int kb_begin = wave * per;
-    const int kb_end = min(nkb, kb_begin + per);
-
-    v4i acc[MT];
+    for (int j = 0; j < PER_WAVE; j++) {
+        const int d = wave + 4 * j;
+        const int r = d / PIECES, q = d % PIECES;
+        const int chunk = (64 * q + lane) ^ (r & 15);   // global chunk for this lane's slot
+        const int8_t *row = r < WR ? Wq + (int64_t)min(n0 + r, N - 1) * K
+                                   : Xq + (int64_t)min(r - WR, M - 1) * K;
+        src[j] = row + 16 * chunk;
+        kc[j] = 16 * chunk;
+        slot_bytes[j] = r * BKB + q * 1024;
+    }
+    auto issue = [&](int slab, int8_t *buf) {
+        const int k0 = slab * BKB;
 #pragma unroll
-    for (int t = 0; t < MT; t++)
-        acc[t] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < PER_WAVE; j++)
+            dma16(k0 + kc[j] < K ? src[j] + k0 : zero16, buf + slot_bytes[j]);
+    };
 
-    for (int kb = kb_begin; kb < kb_end; kb += UNROLL) {
-        v4i w[UNROLL], x[UNROLL][MT];
+    // MFMA operand rows: lane (r16, kq) reads row r16 of a 16-row group at
+    // chunk 4 kb + kq, stored at slot (4 kb + kq) ^ r16.
+    const int r16 = lane & 15;
+    const int kq = lane >> 4;
+
+    v4i acc[RG][MT];
 #pragma unroll
-        for (int u = 0; u < UNROLL; u++) {
-            const int k = (kb + u) * 64 + kq * 16;
-            const bool ok = (kb + u < kb_end) && (k < K);
-            w[u] = ok ? *reinterpret_cast<const v4i *>(wrow + (int64_t)(kb + u) * 64) : v4i{0, 0, 0, 0};
+    for (int g = 0; g < RG; g++)
+#pragma unroll
+        for (int t = 0; t < MT; t++)
+            acc[g][t] = v4i{0, 0, 0, 0};
+
+    auto compute = [&](const int8_t *buf) {
+#pragma unroll
+        for (int kb = wave; kb < KB; kb += 4) {
+            const int off = 16 * ((4 * kb + kq) ^ r16);
+            v4i a[RG], b[MT];
+#pragma unroll
+            for (int g = 0; g < RG; g++)
+                a[g] = *reinterpret_cast<const v4i *>(buf + (16 * g + r16) * BKB + off);
 #pragma unroll
             for (int t = 0; t < MT; t++)
-                x[u][t] = ok ? *reinterpret_cast<const v4i *>(xrow[t] + (int64_t)(kb + u) * 64)
-                             : v4i{0, 0, 0, 0};
+                b[t] = *reinterpret_cast<const v4i *>(buf + (WR + 16 * t + r16) * BKB + off);
+#pragma unroll
+            for (int g = 0; g < RG; g++)
+#pragma unroll
+                for (int t = 0; t < MT; t++)
+                    acc[g][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[g], b[t], acc[g][t], 0, 0, 0);
         }
-#pragma unroll
-        for (int u = 0; u < UNROLL; u++)
-#pragma unroll
-            for (int t = 0; t < MT; t++)
-                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u], x[u][t], acc[t], 0, 0, 0);
+    };
+    auto barrier = [] {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+    };
+
+    // Slabs alternate between buf0 and buf1; the slab count is padded to even
+    // (a padding slab lies past K and reads zeros).
+    const int ns = (K + BKB - 1) / BKB;
+    const int nsp = (ns + 1) & ~1;
+    issue(0, buf0);
+    issue(1, buf1);
+    for (int s = 0; s < nsp; s += 2) {
+        wait_vmcnt<PER_WAVE>();   // slab s landed (slab s+1 may be in flight)
+        barrier();
+        compute(buf0);
+        barrier();                // every wave is done with buf0
+        issue(s + 2, buf0);
+        wait_vmcnt<PER_WAVE>();   // slab s+1 landed (slab s+2 may be in flight)
+        barrier();
+        compute(buf1);
+        barrier();
+        issue(s + 3, buf1);
     }
+    wait_vmcnt<0>();  // drain the zero-filled refills before LDS is released
 
 #pragma unroll
-    for (int t = 0; t < MT; t++)
-        part[wave][t][lane] = acc[t];
+    for (int g = 0; g < RG; g++)
+#pragma unroll
+        for (int t = 0; t < MT; t++)
+            part[wave][g][t][lane] = acc[g][t];
     __syncthreads();
-    if (wave != 0)
-        return;
-#pragma unroll
-    for (int t = 0; t < MT; t++) {
-        v4i s = part[0][t][lane];
-#pragma unroll
-        for (int w = 1; w < NWAVE; w++)
-            s += part[w][t][lane];
-        acc[t] = s;
-    }
 
-    // Accumulator register r holds token m = 16 t + lane % 16 and
-    // output row n = n0 + 4 * (lane / 16) + r.
+    // Wave w finishes row groups w, w+4, ...: fixed-order sum of the four
+    // partials, then the epilogue.  Accumulator register i of (g, t) holds
+    // token m = 16 t + lane % 16 and output row n = n0 + 16 g + 4 (lane / 16) + i.
 #pragma unroll
-    for (int t = 0; t < MT; t++) {
-        const int m = 16 * t + r16;
-        const int nn = n0 + 4 * kq;
-        if (m >= M || nn >= N)
+    for (int g = 0; g < RG; g++) {
+        if (g % 4 != wave)
             continue;
-        if constexpr (OUT_I32) {
-            *reinterpret_cast<v4i *>(static_cast<int32_t *>(Y) + (int64_t)m * N + nn) = acc[t];
-        } else {
-            const float sxm = sx[m];
-            h4 o;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                float v = (float)acc[t][i] * (sxm * sw[(nn + i) / G]);
-                if (bias)
-                    v += bias[nn + i];
-                if (act == 1)
-                    v = gelu_erf(v);
-                o[i] = (_Float16)v;
+        for (int t = 0; t < MT; t++) {
+            const v4i sum = part[0][g][t][lane] + part[1][g][t][lane] + part[2][g][t][lane] +
+                            part[3][g][t][lane];
+            const int m = 16 * t + r16;
+            const int nn = n0 + 16 * g + 4 * kq;
+            if (m >= M || nn >= N)
+                continue;
+            if constexpr (OUT_I32) {
+                *reinterpret_cast<v4i *>(static_cast<int32_t *>(Y) + (int64_t)m * N + nn) = sum;
+            } else {
+                const float sxm = sx[m];
+                h4 o;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    float v = (float)sum[i] * (sxm * sw[(nn + i) / G]);
+                    if (bias)
+                        v += bias[nn + i];
+                    if (act == 1)
+                        v = gelu_erf(v);
+                    o[i] = (_Float16)v;
+                }
+                *reinterpret_cast<h4 *>(static_cast<_Float16 *>(Y) + (int64_t)m * N + nn) = o;
             }
-            *reinterpret_cast<h4 *>(static_cast<_Float16 *>(Y) + (int64_t)m * N + nn) = o;
         }
     }
 }
 
-template <int MT, int NWAVE, int UNROLL>
+template <int MT, int RG, int BKB>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
                       void *Y, bool out_i32, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((N + 15) / 16));
-    const dim3 block(NWAVE * kWave);
+    const dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)));
+    const dim3 block(kThreads);
     if (out_i32)
-        hipLaunchKernelGGL((k_gemm_skinny<MT, NWAVE, UNROLL, true>), grid, block, 0, stream, Xq,
-                           sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, true>), grid, block, 0, stream, Xq, sx, Wq,
+                           sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
     else
-        hipLaunchKernelGGL((k_gemm_skinny<MT, NWAVE, UNROLL, false>), grid, block, 0, stream, Xq,
-                           sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, false>), grid, block, 0, stream, Xq, sx, Wq,
+                           sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
     return hipGetLastError();
 }
 
@@ -140,11 +210,12 @@ hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int
                               int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
                               hipStream_t stream)
 {
+    // 32 weight rows per workgroup (two row groups) fills 256 CUs at N = 8192.
     if (M <= 16)
-        return launch_cfg<1, 8, 4>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y, out_i32,
-                                   stream);
-    return launch_cfg<2, 8, 4>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y, out_i32,
-                               stream);
+        return launch_cfg<1, 2, 1024>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,
+                                      out_i32, stream);
+    return launch_cfg<2, 2, 1024>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y, out_i32,
+                                  stream);
 }
 
 }  // namespace zq

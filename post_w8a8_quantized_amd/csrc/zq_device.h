@@ -52,26 +52,78 @@ __device__ __forceinline__ int quant_code(float v, float s)
     return (int)r;
 }
 
+// The same code from t = v * rs with rs = fl32(1 / s), without a division in
+// the common case.  t is within 3 ulp of v / s and fl32(v / s) within 1 ulp;
+// below 2^8 an ulp is at most 2^-16, so when t is more than 2^-13 away from
+// every half-integer both round to the same integer.  Otherwise (about one
+// element in 10^4) the IEEE quotient decides.  Requires s normal and nonzero
+// and rs = fl32(1/s) finite (the caller checks this once per vector).
+__device__ __forceinline__ int quant_code_rcp(float v, float s, float rs)
+{
+    float t = v * rs;
+    float r = __builtin_rintf(t);
+    if (fabsf(fabsf(t - r) - 0.5f) < 1.220703125e-4f)
+        r = __builtin_rintf(v / s);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// Whether quant_code_rcp may be used for scale s.
+__device__ __forceinline__ bool rcp_quant_ok(float s)
+{
+    return s >= 1.0e-30f && s <= 1.0e30f;
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d)
 {
     return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
            ((uint32_t)(d & 0xff) << 24);
 }
 
+// Wave-wide reductions without LDS: DPP within each 16-lane row (quad
+// swaps, half-row and row mirrors), then the four row results are read into
+// scalar registers and combined in a fixed order, so every lane gets the same
+// bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float rows_combine_sum(float v)
+{
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float rows_combine_max(float v)
+{
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off, kWave);
-    return v;
+    v += dpp<0xb1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4e>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    return rows_combine_sum(v);
 }
 
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
+    v = fmaxf(v, dpp<0xb1>(v));
+    v = fmaxf(v, dpp<0x4e>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    return rows_combine_max(v);
 }
 
 // Non-negative floats order like their bit patterns, so an unsigned atomic

@@ -268,3 +268,31 @@ def test_linear_deterministic(zq):
     a = host(zq.linear_w8a8(X, Wq, s_w, G))
     b = host(zq.linear_w8a8(X, Wq, s_w, G))
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,pre", [
+    (3, 8208, ref.PRE_GELU),      # one segment of 16 elements past the one-wave limit
+    (16, 28672, ref.PRE_GELU),    # the decode shape: 14 full segments
+    (40, 10000, ref.PRE_NONE),    # ragged last segment, tiled GEMM path
+    (5, 131072, ref.PRE_GELU),    # 64 segments, the most the workspace holds
+])
+def test_linear_split_prologue(zq, M, K, pre):
+    """Rows longer than 8192 without LayerNorm are quantized by the split
+    (segment-maxima) path inside zq_linear_w8a8; the codes and scales it
+    leaves in the workspace follow the same rules as the prologue's."""
+    say("split prologue", M, K, pre)
+    rng = np.random.default_rng(M + K)
+    X = (rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))).astype(np.float16)
+    N, G = 64, 64
+    Wq = random_int8(rng, (N, K))
+    s_w = np.full(N // G, 1e-3, np.float32)
+    ws = torch.zeros(zq.linear_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
+    Y = host(zq.linear_w8a8(dev(X), dev(Wq), dev(s_w), G, pre, workspace=ws))
+    q_ref, s_ref = ref.prologue(X, pre)
+    w = host(ws)
+    codes = w[:M * K].view(np.int8).reshape(M, K)
+    off = (M * K + 255) // 256 * 256
+    scales = w[off:off + 4 * M].view(np.float32)
+    assert_codes(codes, q_ref)
+    assert_scales(scales, s_ref)
+    assert_y(Y, ref.epilogue(ref.gemm_i32(q_ref, Wq), s_ref, s_w, G, None, 0))
