@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
                     if (bias)
                         v += bias[nn + i];
                     if (act == 1)
-                        v = gelu_erf(v);
+                        v = gelu_fast(v);
                     o[i] = (_Float16)v;
                 }
                 *reinterpret_cast<h4 *>(static_cast<_Float16 *>(Y) + (int64_t)m * N + nn) = o;

@@ -286,41 +286,50 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
     // Epilogue.  Accumulator register r of fragment (a, b) holds
     // token  m = m0 + wm*TWM + b*32 + lane%32 and
     // column n = n0 + wn*TWN + a*32 + 8*(r/4) + 4*(lane/32) + r%4.
+    // Tiles fully inside Y (every tile at shapes that are tile multiples)
+    // take a copy of the loop without per-group bounds checks.
+    auto epilogue = [&](auto checked) {
+        constexpr bool CHECK = decltype(checked)::value;
 #pragma unroll
-    for (int b = 0; b < C::FM; b++) {
-        const int m = m0 + wm * C::TWM + b * 32 + frow;
-        if (m >= M)
-            continue;
+        for (int b = 0; b < C::FM; b++) {
+            const int m = m0 + wm * C::TWM + b * 32 + frow;
+            if (CHECK && m >= M)
+                continue;
 #pragma unroll
-        for (int a = 0; a < C::FN; a++) {
+            for (int a = 0; a < C::FN; a++) {
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int nl = wn * C::TWN + a * 32 + 8 * q + 4 * fhalf;  // column within tile
-                const int n = n0 + nl;
-                if (n >= N)
-                    continue;
-                if constexpr (OUT_I32) {
-                    v4i o = {acc[a][b][4 * q + 0], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
-                             acc[a][b][4 * q + 3]};
-                    *reinterpret_cast<v4i *>(static_cast<int32_t *>(Y) + (int64_t)m * N + n) = o;
-                } else {
-                    const float4 cs = *reinterpret_cast<const float4 *>(&col_scale[nl]);
-                    const float4 cb = *reinterpret_cast<const float4 *>(&col_bias[nl]);
-                    const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
-                    const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
-                    h4 o;
+                for (int q = 0; q < 4; q++) {
+                    const int nl = wn * C::TWN + a * 32 + 8 * q + 4 * fhalf;  // column within tile
+                    const int n = n0 + nl;
+                    if (CHECK && n >= N)
+                        continue;
+                    if constexpr (OUT_I32) {
+                        v4i o = {acc[a][b][4 * q + 0], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                                 acc[a][b][4 * q + 3]};
+                        *reinterpret_cast<v4i *>(static_cast<int32_t *>(Y) + (int64_t)m * N + n) = o;
+                    } else {
+                        const float4 cs = *reinterpret_cast<const float4 *>(&col_scale[nl]);
+                        const float4 cb = *reinterpret_cast<const float4 *>(&col_bias[nl]);
+                        const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
+                        const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
+                        h4 o;
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        float v = fmaf((float)acc[a][b][4 * q + i], sxm[b] * csv[i], cbv[i]);
-                        if constexpr (ACT == 1)
-                            v = gelu_erf(v);
-                        o[i] = (_Float16)v;
+                        for (int i = 0; i < 4; i++) {
+                            float v = fmaf((float)acc[a][b][4 * q + i], sxm[b] * csv[i], cbv[i]);
+                            if constexpr (ACT == 1)
+                                v = gelu_fast(v);
+                            o[i] = (_Float16)v;
+                        }
+                        *reinterpret_cast<h4 *>(static_cast<_Float16 *>(Y) + (int64_t)m * N + n) = o;
                     }
-                    *reinterpret_cast<h4 *>(static_cast<_Float16 *>(Y) + (int64_t)m * N + n) = o;
                 }
             }
         }
-    }
+    };
+    if (m0 + BM <= M && n0 + BN <= N)
+        epilogue(std::false_type{});
+    else
+        epilogue(std::true_type{});
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int NSTAGE>

@@ -164,8 +164,10 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
                     for (int e = 0; e < 8; e++) b[e] = 0.0f;
                 }
 #pragma unroll
-                for (int e = 0; e < 8; e++)
-                    y[i][e] = (y[i][e] - mean) * rstd * g[e] + b[e];
+                for (int e = 0; e < 8; e++) {
+                    const float a = rstd * g[e];          // y = (x - mean) * rstd * g + b
+                    y[i][e] = fmaf(y[i][e], a, fmaf(-mean, a, b[e]));
+                }
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; e++)

@@ -41,6 +41,33 @@ __device__ __forceinline__ float gelu_erf(float x)
     return x * (x >= 0.0f ? 1.0f - h : h);
 }
 
+// GeLU for the fp16 epilogue, same function, fewer instructions:
+// gelu(x) = max(x, 0) - w with w = |x| erfc(|x| / sqrt 2) / 2 (both signs).
+// erfc(z) = t exp(P(t) - z^2), t = 1/(1 + z/2) as above, with P a degree-6
+// polynomial fitted here by least squares on Chebyshev nodes over
+// t in [1/3, 1] (z <= 4; beyond it erfc < 1.5e-8 and the clamp t >= 1/3 only
+// feeds a factor that exp(-z^2) has already crushed).  log2(e) and the 1/2
+// are folded into the coefficients, so w = |x| t exp2(P'(t) - x^2 log2(e)/2).
+// Measured in fp32 against exact GeLU: relative error <= 2.9e-6 for
+// |x| < 5.5, fp16 results never more than 1 ulp from the exact ones.
+// 14 VALU instructions and two transcendental ones.
+__device__ __forceinline__ float gelu_fast(float x)
+{
+    const float u = fabsf(x);
+    float t = __builtin_amdgcn_rcpf(fmaf(u, 0.35355339059327373f, 1.0f));
+    t = fmaxf(t, 0.33333334f);
+    float p = -0.17533810436725616f;
+    p = fmaf(p, t, 1.0116997957229614f);
+    p = fmaf(p, t, -2.094209909439087f);
+    p = fmaf(p, t, 1.5527278184890747f);
+    p = fmaf(p, t, -0.014720594510436058f);
+    p = fmaf(p, t, 1.5548698902130127f);
+    p = fmaf(p, t, -2.8350281715393066f);
+    const float e = fmaf(u, u * -0.72134752044448170f, p);
+    const float w = (u * t) * __builtin_amdgcn_exp2f(e);
+    return fmaxf(x, 0.0f) - w;
+}
+
 // Symmetric absmax code: clamp(round_half_even(fl32(v / s)), -127, 127); s == 0 gives 0.
 // The division is IEEE-correct (HIP's default for fp32 '/').
 __device__ __forceinline__ int quant_code(float v, float s)
@@ -58,14 +85,17 @@ __device__ __forceinline__ int quant_code(float v, float s)
 // every half-integer both round to the same integer.  Otherwise (about one
 // element in 10^4) the IEEE quotient decides.  Requires s normal and nonzero
 // and rs = fl32(1/s) finite (the caller checks this once per vector).
+//
+// v is an element of the vector whose absmax defined s, so |v / s| <= 127
+// up to rounding and no clamp is needed on the fast path (rint(t) <= 127 for
+// t < 127.5); the exact path clamps as quant_code does.
 __device__ __forceinline__ int quant_code_rcp(float v, float s, float rs)
 {
-    float t = v * rs;
-    float r = __builtin_rintf(t);
-    if (fabsf(fabsf(t - r) - 0.5f) < 1.220703125e-4f)
-        r = __builtin_rintf(v / s);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
+    const float t = v * rs;
+    const float r = __builtin_rintf(t);
+    if (fabsf(t - r) <= 0.4998779296875f)  // more than 2^-13 away from a half-integer
+        return (int)r;
+    return quant_code(v, s);
 }
 
 // Whether quant_code_rcp may be used for scale s.
