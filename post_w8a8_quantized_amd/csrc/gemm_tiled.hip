@@ -280,48 +280,92 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
             slab(kt + 3, std::integral_constant<int, 3>{});
     }
     // The refills issued by the last slabs read past K (zeros) into buffers
-    // nobody reads again; drain them before the workgroup's LDS is released.
+    // nobody reads again; drain them, then let every wave finish its last
+    // operand reads, before the slab buffers are reused below.
     wait_vmcnt<0>();
+    barrier();
 
     // Epilogue.  Accumulator register r of fragment (a, b) holds
     // token  m = m0 + wm*TWM + b*32 + lane%32 and
     // column n = n0 + wn*TWN + a*32 + 8*(r/4) + 4*(lane/32) + r%4.
-    // Tiles fully inside Y (every tile at shapes that are tile multiples)
-    // take a copy of the loop without per-group bounds checks.
+    if constexpr (OUT_I32) {
+#pragma unroll
+        for (int b = 0; b < C::FM; b++) {
+            const int m = m0 + wm * C::TWM + b * 32 + frow;
+#pragma unroll
+            for (int a = 0; a < C::FN; a++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int n = n0 + wn * C::TWN + a * 32 + 8 * q + 4 * fhalf;
+                    if (m >= M || n >= N)
+                        continue;
+                    v4i o = {acc[a][b][4 * q + 0], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                             acc[a][b][4 * q + 3]};
+                    *reinterpret_cast<v4i *>(static_cast<int32_t *>(Y) + (int64_t)m * N + n) = o;
+                }
+        }
+        return;
+    }
+
+    // fp16 results go out through a wave-private LDS block, one 32-token
+    // fragment row at a time: registers hold 8-byte pieces of 32 different
+    // rows, while the stores from LDS write whole runs of TWN columns, 16
+    // bytes per lane, so far fewer write requests reach L2.  Rows of the
+    // block are padded by 16 bytes to spread the 8-byte writes over the banks.
+    constexpr int RS = C::TWN * 2 + 16;          // bytes per staged row
+    constexpr int CPR_OUT = C::TWN / 8;          // 16-byte pieces per row
+    constexpr int WPB = (C::NW + NSTAGE - 1) / NSTAGE;  // waves sharing one slab buffer
+    static_assert(WPB * 32 * RS <= C::STAGE, "staging block fits in the slab buffers");
+    static_assert((32 * CPR_OUT) % 64 == 0, "whole waves of 16-byte pieces");
+    const int wb = wave % NSTAGE;
+    int8_t *const stage_out =
+        (wb == 0 ? lds0 : wb == 1 ? lds1 : wb == 2 ? lds2 : lds3) + (wave / NSTAGE) * 32 * RS;
+    _Float16 *const Yh = static_cast<_Float16 *>(Y);
+    const bool rows16 = (N & 7) == 0;            // 16-byte aligned rows of Y
     auto epilogue = [&](auto checked) {
         constexpr bool CHECK = decltype(checked)::value;
 #pragma unroll
         for (int b = 0; b < C::FM; b++) {
-            const int m = m0 + wm * C::TWM + b * 32 + frow;
-            if (CHECK && m >= M)
-                continue;
 #pragma unroll
             for (int a = 0; a < C::FN; a++) {
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    const int nl = wn * C::TWN + a * 32 + 8 * q + 4 * fhalf;  // column within tile
-                    const int n = n0 + nl;
-                    if (CHECK && n >= N)
-                        continue;
-                    if constexpr (OUT_I32) {
-                        v4i o = {acc[a][b][4 * q + 0], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
-                                 acc[a][b][4 * q + 3]};
-                        *reinterpret_cast<v4i *>(static_cast<int32_t *>(Y) + (int64_t)m * N + n) = o;
-                    } else {
-                        const float4 cs = *reinterpret_cast<const float4 *>(&col_scale[nl]);
-                        const float4 cb = *reinterpret_cast<const float4 *>(&col_bias[nl]);
-                        const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
-                        const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
-                        h4 o;
+                    const int nw = a * 32 + 8 * q + 4 * fhalf;        // column within wave block
+                    const int nl = wn * C::TWN + nw;                  // column within tile
+                    const float4 cs = *reinterpret_cast<const float4 *>(&col_scale[nl]);
+                    const float4 cb = *reinterpret_cast<const float4 *>(&col_bias[nl]);
+                    const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
+                    const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
+                    h4 o;
 #pragma unroll
-                        for (int i = 0; i < 4; i++) {
-                            float v = fmaf((float)acc[a][b][4 * q + i], sxm[b] * csv[i], cbv[i]);
-                            if constexpr (ACT == 1)
-                                v = gelu_fast(v);
-                            o[i] = (_Float16)v;
-                        }
-                        *reinterpret_cast<h4 *>(static_cast<_Float16 *>(Y) + (int64_t)m * N + n) = o;
+                    for (int i = 0; i < 4; i++) {
+                        float v = fmaf((float)acc[a][b][4 * q + i], sxm[b] * csv[i], cbv[i]);
+                        if constexpr (ACT == 1)
+                            v = gelu_fast(v);
+                        o[i] = (_Float16)v;
                     }
+                    *reinterpret_cast<h4 *>(stage_out + frow * RS + 2 * nw) = o;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 32 * CPR_OUT / 64; j++) {
+                const int i = lane + 64 * j;
+                const int row = i / CPR_OUT;
+                const int c = i % CPR_OUT;
+                const h8 v = *reinterpret_cast<const h8 *>(stage_out + row * RS + 16 * c);
+                const int m = m0 + wm * C::TWM + b * 32 + row;
+                const int n = n0 + wn * C::TWN + 8 * c;
+                if (CHECK && m >= M)
+                    continue;
+                _Float16 *dst = Yh + (int64_t)m * N + n;
+                if (rows16 && (!CHECK || n + 8 <= N)) {
+                    *reinterpret_cast<h8 *>(dst) = v;
+                } else {
+                    // N is a multiple of 4: each half is wholly inside or outside Y.
+                    if (!CHECK || n < N)
+                        *reinterpret_cast<h4 *>(dst) = v.lo;
+                    if (!CHECK || n + 4 < N)
+                        *reinterpret_cast<h4 *>(dst + 4) = v.hi;
                 }
             }
         }

@@ -121,6 +121,34 @@ def test_gemm_dequant_epilogue(zq, path, act, G):
     assert off.mean() <= 1e-3, off.mean()
 
 
+@pytest.mark.parametrize("M,N,K", TILED_SHAPES + [(520, 392, 256), (300, 204, 96)])
+def test_gemm_tiled_f16_tile_edges(zq, M, N, K):
+    """fp16 output of the tiled kernel at tile multiples and at ragged M and N
+    tails, including rows of Y that are only 8-byte aligned (N % 8 == 4)."""
+    say("tiled f16 edges", M, N, K)
+    rng = np.random.default_rng(M * 13 + N * 7 + K)
+    G = 4
+    Xq = random_int8(rng, (M, K))
+    Wq = random_int8(rng, (N, K))
+    s_x = (np.exp(rng.standard_normal(M)) * 0.01).astype(np.float32)
+    s_w = (np.exp(rng.standard_normal(N // G)) * 2e-4).astype(np.float32)
+    bias = (0.01 * rng.standard_normal(N)).astype(np.float32)
+    act = (M + N) % 2
+    want = ref.epilogue(ref.gemm_i32(Xq, Wq), s_x, s_w, G, bias, act)
+    # Y sits at the start of a larger buffer whose tail must stay untouched.
+    guard = 4096
+    buf = torch.full((M * N + guard,), 7.0, dtype=torch.float16, device="cuda")
+    zq.w8a8_gemm_dequant(dev(Xq), dev(s_x), dev(Wq), dev(s_w), G, dev(bias), act,
+                         path=zq.PATH_TILED, out=buf[:M * N].view(M, N))
+    flat = host(buf)
+    assert np.all(flat[M * N:] == 7.0)
+    got = flat[:M * N].reshape(M, N)
+    assert_y(got, want)
+    ulp = np.spacing(np.abs(want).astype(np.float16)).astype(np.float64)
+    off = np.abs(got.astype(np.float64) - want.astype(np.float64)) > ulp
+    assert off.mean() <= 1e-3, off.mean()
+
+
 def test_gemm_no_bias_and_zero_scale_token(zq):
     """A token with scale 0 (all-zero row) gives exactly the bias; without
     bias it gives exactly 0."""
