@@ -22,6 +22,10 @@
 #include "zq_device.h"
 #include "zq_kernels.h"
 
+#include <stdlib.h>
+
+#include <type_traits>
+
 namespace zq {
 namespace {
 
@@ -30,10 +34,13 @@ __device__ __attribute__((aligned(16))) int8_t zero16[16];
 
 constexpr int kThreads = 256;  // 4 waves
 
+// POLICY is the cache-policy operand of the load (2 = nt: streamed, not kept).
+template <int POLICY>
 __device__ __forceinline__ void dma16(const int8_t *src, int8_t *lds_base)
 {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0,
+                                     POLICY);
 }
 
 template <int N>
@@ -43,7 +50,7 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MT, int RG, int BKB, bool OUT_I32>
+template <int MT, int RG, int BKB, int NS, bool NTW, bool OUT_I32>
 __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int act, int M, int N,
@@ -52,42 +59,68 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     constexpr int WR = 16 * RG;            // weight rows per workgroup
     constexpr int XR = 16 * MT;            // token rows (padded to 16s)
     constexpr int ROWS = WR + XR;
-    constexpr int PIECES = BKB / 1024;     // 1 KB DMA pieces per row per slab
-    constexpr int DMAS = ROWS * PIECES;    // wave-wide DMAs per slab
-    static_assert(DMAS % 4 == 0, "DMAs split evenly over the four waves");
-    constexpr int PER_WAVE = DMAS / 4;
+    constexpr int CPR = BKB / 16;          // 16-byte chunks per row and slab
+    constexpr int LW = WR * CPR / 256;     // wave-wide DMAs per wave and slab, weights
+    constexpr int LX = XR * CPR / 256;     // the same, tokens
+    static_assert(CPR >= 16 && (XR * CPR) % 256 == 0, "DMAs split evenly over the four waves");
+    constexpr int PER_WAVE = LW + LX;
     constexpr int STAGE = ROWS * BKB;
     constexpr int KB = BKB / 64;           // 64-byte MFMA k blocks per slab
+    static_assert(NS >= 2 && NS <= 8, "pipeline depth");
+    static_assert(4 * RG * MT * 64 * 16 <= STAGE, "partial sums fit in one slab buffer");
 
+    // One LDS object per slab buffer, referenced statically from the unrolled
+    // loop, so the compiler can tell the buffers apart from in-flight DMAs.
     __shared__ __attribute__((aligned(1024))) int8_t buf0[STAGE];
     __shared__ __attribute__((aligned(1024))) int8_t buf1[STAGE];
-    __shared__ v4i part[4][RG][MT][kWave];
+    __shared__ __attribute__((aligned(1024))) int8_t buf2[NS > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t buf3[NS > 3 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t buf4[NS > 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t buf5[NS > 5 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t buf6[NS > 6 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t buf7[NS > 7 ? STAGE : 16];
+    int8_t *const bufs[8] = {buf0, buf1, buf2, buf3, buf4, buf5, buf6, buf7};
 
-    const int wave = threadIdx.x / kWave;
+    // Wave index as a scalar: the DMA split, k blocks and row groups below
+    // are uniform per wave.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int n0 = blockIdx.x * WR;
 
-    // DMA j of this wave: row (wave + 4 j) / PIECES, piece (wave + 4 j) % PIECES.
-    // Row index < WR is a weight row, otherwise a token row.
-    const int8_t *src[PER_WAVE];
-    int kc[PER_WAVE];          // byte offset of this lane's chunk within the slab
-    int slot_bytes[PER_WAVE];  // LDS destination of the DMA
+    // Wave-wide DMA d of a row block fills LDS bytes [1024 d, 1024 d + 1024)
+    // of that block: lane l lands at flat chunk position f = 64 d + l, i.e.
+    // slot f % CPR of row f / CPR, and fetches the chunk stored there.
+    // Wave w issues DMAs w, w + 4, ... of the weight block and of the token block.
+    const int8_t *src_w[LW], *src_x[LX];
+    int kc_w[LW], kc_x[LX];    // byte offset of this lane's chunk within the slab
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; j++) {
-        const int d = wave + 4 * j;
-        const int r = d / PIECES, q = d % PIECES;
-        const int chunk = (64 * q + lane) ^ (r & 15);   // global chunk for this lane's slot
-        const int8_t *row = r < WR ? Wq + (int64_t)min(n0 + r, N - 1) * K
-                                   : Xq + (int64_t)min(r - WR, M - 1) * K;
-        src[j] = row + 16 * chunk;
-        kc[j] = 16 * chunk;
-        slot_bytes[j] = r * BKB + q * 1024;
+    for (int j = 0; j < LW; j++) {
+        const int f = 64 * (wave + 4 * j) + lane;
+        const int r = f / CPR;
+        const int chunk = (f % CPR) ^ (r & 15);
+        src_w[j] = Wq + (int64_t)min(n0 + r, N - 1) * K + 16 * chunk;
+        kc_w[j] = 16 * chunk;
     }
+#pragma unroll
+    for (int j = 0; j < LX; j++) {
+        const int f = 64 * (wave + 4 * j) + lane;
+        const int r = f / CPR;
+        const int chunk = (f % CPR) ^ (r & 15);
+        src_x[j] = Xq + (int64_t)min(r, M - 1) * K + 16 * chunk;
+        kc_x[j] = 16 * chunk;
+    }
+    // Lanes whose chunk lies past K (and every lane of a padding slab) fetch
+    // the zero block instead.
     auto issue = [&](int slab, int8_t *buf) {
         const int k0 = slab * BKB;
 #pragma unroll
-        for (int j = 0; j < PER_WAVE; j++)
-            dma16(k0 + kc[j] < K ? src[j] + k0 : zero16, buf + slot_bytes[j]);
+        for (int j = 0; j < LW; j++)
+            dma16<NTW ? 2 : 0>(k0 + kc_w[j] < K ? src_w[j] + k0 : zero16,
+                               buf + 1024 * (wave + 4 * j));
+#pragma unroll
+        for (int j = 0; j < LX; j++)
+            dma16<0>(k0 + kc_x[j] < K ? src_x[j] + k0 : zero16,
+                     buf + WR * BKB + 1024 * (wave + 4 * j));
     };
 
     // MFMA operand rows: lane (r16, kq) reads row r16 of a 16-row group at
@@ -102,9 +135,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
         for (int t = 0; t < MT; t++)
             acc[g][t] = v4i{0, 0, 0, 0};
 
+    // Wave w takes k blocks w, w + 4, ... of each slab.
     auto compute = [&](const int8_t *buf) {
 #pragma unroll
-        for (int kb = wave; kb < KB; kb += 4) {
+        for (int i = 0; i < KB / 4; i++) {
+            const int kb = wave + 4 * i;
             const int off = 16 * ((4 * kb + kq) ^ r16);
             v4i a[RG], b[MT];
 #pragma unroll
@@ -125,31 +160,51 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
         __builtin_amdgcn_s_barrier();
     };
 
-    // Slabs alternate between buf0 and buf1; the slab count is padded to even
-    // (a padding slab lies past K and reads zeros).
+    // Slab s lives in buffer s % NS; NS - 1 slabs are in flight while one is
+    // multiplied.  Step s: wait for slab s, barrier (every wave is done with
+    // slab s - 1), refill slab s - 1's buffer with slab s + NS - 1, multiply.
+    // The slab count is padded to a multiple of NS (padding slabs read zeros
+    // and add 0), so the loop has no branches and every wait the same count.
     const int ns = (K + BKB - 1) / BKB;
-    const int nsp = (ns + 1) & ~1;
-    issue(0, buf0);
-    issue(1, buf1);
-    for (int s = 0; s < nsp; s += 2) {
-        wait_vmcnt<PER_WAVE>();   // slab s landed (slab s+1 may be in flight)
+    const int nsp = (ns + NS - 1) / NS * NS;
+#pragma unroll
+    for (int j = 0; j < NS - 1; j++)
+        issue(j, bufs[j]);
+    auto step = [&](int s, auto J) {
+        constexpr int j = decltype(J)::value;
+        wait_vmcnt<(NS - 2) * PER_WAVE>();
         barrier();
-        compute(buf0);
-        barrier();                // every wave is done with buf0
-        issue(s + 2, buf0);
-        wait_vmcnt<PER_WAVE>();   // slab s+1 landed (slab s+2 may be in flight)
-        barrier();
-        compute(buf1);
-        barrier();
-        issue(s + 3, buf1);
+        issue(s + NS - 1, bufs[(j + NS - 1) % NS]);
+        compute(bufs[j]);
+    };
+    for (int s = 0; s < nsp; s += NS) {
+        step(s, std::integral_constant<int, 0>{});
+        step(s + 1, std::integral_constant<int, 1>{});
+        if constexpr (NS > 2)
+            step(s + 2, std::integral_constant<int, 2>{});
+        if constexpr (NS > 3)
+            step(s + 3, std::integral_constant<int, 3>{});
+        if constexpr (NS > 4)
+            step(s + 4, std::integral_constant<int, 4>{});
+        if constexpr (NS > 5)
+            step(s + 5, std::integral_constant<int, 5>{});
+        if constexpr (NS > 6)
+            step(s + 6, std::integral_constant<int, 6>{});
+        if constexpr (NS > 7)
+            step(s + 7, std::integral_constant<int, 7>{});
     }
-    wait_vmcnt<0>();  // drain the zero-filled refills before LDS is released
+    // The last NS - 1 refills lie past K and fill buffers nobody reads; drain
+    // them, and let every wave finish its reads, before buf0 is reused.
+    wait_vmcnt<0>();
+    barrier();
 
+    // Partial sums of the four waves go through buf0 (free now).
+    v4i *part = reinterpret_cast<v4i *>(buf0);   // [wave][g][t][lane]
 #pragma unroll
     for (int g = 0; g < RG; g++)
 #pragma unroll
         for (int t = 0; t < MT; t++)
-            part[wave][g][t][lane] = acc[g][t];
+            part[((wave * RG + g) * MT + t) * kWave + lane] = acc[g][t];
     __syncthreads();
 
     // Wave w finishes row groups w, w+4, ...: fixed-order sum of the four
@@ -161,8 +216,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
             continue;
 #pragma unroll
         for (int t = 0; t < MT; t++) {
-            const v4i sum = part[0][g][t][lane] + part[1][g][t][lane] + part[2][g][t][lane] +
-                            part[3][g][t][lane];
+            v4i sum = part[((0 * RG + g) * MT + t) * kWave + lane];
+#pragma unroll
+            for (int w = 1; w < 4; w++)
+                sum += part[((w * RG + g) * MT + t) * kWave + lane];
             const int m = 16 * t + r16;
             const int nn = n0 + 16 * g + 4 * kq;
             if (m >= M || nn >= N)
@@ -187,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     }
 }
 
-template <int MT, int RG, int BKB>
+template <int MT, int RG, int BKB, int NS, bool NTW>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
                       void *Y, bool out_i32, hipStream_t stream)
@@ -195,12 +252,22 @@ hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const
     const dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)));
     const dim3 block(kThreads);
     if (out_i32)
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, true>), grid, block, 0, stream, Xq, sx, Wq,
-                           sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, true>), grid, block, 0, stream, Xq,
+                           sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
     else
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, false>), grid, block, 0, stream, Xq, sx, Wq,
-                           sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, false>), grid, block, 0, stream,
+                           Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
     return hipGetLastError();
+}
+
+// ZQ_SKINNY_CFG=0..8 forces one configuration (measurement aid).
+int skinny_cfg()
+{
+    static const int forced = [] {
+        const char *e = getenv("ZQ_SKINNY_CFG");
+        return e ? atoi(e) : -1;
+    }();
+    return forced;
 }
 
 }  // namespace
@@ -210,12 +277,34 @@ hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int
                               int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
                               hipStream_t stream)
 {
+#define ZQ_SK(MT, RG, BKB, NS, NT)                                                               \
+    launch_cfg<MT, RG, BKB, NS, NT>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,        \
+                                    out_i32, stream)
     // 32 weight rows per workgroup (two row groups) fills 256 CUs at N = 8192.
-    if (M <= 16)
-        return launch_cfg<1, 2, 1024>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,
-                                      out_i32, stream);
-    return launch_cfg<2, 2, 1024>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y, out_i32,
-                                  stream);
+    // Configurations: slab bytes per row x pipeline depth, nt = weight stream
+    // loaded with the non-temporal policy.
+    const int cfg = skinny_cfg();
+    if (M <= 16) {
+        switch (cfg) {
+        case 0: return ZQ_SK(1, 2, 1024, 2, false);
+        case 1: return ZQ_SK(1, 2, 1024, 3, false);
+        case 2: return ZQ_SK(1, 2, 512, 4, false);
+        case 3: return ZQ_SK(1, 2, 1024, 3, true);
+        case 5: return ZQ_SK(1, 2, 512, 6, true);
+        case 6: return ZQ_SK(1, 2, 256, 8, true);
+        case 7: return ZQ_SK(1, 2, 512, 5, true);
+        case 8: return ZQ_SK(1, 2, 256, 6, true);
+        default: return ZQ_SK(1, 2, 512, 4, true);
+        }
+    }
+    switch (cfg) {
+    case 0: return ZQ_SK(2, 2, 1024, 2, false);
+    case 1: return ZQ_SK(2, 2, 512, 4, false);
+    case 3: return ZQ_SK(2, 2, 1024, 2, true);
+    case 5: return ZQ_SK(2, 2, 256, 8, true);
+    default: return ZQ_SK(2, 2, 512, 4, true);
+    }
+#undef ZQ_SK
 }
 
 }  // namespace zq
