@@ -186,6 +186,50 @@ zq_status zq_linear_w8a8(const void *X, zq_dtype x_dtype, zq_pre pre, const floa
 size_t zq_linear_workspace_bytes(int64_t M, int64_t K);
 
 /*
+ * Packed weights for the weight-streaming (decode) GEMM.
+ *
+ * At decode shapes (M <= 32) the layer streams all of Wq from HBM once per
+ * call and is bound by HBM bandwidth ("Integer Quantization: Deep Dive":
+ * decoding is memory-bandwidth bound).  Read row-major, each workgroup's
+ * slice of Wq is 32 rows one K apart; the packed layout stores what one
+ * workgroup reads per pipeline step as one contiguous 16 KB run instead.
+ * Packing is an offline re-layout of the quantized weights, like the
+ * quantization itself ([T36] 1.2.2: weights are quantized ahead of time);
+ * the codes and w_scales are unchanged, and results equal the row-major
+ * calls bit for bit.
+ *
+ * Layout: with KS = ceil(K / 512), byte c of row r of block (b, s) is
+ *   Wp[((b * KS + s) * 32 + r) * 512 + c] = Wq[(32 b + r) * K + 512 s + c],
+ * or 0 where 32 b + r >= N or 512 s + c >= K.  b = 0 .. ceil(N / 32) - 1.
+ */
+
+/* Bytes of the packed layout: ceil(N / 32) * 32 * ceil(K / 512) * 512.
+ * Returns 0 for sizes zq_pack_weights would reject. */
+size_t zq_packed_weights_bytes(int64_t N, int64_t K);
+
+/* zq_pack_weights -- offline: Wq [N x K] int8 -> Wp, zq_packed_weights_bytes(N, K)
+ * bytes, both 16-byte aligned, not overlapping.  Requires N >= 1,
+ * 1 <= K <= ZQ_MAX_K, K % 16 == 0. */
+zq_status zq_pack_weights(const int8_t *Wq, int64_t N, int64_t K, int8_t *Wp,
+                          hipStream_t stream);
+
+/* As zq_w8a8_gemm_dequant (same arguments, y_dtype ZQ_F16 or the ZQ_I32 test
+ * mode) with the weights given packed.  Runs the weight-streaming kernel:
+ * requires M <= 32 (else ZQ_ERR_SHAPE). */
+zq_status zq_w8a8_gemm_dequant_packed(const int8_t *Xq, const float *x_scales, const int8_t *Wp,
+                                      const float *w_scales, int64_t group_rows,
+                                      const float *bias, zq_act act, int64_t M, int64_t N,
+                                      int64_t K, void *Y, zq_dtype y_dtype, hipStream_t stream);
+
+/* As zq_linear_w8a8 with the weights given packed; requires M <= 32. */
+zq_status zq_linear_w8a8_packed(const void *X, zq_dtype x_dtype, zq_pre pre,
+                                const float *gamma, const float *beta, float eps,
+                                const int8_t *Wp, const float *w_scales, int64_t group_rows,
+                                const float *bias, zq_act act, int64_t M, int64_t N, int64_t K,
+                                void *workspace, size_t workspace_bytes, void *Y,
+                                hipStream_t stream);
+
+/*
  * zq_smoothquant_factors -- offline SmoothQuant calibration and LayerNorm fold.
  * [SQ] 2.2: Y = (X diag(s)^-1)(diag(s) W), s per input channel; [SQ] 3.2:
  * the factors are computed offline from activation statistics.

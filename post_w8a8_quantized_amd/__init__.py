@@ -12,7 +12,9 @@ or cannot be loaded, every call raises.
     Y = zq.linear_w8a8(X, Wq, s_w, 128, pre=zq.PRE_LAYERNORM, bias=b)
 
 Offline weight preparation and the SmoothQuant fold are also exposed
-(`smoothquant_factors`, `quantize_weights_grouped(..., smooth=s)`).
+(`smoothquant_factors`, `quantize_weights_grouped(..., smooth=s)`), and for
+decode shapes (M <= 32) the weights can be re-laid out once with
+`pack_weights` and used by `linear_w8a8_packed` / `w8a8_gemm_dequant_packed`.
 """
 from __future__ import annotations
 
@@ -30,17 +32,22 @@ from ._binding import (  # noqa: F401
     library,
     library_path,
     linear_w8a8,
+    linear_w8a8_packed,
     linear_workspace_bytes,
     ln_quant_per_token,
+    pack_weights,
+    packed_weights_bytes,
     quantize_weights_grouped,
     smoothquant_factors,
     smoothquant_workspace_bytes,
     w8a8_gemm_dequant,
+    w8a8_gemm_dequant_packed,
 )
 
 __all__ = [
     "ACT_GELU", "ACT_NONE", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "PRE_GELU",
     "PRE_LAYERNORM", "PRE_NONE", "ZQError", "exported_symbols", "library", "library_path",
-    "linear_w8a8", "linear_workspace_bytes", "ln_quant_per_token", "quantize_weights_grouped",
-    "smoothquant_factors", "smoothquant_workspace_bytes", "w8a8_gemm_dequant",
+    "linear_w8a8", "linear_w8a8_packed", "linear_workspace_bytes", "ln_quant_per_token",
+    "pack_weights", "packed_weights_bytes", "quantize_weights_grouped", "smoothquant_factors",
+    "smoothquant_workspace_bytes", "w8a8_gemm_dequant", "w8a8_gemm_dequant_packed",
 ]

@@ -46,6 +46,12 @@ _SIGS = {
                                    _sz, _p]),
     "zq_smoothquant_workspace_bytes": (_sz, [_i64, _i64]),
     "zq_status_str": (ctypes.c_char_p, [_i]),
+    "zq_packed_weights_bytes": (_sz, [_i64, _i64]),
+    "zq_pack_weights": (_i, [_p, _i64, _i64, _p, _p]),
+    "zq_w8a8_gemm_dequant_packed": (_i, [_p, _p, _p, _p, _i64, _p, _i, _i64, _i64, _i64, _p, _i,
+                                         _p]),
+    "zq_linear_w8a8_packed": (_i, [_p, _i, _i, _p, _p, _f, _p, _p, _i64, _p, _i, _i64, _i64, _i64,
+                                   _p, _sz, _p, _p]),
 }
 
 _lib = None
@@ -215,6 +221,80 @@ def linear_w8a8(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor, group
     Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
     _call("zq_linear_w8a8", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps, _ptr(Wq),
           _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
+    return Y
+
+
+def packed_weights_bytes(N: int, K: int) -> int:
+    return int(library().zq_packed_weights_bytes(N, K))
+
+
+def pack_weights(Wq: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Offline re-layout of Wq int8 [N, K] into the packed layout zq.h defines
+    (32-row x 512-byte blocks); returns a 1-D int8 tensor of
+    packed_weights_bytes(N, K) bytes.  The packed calls take N explicitly."""
+    _need(Wq, "Wq", (torch.int8,))
+    N, K = Wq.shape
+    nbytes = packed_weights_bytes(N, K)
+    if nbytes == 0:
+        raise ZQError("zq_pack_weights", 2)
+    Wp = torch.empty((nbytes,), dtype=torch.int8, device=Wq.device) if out is None else out
+    _need(Wp, "Wp", (torch.int8,), (nbytes,), Wq.device)
+    _call("zq_pack_weights", _ptr(Wq), N, K, _ptr(Wp), _stream(Wq))
+    return Wp
+
+
+def _need_packed(Wp: torch.Tensor, N: int, K: int, device):
+    _need(Wp, "Wp", (torch.int8,), None, device)
+    if Wp.numel() != packed_weights_bytes(N, K):
+        raise ValueError(f"Wp has {Wp.numel()} bytes, the packed layout of {N}x{K} has "
+                         f"{packed_weights_bytes(N, K)}")
+
+
+def w8a8_gemm_dequant_packed(Xq: torch.Tensor, x_scales: Optional[torch.Tensor], Wp: torch.Tensor,
+                             w_scales: Optional[torch.Tensor], group_rows: int, N: int, bias=None,
+                             act: int = ACT_NONE, out_dtype: torch.dtype = torch.float16,
+                             out: Optional[torch.Tensor] = None):
+    """As w8a8_gemm_dequant with packed weights (M <= 32)."""
+    _need(Xq, "Xq", (torch.int8,))
+    M, K = Xq.shape
+    _need_packed(Wp, N, K, Xq.device)
+    if out_dtype == torch.float16:
+        _need(x_scales, "x_scales", (torch.float32,), (M,), Xq.device)
+        _need(w_scales, "w_scales", (torch.float32,), (N // group_rows,), Xq.device)
+        ydt = F16
+    elif out_dtype == torch.int32:
+        ydt = I32
+    else:
+        raise TypeError("out_dtype must be torch.float16 or torch.int32")
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), (N,), Xq.device)
+    Y = torch.empty((M, N), dtype=out_dtype, device=Xq.device) if out is None else out
+    _call("zq_w8a8_gemm_dequant_packed", _ptr(Xq), _ptr(x_scales), _ptr(Wp), _ptr(w_scales),
+          group_rows, _ptr(bias), act, M, N, K, _ptr(Y), ydt, _stream(Xq))
+    return Y
+
+
+def linear_w8a8_packed(X: torch.Tensor, Wp: torch.Tensor, w_scales: torch.Tensor, group_rows: int,
+                       N: int, pre: int = PRE_LAYERNORM, gamma=None, beta=None, eps: float = 1e-5,
+                       bias=None, act: int = ACT_NONE, workspace: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None):
+    """As linear_w8a8 with packed weights (M <= 32)."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    _need_packed(Wp, N, K, X.device)
+    _need(w_scales, "w_scales", (torch.float32,), (N // group_rows,), X.device)
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), (N,), X.device)
+    need = linear_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _call("zq_linear_w8a8_packed", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps,
+          _ptr(Wp), _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(workspace),
           workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
     return Y
 

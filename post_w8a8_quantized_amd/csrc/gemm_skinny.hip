@@ -24,6 +24,8 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 namespace zq {
@@ -33,6 +35,8 @@ namespace {
 __device__ __attribute__((aligned(16))) int8_t zero16[16];
 
 constexpr int kThreads = 256;  // 4 waves
+constexpr int kPackRows = 32;   // weight rows per packed block
+constexpr int kPackBytes = 512; // bytes of each row per packed block
 
 // POLICY is the cache-policy operand of the load (2 = nt: streamed, not kept).
 template <int POLICY>
@@ -50,7 +54,7 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MT, int RG, int BKB, int NS, bool NTW, bool OUT_I32>
+template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED, bool OUT_I32>
 __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int act, int M, int N,
@@ -68,6 +72,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     constexpr int KB = BKB / 64;           // 64-byte MFMA k blocks per slab
     static_assert(NS >= 2 && NS <= 8, "pipeline depth");
     static_assert(4 * RG * MT * 64 * 16 <= STAGE, "partial sums fit in one slab buffer");
+    static_assert(!PACKED || (WR == kPackRows && BKB == kPackBytes), "packed blocks are slabs");
 
     // One LDS object per slab buffer, referenced statically from the unrolled
     // loop, so the compiler can tell the buffers apart from in-flight DMAs.
@@ -91,6 +96,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     // of that block: lane l lands at flat chunk position f = 64 d + l, i.e.
     // slot f % CPR of row f / CPR, and fetches the chunk stored there.
     // Wave w issues DMAs w, w + 4, ... of the weight block and of the token block.
+    // Packed weights: the workgroup's slab s is one contiguous block of WR
+    // rows x BKB bytes at ((blockIdx.x * ns) + s) * WR * BKB, zero padded.
+    const int ns = (K + BKB - 1) / BKB;
     const int8_t *src_w[LW], *src_x[LX];
     int kc_w[LW], kc_x[LX];    // byte offset of this lane's chunk within the slab
 #pragma unroll
@@ -98,7 +106,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
         const int f = 64 * (wave + 4 * j) + lane;
         const int r = f / CPR;
         const int chunk = (f % CPR) ^ (r & 15);
-        src_w[j] = Wq + (int64_t)min(n0 + r, N - 1) * K + 16 * chunk;
+        if constexpr (PACKED)
+            src_w[j] = Wq + (int64_t)blockIdx.x * ns * (WR * BKB) + r * BKB + 16 * chunk;
+        else
+            src_w[j] = Wq + (int64_t)min(n0 + r, N - 1) * K + 16 * chunk;
         kc_w[j] = 16 * chunk;
     }
 #pragma unroll
@@ -114,9 +125,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     auto issue = [&](int slab, int8_t *buf) {
         const int k0 = slab * BKB;
 #pragma unroll
-        for (int j = 0; j < LW; j++)
-            dma16<NTW ? 2 : 0>(k0 + kc_w[j] < K ? src_w[j] + k0 : zero16,
-                               buf + 1024 * (wave + 4 * j));
+        for (int j = 0; j < LW; j++) {
+            const int8_t *p;
+            if constexpr (PACKED)
+                p = slab < ns ? src_w[j] + (int64_t)slab * (WR * BKB) : zero16;
+            else
+                p = k0 + kc_w[j] < K ? src_w[j] + k0 : zero16;
+            dma16<NTW ? 2 : 0>(p, buf + 1024 * (wave + 4 * j));
+        }
 #pragma unroll
         for (int j = 0; j < LX; j++)
             dma16<0>(k0 + kc_x[j] < K ? src_x[j] + k0 : zero16,
@@ -165,7 +181,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     // slab s - 1), refill slab s - 1's buffer with slab s + NS - 1, multiply.
     // The slab count is padded to a multiple of NS (padding slabs read zeros
     // and add 0), so the loop has no branches and every wait the same count.
-    const int ns = (K + BKB - 1) / BKB;
     const int nsp = (ns + NS - 1) / NS * NS;
 #pragma unroll
     for (int j = 0; j < NS - 1; j++)
@@ -244,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     }
 }
 
-template <int MT, int RG, int BKB, int NS, bool NTW>
+template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED = false>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
                       void *Y, bool out_i32, hipStream_t stream)
@@ -252,12 +267,35 @@ hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const
     const dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)));
     const dim3 block(kThreads);
     if (out_i32)
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, true>), grid, block, 0, stream, Xq,
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, true>), grid, block, 0, stream, Xq,
                            sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
     else
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, false>), grid, block, 0, stream,
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, false>), grid, block, 0, stream,
                            Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
     return hipGetLastError();
+}
+
+// Packed weight layout: block b (rows 32 b .. 32 b + 31) and slab s (bytes
+// 512 s .. 512 s + 511 of each row) form one contiguous 16 KB run at
+// ((b * KS) + s) * 16384, rows 512 bytes apart; KS = ceil(K / 512).  Rows
+// past N and bytes past K are zero.  One thread moves one 16-byte chunk.
+__global__ __launch_bounds__(256) void k_pack_weights(const int8_t *__restrict__ Wq, int N, int K,
+                                                      int KS, int64_t chunks,
+                                                      int8_t *__restrict__ Wp)
+{
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < chunks;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int c = (int)(i % (kPackBytes / 16));
+        const int r = (int)((i / (kPackBytes / 16)) % kPackRows);
+        const int64_t bs = i / (kPackBytes / 16 * kPackRows);  // b * KS + s
+        const int s = (int)(bs % KS);
+        const int64_t n = bs / KS * kPackRows + r;
+        const int64_t k = (int64_t)s * kPackBytes + 16 * c;
+        v4i v = {0, 0, 0, 0};
+        if (n < N && k < K)
+            v = *reinterpret_cast<const v4i *>(Wq + n * K + k);
+        *reinterpret_cast<v4i *>(Wp + 16 * i) = v;
+    }
 }
 
 // ZQ_SKINNY_CFG=0..8 forces one configuration (measurement aid).
@@ -305,6 +343,34 @@ hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int
     default: return ZQ_SK(2, 2, 512, 4, true);
     }
 #undef ZQ_SK
+}
+
+hipError_t launch_gemm_skinny_packed(const int8_t *Xq, const float *x_scales, const int8_t *Wp,
+                                     const float *w_scales, int64_t G, const float *bias, int act,
+                                     int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
+                                     hipStream_t stream)
+{
+    if (M <= 16)
+        return launch_cfg<1, 2, kPackBytes, 4, true, true>(Xq, x_scales, Wp, w_scales, G, bias, act,
+                                                           M, N, K, Y, out_i32, stream);
+    return launch_cfg<2, 2, kPackBytes, 4, true, true>(Xq, x_scales, Wp, w_scales, G, bias, act, M,
+                                                       N, K, Y, out_i32, stream);
+}
+
+int64_t packed_weights_bytes(int64_t N, int64_t K)
+{
+    return (N + kPackRows - 1) / kPackRows * kPackRows * ((K + kPackBytes - 1) / kPackBytes) *
+           kPackBytes;
+}
+
+hipError_t launch_pack_weights(const int8_t *Wq, int64_t N, int64_t K, int8_t *Wp,
+                               hipStream_t stream)
+{
+    const int64_t chunks = packed_weights_bytes(N, K) / 16;
+    const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 8192);
+    hipLaunchKernelGGL(k_pack_weights, dim3((unsigned)blocks), dim3(256), 0, stream, Wq, (int)N,
+                       (int)K, (int)((K + kPackBytes - 1) / kPackBytes), chunks, Wp);
+    return hipGetLastError();
 }
 
 }  // namespace zq

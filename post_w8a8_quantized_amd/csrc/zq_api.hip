@@ -189,11 +189,13 @@ ZQ_API size_t zq_linear_workspace_bytes(int64_t M, int64_t K)
            4 * kPartialsPerToken * (size_t)M;
 }
 
-ZQ_API zq_status zq_linear_w8a8(const void *X, zq_dtype x_dtype, zq_pre pre, const float *gamma,
-                                const float *beta, float eps, const int8_t *Wq,
-                                const float *w_scales, int64_t group_rows, const float *bias,
-                                zq_act act, int64_t M, int64_t N, int64_t K, void *workspace,
-                                size_t workspace_bytes, void *Y, hipStream_t stream)
+namespace {
+
+zq_status linear_impl(const void *X, zq_dtype x_dtype, zq_pre pre, const float *gamma,
+                      const float *beta, float eps, const int8_t *Wq, const float *w_scales,
+                      int64_t group_rows, const float *bias, zq_act act, int64_t M, int64_t N,
+                      int64_t K, void *workspace, size_t workspace_bytes, void *Y, bool packed,
+                      hipStream_t stream)
 {
     if (!X || !Wq || !w_scales || !Y)
         return ZQ_ERR_NULL;
@@ -214,6 +216,8 @@ ZQ_API zq_status zq_linear_w8a8(const void *X, zq_dtype x_dtype, zq_pre pre, con
     st = check_gemm(Xq, x_scales, Wq, w_scales, group_rows, act, M, N, K, Y, ZQ_F16, bias);
     if (st != ZQ_OK)
         return st;
+    if (packed && M > kSkinnyMaxM)
+        return ZQ_ERR_SHAPE;
     if (workspace_bytes < need)
         return ZQ_ERR_WORKSPACE;
     clear_stale_error();
@@ -223,8 +227,72 @@ ZQ_API zq_status zq_linear_w8a8(const void *X, zq_dtype x_dtype, zq_pre pre, con
                                      partial, stream));
     if (st != ZQ_OK)
         return st;
+    if (packed)
+        return map_hip(zq::launch_gemm_skinny_packed(Xq, x_scales, Wq, w_scales, group_rows, bias,
+                                                     (int)act, M, N, K, Y, false, stream));
     return gemm_dispatch(Xq, x_scales, Wq, w_scales, group_rows, bias, act, M, N, K, Y, ZQ_F16,
                          ZQ_PATH_AUTO, stream);
+}
+
+}  // namespace
+
+ZQ_API zq_status zq_linear_w8a8(const void *X, zq_dtype x_dtype, zq_pre pre, const float *gamma,
+                                const float *beta, float eps, const int8_t *Wq,
+                                const float *w_scales, int64_t group_rows, const float *bias,
+                                zq_act act, int64_t M, int64_t N, int64_t K, void *workspace,
+                                size_t workspace_bytes, void *Y, hipStream_t stream)
+{
+    return linear_impl(X, x_dtype, pre, gamma, beta, eps, Wq, w_scales, group_rows, bias, act, M,
+                       N, K, workspace, workspace_bytes, Y, false, stream);
+}
+
+ZQ_API zq_status zq_linear_w8a8_packed(const void *X, zq_dtype x_dtype, zq_pre pre,
+                                       const float *gamma, const float *beta, float eps,
+                                       const int8_t *Wp, const float *w_scales,
+                                       int64_t group_rows, const float *bias, zq_act act,
+                                       int64_t M, int64_t N, int64_t K, void *workspace,
+                                       size_t workspace_bytes, void *Y, hipStream_t stream)
+{
+    return linear_impl(X, x_dtype, pre, gamma, beta, eps, Wp, w_scales, group_rows, bias, act, M,
+                       N, K, workspace, workspace_bytes, Y, true, stream);
+}
+
+ZQ_API size_t zq_packed_weights_bytes(int64_t N, int64_t K)
+{
+    if (N < 1 || !k_ok(K) || N > INT32_MAX || N * K > (int64_t)1 << 40)
+        return 0;
+    return (size_t)zq::packed_weights_bytes(N, K);
+}
+
+ZQ_API zq_status zq_pack_weights(const int8_t *Wq, int64_t N, int64_t K, int8_t *Wp,
+                                 hipStream_t stream)
+{
+    if (!Wq || !Wp)
+        return ZQ_ERR_NULL;
+    if (zq_packed_weights_bytes(N, K) == 0)
+        return ZQ_ERR_SHAPE;
+    if (!aligned16(Wq) || !aligned16(Wp))
+        return ZQ_ERR_ALIGN;
+    clear_stale_error();
+    return map_hip(zq::launch_pack_weights(Wq, N, K, Wp, stream));
+}
+
+ZQ_API zq_status zq_w8a8_gemm_dequant_packed(const int8_t *Xq, const float *x_scales,
+                                             const int8_t *Wp, const float *w_scales,
+                                             int64_t group_rows, const float *bias, zq_act act,
+                                             int64_t M, int64_t N, int64_t K, void *Y,
+                                             zq_dtype y_dtype, hipStream_t stream)
+{
+    zq_status st = check_gemm(Xq, x_scales, Wp, w_scales, group_rows, act, M, N, K, Y, y_dtype,
+                              bias);
+    if (st != ZQ_OK)
+        return st;
+    if (M > kSkinnyMaxM)
+        return ZQ_ERR_SHAPE;
+    clear_stale_error();
+    return map_hip(zq::launch_gemm_skinny_packed(Xq, x_scales, Wp, w_scales, group_rows, bias,
+                                                 (int)act, M, N, K, Y, y_dtype == ZQ_I32,
+                                                 stream));
 }
 
 ZQ_API size_t zq_smoothquant_workspace_bytes(int64_t M, int64_t K)

@@ -31,6 +31,18 @@ hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int
                               int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
                               hipStream_t stream);
 
+// The same kernel reading weights in the packed layout of launch_pack_weights.
+hipError_t launch_gemm_skinny_packed(const int8_t *Xq, const float *x_scales, const int8_t *Wp,
+                                     const float *w_scales, int64_t G, const float *bias, int act,
+                                     int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
+                                     hipStream_t stream);
+
+// Offline re-layout of Wq [N x K] into 32-row x 512-byte blocks (zero padded)
+// that the weight-streaming kernel reads as contiguous 16 KB runs.
+int64_t packed_weights_bytes(int64_t N, int64_t K);
+hipError_t launch_pack_weights(const int8_t *Wq, int64_t N, int64_t K, int8_t *Wp,
+                               hipStream_t stream);
+
 // Offline group-wise weight quantization (optionally W * diag(smooth)).
 hipError_t launch_quantize_weights(const void *W, bool w_f16, const float *smooth,
                                    int64_t N, int64_t K, int64_t G, int8_t *Wq,

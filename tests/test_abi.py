@@ -26,7 +26,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = zq.exported_symbols()
-    assert len(names) == 9
+    assert len(names) == 13
     out = subprocess.run(["nm", "-D", "--defined-only", zq.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -144,6 +144,47 @@ def test_smooth_validation(L, kw, want):
     assert L.zq_smoothquant_factors(a["X"], a["xdt"], a["M"], a["K"], 1e-5, a["W"], a["wdt"],
                                     a["N"], None, None, a["s"], A, A, a["ws"], a["wsb"],
                                     None) == want
+
+
+def test_packed_weight_sizes(L):
+    # ceil(N / 32) * 32 rows by ceil(K / 512) * 512 bytes.
+    assert L.zq_packed_weights_bytes(8192, 28672) == 8192 * 28672
+    assert L.zq_packed_weights_bytes(100, 208) == 128 * 512
+    assert L.zq_packed_weights_bytes(32, 528) == 32 * 1024
+    assert L.zq_packed_weights_bytes(0, 512) == 0
+    assert L.zq_packed_weights_bytes(32, 24) == 0
+    assert L.zq_packed_weights_bytes(32, 131072 + 16) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Wq=None), NULL), (dict(Wp=None), NULL), (dict(N=0), SHAPE), (dict(K=40), SHAPE),
+    (dict(Wq=UNALIGNED), ALIGN), (dict(Wp=UNALIGNED), ALIGN),
+])
+def test_pack_validation(L, kw, want):
+    a = dict(Wq=A, N=64, K=512, Wp=A)
+    a.update(kw)
+    assert L.zq_pack_weights(a["Wq"], a["N"], a["K"], a["Wp"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Xq=None), NULL), (dict(Wp=None), NULL), (dict(M=33), SHAPE), (dict(K=24), SHAPE),
+    (dict(N=250, G=2), SHAPE), (dict(Wp=UNALIGNED), ALIGN), (dict(ydt=0), DTYPE),
+])
+def test_gemm_packed_validation(L, kw, want):
+    a = dict(Xq=A, sx=A, Wp=A, sw=A, G=128, M=16, N=256, K=256, Y=A, ydt=1)
+    a.update(kw)
+    assert L.zq_w8a8_gemm_dequant_packed(a["Xq"], a["sx"], a["Wp"], a["sw"], a["G"], None, 0,
+                                         a["M"], a["N"], a["K"], a["Y"], a["ydt"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Wp=None), NULL), (dict(M=33), SHAPE), (dict(ws=None), WS), (dict(wsb=16), WS),
+])
+def test_linear_packed_validation(L, kw, want):
+    a = dict(Wp=A, M=16, ws=A, wsb=1 << 30)
+    a.update(kw)
+    assert L.zq_linear_w8a8_packed(A, 1, 1, None, None, 1e-5, a["Wp"], A, 128, None, 0, a["M"],
+                                   256, 256, a["ws"], a["wsb"], A, None) == want
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="checks the no-GPU error path")
