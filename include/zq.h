@@ -180,9 +180,9 @@ zq_status zq_linear_w8a8(const void *X, zq_dtype x_dtype, zq_pre pre, const floa
                          void *workspace, size_t workspace_bytes, void *Y, hipStream_t stream);
 
 /* Bytes of workspace zq_linear_w8a8 needs: the int8 codes (M*K rounded up to
- * 256), the per-token scales (4*M rounded up to 256), then 256*M bytes for
- * per-segment maxima of long rows.  Returns 0 for sizes that zq_linear_w8a8
- * would reject.  Layout: codes at offset 0, scales right after the codes. */
+ * 256) then the per-token scales (4*M rounded up to 256).  Returns 0 for
+ * sizes that zq_linear_w8a8 would reject.  Layout: codes at offset 0, scales
+ * right after the codes. */
 size_t zq_linear_workspace_bytes(int64_t M, int64_t K);
 
 /*

@@ -13,10 +13,8 @@
 // mean, absmax) run on DPP without touching LDS (and through LDS only across
 // the waves of one token), and codes go out as 8-byte groups.
 //
-// Rows longer than 8192 without LayerNorm (the decode shape) are split over
-// many workgroups when a workspace is available: one kernel writes the
-// absmax of each 2048-element segment, a second reads a token's segment
-// maxima in a fixed order and quantizes its segment.
+// A few tokens with long rows (the decode shape) are spread over many
+// workgroups per row instead (see k_rowseg_quant).
 #include "zq_device.h"
 #include "zq_kernels.h"
 
@@ -206,85 +204,254 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
         sx[m] = scale;
 }
 
-// ---- Split path for long rows without LayerNorm ----
+// ---- Few tokens with long rows (the decode shape): a row over many workgroups ----
+//
+// Workgroup (seg, m) quantizes chunks [256 seg, 256 seg + 256) of token m.
+// The token's scale needs a statistic of the whole row; every workgroup of
+// the token computes it itself, over the whole row (from L2 after the first
+// touch), in the same fixed order, so all of them reach the same bits and no
+// workgroup waits for another.  That costs little because the statistic
+// needs no GeLU per element: GeLU(x) = x Phi(x) increases on [x0, inf) and
+// decreases on (-inf, x0], x0 = -0.7517915 its minimum, where it is -0.16997.
+// So when max_k x_k >= 0.3 (GeLU(0.3) = 0.185), max_k |GeLU(x_k)| is
+// GeLU(max_k x_k); otherwise it is the largest of |GeLU| at max_k x_k, at
+// L = the largest x_k <= x0 and at R = the smallest x_k > x0, found by a
+// second pass.  Without an op the statistic is max(max x, -min x); max and
+// min of fp16 rows run on packed fp16 pairs (exact).  LayerNorm needs the
+// mean, the variance about it and max |y_k|, three passes of a few flops per
+// element.
 
 constexpr int kSegThreads = 256;
-constexpr int kSegChunks = 1;                          // 8-element chunks per thread
-constexpr int kSegElems = kSegThreads * kSegChunks * 8;  // 2048 elements per segment
+constexpr int kSegElems = kSegThreads * 8;  // elements per workgroup
 
+constexpr float kGeluArgMin = -0.75179152f;
+constexpr float kGeluPosBound = 0.3f;   // GeLU(x) > max over x < 0 of |GeLU(x)| for x >= 0.3
+constexpr int64_t kRowSegMaxM = 64;     // token counts that leave most CUs idle otherwise
+constexpr int64_t kRowSegMinK = 4096;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// Running max and min of a row, loaded RB chunks per thread at a time.
 template <typename T>
-__device__ __forceinline__ void seg_load(const T *xrow, int K, int seg, int pre, float (&y)[8],
-                                         int &c)
-{
-    c = seg * (kSegElems / 8) + threadIdx.x;
-    if (c < K / 8) {
-        Chunk<T>::load(xrow + (int64_t)c * 8, y);
-        if (pre == 2) {
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                y[e] = gelu_erf(y[e]);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            y[e] = 0.0f;
-    }
-}
+struct RowMinMax;
 
-__device__ __forceinline__ float block_max(float v)
+template <>
+struct RowMinMax<_Float16> {
+    static constexpr int RB = 16;
+    using Raw = h8;
+    h2 mx = {-(_Float16)__builtin_inff(), -(_Float16)__builtin_inff()};
+    h2 mn = {(_Float16)__builtin_inff(), (_Float16)__builtin_inff()};
+    static __device__ __forceinline__ Raw load(const _Float16 *p)
+    {
+        return *reinterpret_cast<const h8 *>(p);
+    }
+    __device__ __forceinline__ void add(const Raw &v)
+    {
+        mx = __builtin_elementwise_max(mx, v.s01);
+        mx = __builtin_elementwise_max(mx, v.s23);
+        mx = __builtin_elementwise_max(mx, v.s45);
+        mx = __builtin_elementwise_max(mx, v.s67);
+        mn = __builtin_elementwise_min(mn, v.s01);
+        mn = __builtin_elementwise_min(mn, v.s23);
+        mn = __builtin_elementwise_min(mn, v.s45);
+        mn = __builtin_elementwise_min(mn, v.s67);
+    }
+    __device__ __forceinline__ float max() const { return fmaxf((float)mx.x, (float)mx.y); }
+    __device__ __forceinline__ float min() const { return fminf((float)mn.x, (float)mn.y); }
+};
+
+template <>
+struct RowMinMax<float> {
+    static constexpr int RB = 8;
+    struct Raw {
+        float4 a, b;
+    };
+    float mx = -__builtin_inff(), mn = __builtin_inff();
+    static __device__ __forceinline__ Raw load(const float *p)
+    {
+        return Raw{*reinterpret_cast<const float4 *>(p), *reinterpret_cast<const float4 *>(p + 4)};
+    }
+    __device__ __forceinline__ void add(const Raw &v)
+    {
+        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(v.a.x, v.a.y), fmaxf(v.a.z, v.a.w)),
+                             fmaxf(fmaxf(v.b.x, v.b.y), fmaxf(v.b.z, v.b.w))));
+        mn = fminf(mn, fminf(fminf(fminf(v.a.x, v.a.y), fminf(v.a.z, v.a.w)),
+                             fminf(fminf(v.b.x, v.b.y), fminf(v.b.z, v.b.w))));
+    }
+    __device__ __forceinline__ float max() const { return mx; }
+    __device__ __forceinline__ float min() const { return mn; }
+};
+
+template <bool IS_MAX>
+__device__ __forceinline__ float block_reduce(float v, float *red)
 {
-    __shared__ float red[kSegThreads / kWave];
-    v = wave_max(v);
+    v = IS_MAX ? wave_max(v) : wave_sum(v);
+    __syncthreads();  // red is reused by consecutive reductions
     if (threadIdx.x % kWave == 0)
         red[threadIdx.x / kWave] = v;
     __syncthreads();
     float r = red[0];
 #pragma unroll
     for (int w = 1; w < kSegThreads / kWave; w++)
-        r = fmaxf(r, red[w]);
+        r = IS_MAX ? fmaxf(r, red[w]) : r + red[w];
     return r;
 }
 
-// Grid (segments, M): partial[m * nseg + seg] = max |pre(x)| over the segment.
-template <typename T>
-__global__ __launch_bounds__(kSegThreads) void k_seg_absmax(const T *__restrict__ X, int K, int pre,
-                                                            float *__restrict__ partial)
+// 1-D grid of 8 * ceil(M / 8) * nseg workgroups.  Workgroup b runs on XCD
+// b % 8; token m's workgroups all get b % 8 == m % 8, so the token's row is
+// fetched into one L2 and re-read from there.
+template <typename T, int PRE>
+__global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
+    const T *__restrict__ X, int M, int K, int nseg, const float *__restrict__ gamma,
+    const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx)
 {
-    const int seg = blockIdx.x, nseg = gridDim.x;
-    const int64_t m = blockIdx.y;
-    float y[8];
-    int c;
-    seg_load(X + m * K, K, seg, pre, y, c);
-    float a = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; e++)
-        a = fmaxf(a, fabsf(y[e]));
-    a = block_max(a);
-    if (threadIdx.x == 0)
-        partial[m * nseg + seg] = a;
-}
+    __shared__ float red[kSegThreads / kWave];
+    const int j = blockIdx.x / 8;
+    const int seg = j % nseg;
+    const int64_t m = (int64_t)(j / nseg) * 8 + blockIdx.x % 8;
+    if (m >= M)
+        return;
+    const T *xrow = X + m * (int64_t)K;
+    const int nch = K / 8;
+    const int own = seg * kSegThreads + threadIdx.x;  // this thread's chunk
+    const float inf = __builtin_inff();
 
-// Grid (segments, M): token scale from the segment maxima (fixed order), then
-// the segment's codes; segment 0 stores the scale.
-template <typename T>
-__global__ __launch_bounds__(kSegThreads) void k_seg_quant(const T *__restrict__ X, int K, int pre,
-                                                           const float *__restrict__ partial,
-                                                           int8_t *__restrict__ Xq,
-                                                           float *__restrict__ sx)
-{
-    const int seg = blockIdx.x, nseg = gridDim.x;
-    const int64_t m = blockIdx.y;
-    float a = 0.0f;
-    for (int j = 0; j < nseg; j++)
-        a = fmaxf(a, partial[m * nseg + j]);
+    float mine[8];
+    if (own < nch) {
+        Chunk<T>::load(xrow + (int64_t)own * 8, mine);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            mine[e] = 0.0f;
+    }
+
+    float a, mean = 0.0f, rstd = 0.0f;
+    if constexpr (PRE == 1) {
+        float s = 0.0f;
+#pragma unroll 4
+        for (int c = threadIdx.x; c < nch; c += kSegThreads) {
+            float v[8];
+            Chunk<T>::load(xrow + (int64_t)c * 8, v);
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                s += v[e];
+        }
+        mean = block_reduce<false>(s, red) / (float)K;
+        float ss = 0.0f;
+#pragma unroll 4
+        for (int c = threadIdx.x; c < nch; c += kSegThreads) {
+            float v[8];
+            Chunk<T>::load(xrow + (int64_t)c * 8, v);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float d = v[e] - mean;
+                ss += d * d;
+            }
+        }
+        rstd = 1.0f / sqrtf(block_reduce<false>(ss, red) / (float)K + eps);
+        float amax = 0.0f;
+#pragma unroll 2
+        for (int c = threadIdx.x; c < nch; c += kSegThreads) {
+            float v[8], g[8], b[8];
+            Chunk<T>::load(xrow + (int64_t)c * 8, v);
+            if (gamma) {
+                load8(gamma + c * 8, g);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) g[e] = 1.0f;
+            }
+            if (beta) {
+                load8(beta + c * 8, b);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) b[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float ga = rstd * g[e];
+                amax = fmaxf(amax, fabsf(fmaf(v[e], ga, fmaf(-mean, ga, b[e]))));
+            }
+        }
+        a = block_reduce<true>(amax, red);
+    } else {
+        // Max and min of the row, RB chunks per thread in flight at a time.
+        using MM = RowMinMax<T>;
+        MM mm;
+        for (int base = threadIdx.x; base < nch; base += kSegThreads * MM::RB) {
+            typename MM::Raw raw[MM::RB];
+#pragma unroll
+            for (int i = 0; i < MM::RB; i++)
+                if (base + kSegThreads * i < nch)
+                    raw[i] = MM::load(xrow + (int64_t)(base + kSegThreads * i) * 8);
+#pragma unroll
+            for (int i = 0; i < MM::RB; i++)
+                if (base + kSegThreads * i < nch)
+                    mm.add(raw[i]);
+        }
+        const float xmax = block_reduce<true>(mm.max(), red);
+        if constexpr (PRE == 0) {
+            const float xmin = -block_reduce<true>(-mm.min(), red);
+            a = fmaxf(xmax, -xmin);
+        } else {
+            a = fabsf(gelu_erf(xmax));
+            if (!(xmax >= kGeluPosBound)) {
+                // The negative side may win: find L and R (uniform per token).
+                float lo = -inf, hi = inf;
+#pragma unroll 4
+                for (int c = threadIdx.x; c < nch; c += kSegThreads) {
+                    float v[8];
+                    Chunk<T>::load(xrow + (int64_t)c * 8, v);
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        lo = fmaxf(lo, v[e] <= kGeluArgMin ? v[e] : -inf);
+                        hi = fminf(hi, v[e] > kGeluArgMin ? v[e] : inf);
+                    }
+                }
+                const float L = block_reduce<true>(lo, red);
+                const float R = -block_reduce<true>(-hi, red);
+                if (L > -inf)
+                    a = fmaxf(a, fabsf(gelu_erf(L)));
+                if (R < inf)
+                    a = fmaxf(a, fabsf(gelu_erf(R)));
+            }
+        }
+    }
+
     const float scale = a / 127.0f;
     const bool fast = rcp_quant_ok(scale);
     const float rs = fast ? 1.0f / scale : 0.0f;
-    float y[8];
-    int c;
-    seg_load(X + m * K, K, seg, pre, y, c);
-    if (c < K / 8)
-        *reinterpret_cast<uint2 *>(Xq + m * K + (int64_t)c * 8) = quant8(y, scale, rs, fast);
+    if (own < nch) {
+        float y[8];
+        if constexpr (PRE == 2) {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                y[e] = gelu_erf(mine[e]);
+        } else if constexpr (PRE == 1) {
+            float g[8], b[8];
+            if (gamma) {
+                load8(gamma + own * 8, g);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) g[e] = 1.0f;
+            }
+            if (beta) {
+                load8(beta + own * 8, b);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) b[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float ga = rstd * g[e];
+                y[e] = fmaf(mine[e], ga, fmaf(-mean, ga, b[e]));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                y[e] = mine[e];
+        }
+        *reinterpret_cast<uint2 *>(Xq + m * K + (int64_t)own * 8) = quant8(y, scale, rs, fast);
+    }
     if (seg == 0 && threadIdx.x == 0)
         sx[m] = scale;
 }
@@ -318,42 +485,43 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
 
 template <typename T>
 hipError_t launch_typed(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
-                        const float *beta, float eps, int8_t *Xq, float *sx, float *partial,
-                        hipStream_t stream)
+                        const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream)
 {
+    // Few tokens with long rows: spread each row over ceil(K / 2048) workgroups.
+    if (M <= kRowSegMaxM && K >= kRowSegMinK) {
+        const int nseg = (int)((K + kSegElems - 1) / kSegElems);
+        const dim3 grid((unsigned)(8 * ((M + 7) / 8) * nseg));
+#define ZQ_ROWSEG(P)                                                                              \
+    hipLaunchKernelGGL((k_rowseg_quant<T, P>), grid, dim3(kSegThreads), 0, stream, X, (int)M,     \
+                       (int)K, nseg, gamma, beta, eps, Xq, sx)
+        if (pre == 1)
+            ZQ_ROWSEG(1);
+        else if (pre == 2)
+            ZQ_ROWSEG(2);
+        else
+            ZQ_ROWSEG(0);
+#undef ZQ_ROWSEG
+        return hipGetLastError();
+    }
     // Rows up to 64 lanes x 16 chunks x 8 = 8192 elements: one wave per token,
     // four tokens per block.
     if (K <= 8192)
         return launch_cfg<T, 1, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream);
-    // Longer rows without LayerNorm, with room for the segment maxima: split.
-    if (pre != 1 && partial) {
-        const dim3 grid((unsigned)((K + kSegElems - 1) / kSegElems), (unsigned)M);
-        hipLaunchKernelGGL(k_seg_absmax<T>, grid, dim3(kSegThreads), 0, stream, X, (int)K, pre,
-                           partial);
-        hipLaunchKernelGGL(k_seg_quant<T>, grid, dim3(kSegThreads), 0, stream, X, (int)K, pre,
-                           partial, Xq, sx);
-        return hipGetLastError();
-    }
     // Otherwise 16 waves per token.
     return launch_cfg<T, 16, 1>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream);
 }
 
 }  // namespace
 
-int64_t ln_quant_partials(int64_t K)
-{
-    return (K + kSegElems - 1) / kSegElems;
-}
-
 hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                            const float *gamma, const float *beta, float eps, int8_t *Xq,
-                           float *x_scales, float *partial, hipStream_t stream)
+                           float *x_scales, hipStream_t stream)
 {
     if (x_f16)
         return launch_typed(static_cast<const _Float16 *>(X), M, K, pre, gamma, beta, eps, Xq,
-                            x_scales, partial, stream);
+                            x_scales, stream);
     return launch_typed(static_cast<const float *>(X), M, K, pre, gamma, beta, eps, Xq, x_scales,
-                        partial, stream);
+                        stream);
 }
 
 }  // namespace zq

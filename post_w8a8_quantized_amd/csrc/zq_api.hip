@@ -146,7 +146,7 @@ ZQ_API zq_status zq_ln_quant_per_token(const void *X, zq_dtype x_dtype, int64_t 
     return map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                        pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                        pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, Xq,
-                                       x_scales, nullptr, stream));
+                                       x_scales, stream));
 }
 
 ZQ_API zq_status zq_w8a8_gemm_dequant_ex(const int8_t *Xq, const float *x_scales,
@@ -177,16 +177,13 @@ ZQ_API zq_status zq_w8a8_gemm_dequant(const int8_t *Xq, const float *x_scales, c
                                    y_dtype, ZQ_PATH_AUTO, stream);
 }
 
-// Workspace of zq_linear_w8a8: codes [M*K] | scales [M] | segment maxima [M*64],
-// each part starting on a 256-byte boundary.
-constexpr size_t kPartialsPerToken = 64;
-
+// Workspace of zq_linear_w8a8: codes [M*K] | scales [M], each part starting on
+// a 256-byte boundary.
 ZQ_API size_t zq_linear_workspace_bytes(int64_t M, int64_t K)
 {
     if (M < 1 || !k_ok(K) || M > INT32_MAX || M * K > (int64_t)1 << 40)
         return 0;
-    return round_up((size_t)(M * K), 256) + round_up(4 * (size_t)M, 256) +
-           4 * kPartialsPerToken * (size_t)M;
+    return round_up((size_t)(M * K), 256) + round_up(4 * (size_t)M, 256);
 }
 
 namespace {
@@ -205,11 +202,8 @@ zq_status linear_impl(const void *X, zq_dtype x_dtype, zq_pre pre, const float *
         return ZQ_ERR_ALIGN;
     const size_t need = zq_linear_workspace_bytes(M, K);
     const size_t codes_bytes = round_up((size_t)(M > 0 && K > 0 ? M * K : 0), 256);
-    const size_t scales_bytes = round_up(4 * (size_t)(M > 0 ? M : 0), 256);
     int8_t *Xq = static_cast<int8_t *>(workspace);
     float *x_scales = reinterpret_cast<float *>(static_cast<char *>(workspace) + codes_bytes);
-    float *partial =
-        reinterpret_cast<float *>(static_cast<char *>(workspace) + codes_bytes + scales_bytes);
     zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta, Xq, x_scales);
     if (st != ZQ_OK)
         return st;
@@ -224,7 +218,7 @@ zq_status linear_impl(const void *X, zq_dtype x_dtype, zq_pre pre, const float *
     st = map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                      pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                      pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, Xq, x_scales,
-                                     partial, stream));
+                                     stream));
     if (st != ZQ_OK)
         return st;
     if (packed)

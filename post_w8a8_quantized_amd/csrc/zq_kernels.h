@@ -9,14 +9,9 @@
 namespace zq {
 
 // Prologue: LN / GeLU / none in fp32, then per-token absmax quantization.
-// partial (optional, M * ln_quant_partials(K) floats) lets rows longer than
-// 8192 without LayerNorm be split over many workgroups.
 hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                            const float *gamma, const float *beta, float eps,
-                           int8_t *Xq, float *x_scales, float *partial, hipStream_t stream);
-
-// Segment maxima per token the split prologue path needs (at most 64).
-int64_t ln_quant_partials(int64_t K);
+                           int8_t *Xq, float *x_scales, hipStream_t stream);
 
 // Tiled MFMA GEMM (prefill shapes) with the fused dequant epilogue.
 // out_i32 selects the raw-accumulator test mode.

@@ -183,6 +183,13 @@ PROLOGUE_CASES = [
     (9, 336, ref.PRE_GELU, np.float32, False),
     (7, 16, ref.PRE_LAYERNORM, np.float16, True),     # smallest K
     (2, 131072, ref.PRE_LAYERNORM, np.float16, False),  # largest K
+    # few tokens, long rows: each row spread over ceil(K / 2048) workgroups
+    (16, 28672, ref.PRE_GELU, np.float32, False),
+    (64, 6160, ref.PRE_GELU, np.float16, False),     # ragged last segment, largest such M
+    (65, 4096, ref.PRE_GELU, np.float16, False),     # one more token: one-row-per-wave path
+    (3, 4080, ref.PRE_GELU, np.float16, False),      # just below the long-row threshold
+    (11, 12304, ref.PRE_LAYERNORM, np.float32, True),
+    (1, 131072, ref.PRE_GELU, np.float16, False),
 ]
 
 
@@ -197,6 +204,39 @@ def test_prologue(zq, M, K, pre, dt, affine):
                                  None if b is None else dev(b), 1e-5)
     assert_codes(host(q), q_ref)
     assert_scales(host(s), s_ref)
+
+
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_prologue_gelu_negative_side(zq, dt):
+    """Rows whose largest |GeLU| lies on the negative side (around GeLU's
+    minimum at x = -0.7518), including rows with no value past the minimum
+    and rows with no value before it."""
+    say("prologue gelu negative", dt.__name__)
+    rng = np.random.default_rng(11)
+    M, K = 6, 8192
+    X = -3.0 * rng.random((M, K))                      # (-3, 0]
+    X[1] = -0.5 * rng.random(K)                        # all in (x0, 0]: R decides
+    X[2] = -0.8 - 2.0 * rng.random(K)                  # all below x0: L decides
+    X[3, :] = -0.7517915                               # the minimum itself
+    X[4] = 0.25 * rng.random(K) - 1.0                  # small positives and negatives
+    X[5] = -1e-3 * rng.random(K)                       # tiny values
+    X = X.astype(dt)
+    q_ref, s_ref = ref.prologue(X, ref.PRE_GELU)
+    q, s = zq.ln_quant_per_token(dev(X), ref.PRE_GELU)
+    assert_codes(host(q), q_ref)
+    assert_scales(host(s), s_ref)
+
+
+@pytest.mark.parametrize("M,K", [(12, 20000), (1, 4096), (64, 131072)])
+def test_prologue_none_long_rows_exact(zq, M, K):
+    say("prologue none long", M, K)
+    rng = np.random.default_rng(M + K)
+    X = (rng.standard_normal((M, K)) * np.exp(2 * rng.standard_normal((M, 1)))).astype(np.float16)
+    X[0, :] = 0
+    q_ref, s_ref = ref.prologue(X, ref.PRE_NONE)
+    q, s = zq.ln_quant_per_token(dev(X), ref.PRE_NONE)
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(s), s_ref)
 
 
 @pytest.mark.parametrize("dt", [np.float16, np.float32])
@@ -302,13 +342,13 @@ def test_linear_deterministic(zq):
     (3, 8208, ref.PRE_GELU),      # one segment of 16 elements past the one-wave limit
     (16, 28672, ref.PRE_GELU),    # the decode shape: 14 full segments
     (40, 10000, ref.PRE_NONE),    # ragged last segment, tiled GEMM path
-    (5, 131072, ref.PRE_GELU),    # 64 segments, the most the workspace holds
+    (5, 131072, ref.PRE_GELU),    # 64 workgroups per row, the largest K
 ])
-def test_linear_split_prologue(zq, M, K, pre):
-    """Rows longer than 8192 without LayerNorm are quantized by the split
-    (segment-maxima) path inside zq_linear_w8a8; the codes and scales it
-    leaves in the workspace follow the same rules as the prologue's."""
-    say("split prologue", M, K, pre)
+def test_linear_long_row_prologue(zq, M, K, pre):
+    """Inside zq_linear_w8a8 the codes and scales the prologue leaves in the
+    workspace (few tokens with long rows: each row over many workgroups)
+    follow the same rules as the standalone prologue's."""
+    say("linear prologue", M, K, pre)
     rng = np.random.default_rng(M + K)
     X = (rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))).astype(np.float16)
     N, G = 64, 64
