@@ -32,6 +32,7 @@ _SIGS = {
     "zqref_f64_to_f16": (ctypes.c_uint16, [ctypes.c_double]),
     "zqref_preop": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _p]),
     "zqref_quantize_rows": (_i, [_p, _i64, _i64, _p, _p]),
+    "zqref_round_to_f16": (_i, [_p, _i64, _p]),
     "zqref_prologue": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _p, _p, _p]),
     "zqref_quantize_groups": (_i, [_p, _i64, _i64, _i64, _p, _p]),
     "zqref_smooth_factors": (_i, [_p, _i, _i64, _i64, _f, _p, _i64, _p]),
@@ -132,6 +133,21 @@ def quantize_rows(Y: np.ndarray):
     s = np.empty(M, dtype=np.float32)
     _check(lib().zqref_quantize_rows(_ptr(Y), M, K, _ptr(q), _ptr(s)), "zqref_quantize_rows")
     return q, s
+
+
+def round_to_f16(Y: np.ndarray) -> np.ndarray:
+    """fp32 values rounded once to binary16 (nearest even) and widened back to fp32."""
+    Y = np.ascontiguousarray(Y, dtype=np.float32)
+    out = np.empty_like(Y)
+    _check(lib().zqref_round_to_f16(_ptr(Y), Y.size, _ptr(out)), "zqref_round_to_f16")
+    return out
+
+
+def unfused_prologue(X: np.ndarray, pre: int, gamma=None, beta=None, eps: float = 1e-5):
+    """The unfused order (ZeroQuant reading notes, kernel-fusion figure before fusion):
+    LN/GeLU -> FP16 tensor in memory -> separate per-token quantization.
+    Returns (Xq int8 [M,K], s_x fp32 [M])."""
+    return quantize_rows(round_to_f16(preop(X, pre, gamma, beta, eps)))
 
 
 def prologue(X: np.ndarray, pre: int, gamma=None, beta=None, eps: float = 1e-5,

@@ -189,6 +189,20 @@ static float absmax_quantize(const float *v, int64_t n, int8_t *q)
     return s;
 }
 
+/* The unfused flowchart of the ZeroQuant reading notes (kernel-fusion figure,
+ * before fusion): the LN/GeLU output is written to memory as FP16 and a
+ * separate step reads it back and quantizes it.  Each fp32 value is rounded
+ * once to binary16 (nearest, ties to even) and widened back, exactly. */
+int zqref_round_to_f16(const float *Y, int64_t n, float *out)
+{
+    if ((!Y || !out) && n > 0)
+        return ZQREF_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = zqref_f16_to_f32(zqref_f64_to_f16((double)Y[i]));
+    return ZQREF_OK;
+}
+
 /* Quantize each row of Y [M x K] with its own scale (dynamic per-token). */
 int zqref_quantize_rows(const float *Y, int64_t M, int64_t K, int8_t *Xq, float *s_x)
 {

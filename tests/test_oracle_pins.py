@@ -324,6 +324,45 @@ def pin_smoothquant_identity():
     assert np.max(np.abs(lhs - rhs)) <= 1e-6 * np.max(np.abs(rhs))
 
 
+def pin_round_to_f16_against_numpy():
+    """fp32 -> binary16 (nearest even) -> fp32 against numpy's own conversion,
+    over normal, subnormal, overflowing and exactly-halfway values."""
+    rng = np.random.default_rng(21)
+    y = (rng.standard_normal(20000) * np.exp(3 * rng.standard_normal(20000))).astype(np.float32)
+    ties = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -24 * 1.5, 2.0 ** -24 * 0.5,
+                     65504.0 + 16.0, 65504.0 + 15.99, -(1 + 2.0 ** -11), 6.1e-5], dtype=np.float32)
+    y = np.concatenate([y, ties])
+    with np.errstate(over="ignore"):
+        want = y.astype(np.float16).astype(np.float32)
+    assert np.array_equal(ref.round_to_f16(y), want)
+
+
+def pin_unfused_prologue_reduces_to_fused():
+    """Without an op on fp16 input, the FP16 round trip changes nothing: the
+    unfused quantizer equals the fused one exactly."""
+    rng = np.random.default_rng(22)
+    X = (rng.standard_normal((9, 200)) * np.exp(rng.standard_normal((9, 1)))).astype(np.float16)
+    qa, sa = ref.unfused_prologue(X, ref.PRE_NONE)
+    qb, sb = ref.prologue(X, ref.PRE_NONE)
+    assert np.array_equal(qa, qb) and np.array_equal(sa, sb)
+
+
+def pin_unfused_prologue_brute_force():
+    """LN and GeLU, rounded to FP16 between the op and the quantizer, against
+    the pure-Python brute force with numpy's float16 rounding in between."""
+    rng = np.random.default_rng(23)
+    X = (rng.standard_normal((5, 48)) * 3).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(48)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(48)).astype(np.float32)
+    for pre, gg, bb in ((ref.PRE_LAYERNORM, g, b), (ref.PRE_GELU, None, None)):
+        q, s = ref.unfused_prologue(X, pre, gg, bb)
+        for m in range(X.shape[0]):
+            y = brute.preop_row(X[m], pre, gg, bb)
+            y16 = [float(np.float32(v).astype(np.float16)) for v in y]
+            qb, sb = brute.quantize_vec(y16)
+            assert list(q[m]) == qb and float(s[m]) == sb
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
