@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--rotate-mb", type=float, default=600.0,
                     help="total bytes of the rotated input sets (beyond the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the unfused-order comparison (prefill workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=5.0,
                     help="repeat full oracle passes until this much wall time has passed")
     ap.add_argument("--calib-copy-mb", type=float, default=0.0,
@@ -236,6 +238,31 @@ def main():
     del g_warm, g_steps, g_pro, g_gemm
     torch.cuda.synchronize()
 
+    # ---- fusion ablation (prefill shapes): the same layer in the unfused order
+    # (op -> fp16 -> quantizer -> int32 GEMM -> dequantizer), same rotated sets;
+    # the intermediates share one workspace.
+    ablation = None
+    if not decode and not args.no_ablation:
+        ws_unf = torch.empty(zq.linear_unfused_workspace_bytes(M, N, K), dtype=torch.uint8,
+                             device=dev)
+
+        def layer_unfused(i):
+            s = sets[i % nsets]
+            zq.linear_w8a8_unfused(s["X"], s["Wq"], s["s_w"], G, w.pre, g_arg, b_arg, w.eps,
+                                   bias, w.act, workspace=ws_unf, out=s["Y"])
+
+        for i in range(nsets):
+            layer_unfused(i)
+        g_unf = graph_of(torch, layer_unfused, args.steps)
+        time_graph(torch, g_unf)
+        unf_ms = time_graph(torch, g_unf)[0] / args.steps
+        del g_unf, ws_unf
+        torch.cuda.synchronize()
+        ablation = {"unfused_layer_step_us": round(unf_ms * 1e3, 3),
+                    "fused_layer_step_us": round(ms_step * 1e3, 3),
+                    "fusion_speedup": round(unf_ms / ms_step, 3),
+                    "unfused_order": "op->fp16, quantize, int8 GEMM->int32, dequantize"}
+
     ops = 2.0 * M * N * K
     bytes_pro = M * K * x_el + M * K + 4 * M
     bytes_gemm = M * K + 4 * M + N * K + 4 * (N // G) + (4 * N if bias is not None else 0) + 2 * M * N
@@ -309,6 +336,7 @@ def main():
                          "timed_region_wall_ms": round(ms_wall, 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "ablation": ablation,
     }
     print(json.dumps(out), flush=True)
 

@@ -230,6 +230,32 @@ zq_status zq_linear_w8a8_packed(const void *X, zq_dtype x_dtype, zq_pre pre,
                                 hipStream_t stream);
 
 /*
+ * zq_linear_w8a8_unfused -- the same layer in the unfused order, for measuring
+ * what the fusion saves (ZeroQuant reading notes, kernel-fusion figure, the
+ * flow before fusion): (1) LN/GeLU writes y as an fp16 tensor, (2) a separate
+ * kernel quantizes that tensor per token, (3) the int8 GEMM writes its int32
+ * accumulators, (4) a separate kernel dequantizes them (+ bias, + GeLU) to
+ * fp16.  Not the product path: zq_linear_w8a8 computes the fused form.
+ * Results differ from zq_linear_w8a8 only by the fp16 rounding of y between
+ * (1) and (2); steps (3)-(4) give the fused epilogue's bits for the same codes.
+ *
+ *   Arguments as zq_linear_w8a8.  workspace: zq_linear_unfused_workspace_bytes
+ *   (M, N, K) bytes, 256-byte aligned, overwritten; layout y fp16 [M x K],
+ *   codes int8 [M x K], scales fp32 [M], accumulators int32 [M x N], each at
+ *   the next 256-byte boundary.
+ */
+zq_status zq_linear_w8a8_unfused(const void *X, zq_dtype x_dtype, zq_pre pre,
+                                 const float *gamma, const float *beta, float eps,
+                                 const int8_t *Wq, const float *w_scales, int64_t group_rows,
+                                 const float *bias, zq_act act, int64_t M, int64_t N, int64_t K,
+                                 void *workspace, size_t workspace_bytes, void *Y,
+                                 hipStream_t stream);
+
+/* Bytes of workspace zq_linear_w8a8_unfused needs (see above); 0 for sizes it
+ * would reject. */
+size_t zq_linear_unfused_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * zq_smoothquant_factors -- offline SmoothQuant calibration and LayerNorm fold.
  * [SQ] 2.2: Y = (X diag(s)^-1)(diag(s) W), s per input channel; [SQ] 3.2:
  * the factors are computed offline from activation statistics.

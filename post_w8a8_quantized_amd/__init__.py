@@ -32,7 +32,9 @@ from ._binding import (  # noqa: F401
     library,
     library_path,
     linear_w8a8,
+    linear_unfused_workspace_bytes,
     linear_w8a8_packed,
+    linear_w8a8_unfused,
     linear_workspace_bytes,
     ln_quant_per_token,
     pack_weights,
@@ -47,7 +49,8 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "ACT_GELU", "ACT_NONE", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "PRE_GELU",
     "PRE_LAYERNORM", "PRE_NONE", "ZQError", "exported_symbols", "library", "library_path",
-    "linear_w8a8", "linear_w8a8_packed", "linear_workspace_bytes", "ln_quant_per_token",
+    "linear_unfused_workspace_bytes", "linear_w8a8", "linear_w8a8_packed", "linear_w8a8_unfused",
+    "linear_workspace_bytes", "ln_quant_per_token",
     "pack_weights", "packed_weights_bytes", "quantize_weights_grouped", "smoothquant_factors",
     "smoothquant_workspace_bytes", "w8a8_gemm_dequant", "w8a8_gemm_dequant_packed",
 ]

@@ -47,6 +47,9 @@ _SIGS = {
     "zq_smoothquant_workspace_bytes": (_sz, [_i64, _i64]),
     "zq_status_str": (ctypes.c_char_p, [_i]),
     "zq_packed_weights_bytes": (_sz, [_i64, _i64]),
+    "zq_linear_w8a8_unfused": (_i, [_p, _i, _i, _p, _p, _f, _p, _p, _i64, _p, _i, _i64, _i64, _i64,
+                                    _p, _sz, _p, _p]),
+    "zq_linear_unfused_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "zq_pack_weights": (_i, [_p, _i64, _i64, _p, _p]),
     "zq_w8a8_gemm_dequant_packed": (_i, [_p, _p, _p, _p, _i64, _p, _i, _i64, _i64, _i64, _p, _i,
                                          _p]),
@@ -221,6 +224,37 @@ def linear_w8a8(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor, group
     Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
     _call("zq_linear_w8a8", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps, _ptr(Wq),
           _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
+    return Y
+
+
+def linear_unfused_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(library().zq_linear_unfused_workspace_bytes(M, N, K))
+
+
+def linear_w8a8_unfused(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor,
+                        group_rows: int, pre: int = PRE_LAYERNORM, gamma=None, beta=None,
+                        eps: float = 1e-5, bias=None, act: int = ACT_NONE,
+                        workspace: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None):
+    """The layer in the unfused order (op -> fp16 -> quantize -> int32 GEMM -> dequantize),
+    for measuring the fusion gain.  The workspace holds the intermediates."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    _need(Wq, "Wq", (torch.int8,), None, X.device)
+    N = Wq.shape[0]
+    _need(w_scales, "w_scales", (torch.float32,), (N // group_rows,), X.device)
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), (N,), X.device)
+    need = linear_unfused_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _call("zq_linear_w8a8_unfused", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps,
+          _ptr(Wq), _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(workspace),
           workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
     return Y
 

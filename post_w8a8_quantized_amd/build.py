@@ -40,7 +40,8 @@ COMMON = [
     f"-I{CSRC}",
 ]
 
-SOURCES = ["zq_api.hip", "ln_quant.hip", "gemm_tiled.hip", "gemm_skinny.hip", "offline.hip"]
+SOURCES = ["zq_api.hip", "ln_quant.hip", "gemm_tiled.hip", "gemm_skinny.hip", "offline.hip",
+           "unfused.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

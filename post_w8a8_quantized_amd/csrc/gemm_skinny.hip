@@ -246,9 +246,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
                 h4 o;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    float v = (float)sum[i] * (sxm * sw[(nn + i) / G]);
-                    if (bias)
-                        v += bias[nn + i];
+                    // The tiled kernel's expression, so both give the same bits.
+                    float v = fmaf((float)sum[i], sxm * sw[(nn + i) / G], bias ? bias[nn + i] : 0.0f);
                     if (act == 1)
                         v = gelu_fast(v);
                     o[i] = (_Float16)v;

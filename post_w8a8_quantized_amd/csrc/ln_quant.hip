@@ -75,11 +75,14 @@ __device__ __forceinline__ uint2 quant8(const float (&y)[8], float s, float rs, 
 }
 
 // Block = TPB tokens x WPT waves per token.  Thread t of a token owns chunks
-// t, t + 64*WPT, ... (NCH of them).
-template <typename T, int NCH, int WPT, int TPB>
+// t, t + 64*WPT, ... (NCH of them).  With OUT_F16 the kernel stops after the
+// op and stores y as fp16 to Y16 (the unfused order, where a separate step
+// quantizes that tensor); Xq and sx are then unused.
+template <typename T, int NCH, int WPT, int TPB, bool OUT_F16 = false>
 __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
     const T *__restrict__ X, int M, int K, int pre, const float *__restrict__ gamma,
-    const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx)
+    const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx,
+    _Float16 *__restrict__ Y16)
 {
     constexpr int TT = kWave * WPT;  // threads per token
     const int wave = threadIdx.x / kWave;
@@ -178,6 +181,24 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
 #pragma unroll
             for (int e = 0; e < 8; e++)
                 y[i][e] = gelu_erf(y[i][e]);
+    }
+
+    if constexpr (OUT_F16) {
+        if (!live)
+            return;
+        _Float16 *yrow = Y16 + m * (int64_t)K;
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + TT * i;
+            if (c < nchunks) {
+                h8 h;
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    h[e] = (_Float16)y[i][e];
+                *reinterpret_cast<h8 *>(yrow + (int64_t)c * 8) = h;
+            }
+        }
+        return;
     }
 
     float a = 0.0f;
@@ -456,9 +477,10 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
         sx[m] = scale;
 }
 
-template <typename T, int WPT, int TPB>
+template <typename T, int WPT, int TPB, bool OUT_F16 = false>
 hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
-                      const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream)
+                      const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
+                      _Float16 *Y16 = nullptr)
 {
     const int64_t nchunks = K / 8;
     const int64_t per = (nchunks + kWave * WPT - 1) / (kWave * WPT);
@@ -466,8 +488,8 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
     const dim3 block(kWave * WPT * TPB);
 #define ZQ_LNQ_CASE(n)                                                                          \
     if (per <= n) {                                                                             \
-        hipLaunchKernelGGL((k_ln_quant<T, n, WPT, TPB>), grid, block, 0, stream, X, (int)M,     \
-                           (int)K, pre, gamma, beta, eps, Xq, sx);                              \
+        hipLaunchKernelGGL((k_ln_quant<T, n, WPT, TPB, OUT_F16>), grid, block, 0, stream, X,    \
+                           (int)M, (int)K, pre, gamma, beta, eps, Xq, sx, Y16);                 \
         return hipGetLastError();                                                               \
     }
     ZQ_LNQ_CASE(1)
@@ -512,6 +534,24 @@ hipError_t launch_typed(const T *X, int64_t M, int64_t K, int pre, const float *
 }
 
 }  // namespace
+
+hipError_t launch_ln_to_f16(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
+                            const float *gamma, const float *beta, float eps, _Float16 *Y16,
+                            hipStream_t stream)
+{
+    if (x_f16) {
+        const _Float16 *x = static_cast<const _Float16 *>(X);
+        return K <= 8192 ? launch_cfg<_Float16, 1, 4, true>(x, M, K, pre, gamma, beta, eps, nullptr,
+                                                           nullptr, stream, Y16)
+                         : launch_cfg<_Float16, 16, 1, true>(x, M, K, pre, gamma, beta, eps,
+                                                            nullptr, nullptr, stream, Y16);
+    }
+    const float *x = static_cast<const float *>(X);
+    return K <= 8192 ? launch_cfg<float, 1, 4, true>(x, M, K, pre, gamma, beta, eps, nullptr,
+                                                    nullptr, stream, Y16)
+                     : launch_cfg<float, 16, 1, true>(x, M, K, pre, gamma, beta, eps, nullptr,
+                                                     nullptr, stream, Y16);
+}
 
 hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                            const float *gamma, const float *beta, float eps, int8_t *Xq,

@@ -289,6 +289,66 @@ ZQ_API zq_status zq_w8a8_gemm_dequant_packed(const int8_t *Xq, const float *x_sc
                                                  stream));
 }
 
+// Workspace of zq_linear_w8a8_unfused: y fp16 [M*K] | codes [M*K] | scales [M] |
+// accumulators int32 [M*N], each part starting on a 256-byte boundary.
+ZQ_API size_t zq_linear_unfused_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 1 || N < 1 || !k_ok(K) || M > INT32_MAX || N > INT32_MAX ||
+        M * K > (int64_t)1 << 40 || M * N > (int64_t)1 << 38)
+        return 0;
+    return round_up(2 * (size_t)(M * K), 256) + round_up((size_t)(M * K), 256) +
+           round_up(4 * (size_t)M, 256) + round_up(4 * (size_t)(M * N), 256);
+}
+
+ZQ_API zq_status zq_linear_w8a8_unfused(const void *X, zq_dtype x_dtype, zq_pre pre,
+                                        const float *gamma, const float *beta, float eps,
+                                        const int8_t *Wq, const float *w_scales,
+                                        int64_t group_rows, const float *bias, zq_act act,
+                                        int64_t M, int64_t N, int64_t K, void *workspace,
+                                        size_t workspace_bytes, void *Y, hipStream_t stream)
+{
+    if (!X || !Wq || !w_scales || !Y)
+        return ZQ_ERR_NULL;
+    if (!workspace)
+        return ZQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return ZQ_ERR_ALIGN;
+    const size_t need = zq_linear_unfused_workspace_bytes(M, N, K);
+    const size_t mk = (size_t)(M > 0 && K > 0 ? M * K : 0);
+    char *ws = static_cast<char *>(workspace);
+    _Float16 *y16 = reinterpret_cast<_Float16 *>(ws);
+    int8_t *Xq = reinterpret_cast<int8_t *>(ws + round_up(2 * mk, 256));
+    float *x_scales = reinterpret_cast<float *>(ws + round_up(2 * mk, 256) + round_up(mk, 256));
+    int32_t *acc = reinterpret_cast<int32_t *>(ws + round_up(2 * mk, 256) + round_up(mk, 256) +
+                                               round_up(4 * (size_t)(M > 0 ? M : 0), 256));
+    zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta, Xq, x_scales);
+    if (st != ZQ_OK)
+        return st;
+    st = check_gemm(Xq, x_scales, Wq, w_scales, group_rows, act, M, N, K, Y, ZQ_F16, bias);
+    if (st != ZQ_OK)
+        return st;
+    if (need == 0)
+        return ZQ_ERR_SHAPE;
+    if (workspace_bytes < need)
+        return ZQ_ERR_WORKSPACE;
+    clear_stale_error();
+    st = map_hip(zq::launch_ln_to_f16(X, x_dtype == ZQ_F16, M, K, (int)pre,
+                                      pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
+                                      pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, y16, stream));
+    if (st != ZQ_OK)
+        return st;
+    st = map_hip(zq::launch_ln_quant(y16, true, M, K, ZQ_PRE_NONE, nullptr, nullptr, eps, Xq,
+                                     x_scales, stream));
+    if (st != ZQ_OK)
+        return st;
+    st = gemm_dispatch(Xq, nullptr, Wq, nullptr, group_rows, nullptr, ZQ_ACT_NONE, M, N, K, acc,
+                       ZQ_I32, ZQ_PATH_AUTO, stream);
+    if (st != ZQ_OK)
+        return st;
+    return map_hip(zq::launch_dequant(acc, x_scales, w_scales, group_rows, bias, (int)act, M, N, Y,
+                                      stream));
+}
+
 ZQ_API size_t zq_smoothquant_workspace_bytes(int64_t M, int64_t K)
 {
     if (M < 1 || !k_ok(K) || M > INT32_MAX)

@@ -13,6 +13,16 @@ hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int 
                            const float *gamma, const float *beta, float eps,
                            int8_t *Xq, float *x_scales, hipStream_t stream);
 
+// The op alone, its result stored as fp16 (the unfused order).
+hipError_t launch_ln_to_f16(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
+                            const float *gamma, const float *beta, float eps, _Float16 *Y16,
+                            hipStream_t stream);
+
+// Dequantization of int32 accumulators as its own kernel (the unfused order).
+hipError_t launch_dequant(const int32_t *acc, const float *x_scales, const float *w_scales,
+                          int64_t G, const float *bias, int act, int64_t M, int64_t N, void *Y,
+                          hipStream_t stream);
+
 // Tiled MFMA GEMM (prefill shapes) with the fused dequant epilogue.
 // out_i32 selects the raw-accumulator test mode.
 hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8_t *Wq,

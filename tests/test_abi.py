@@ -26,7 +26,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = zq.exported_symbols()
-    assert len(names) == 13
+    assert len(names) == 15
     out = subprocess.run(["nm", "-D", "--defined-only", zq.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -185,6 +185,27 @@ def test_linear_packed_validation(L, kw, want):
     a.update(kw)
     assert L.zq_linear_w8a8_packed(A, 1, 1, None, None, 1e-5, a["Wp"], A, 128, None, 0, a["M"],
                                    256, 256, a["ws"], a["wsb"], A, None) == want
+
+
+def test_unfused_workspace_sizes(L):
+    r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert L.zq_linear_unfused_workspace_bytes(4096, 3072, 768) == \
+        r(2 * 4096 * 768) + r(4096 * 768) + r(4 * 4096) + r(4 * 4096 * 3072)
+    assert L.zq_linear_unfused_workspace_bytes(3, 4, 16) == 256 * 4
+    assert L.zq_linear_unfused_workspace_bytes(3, 0, 16) == 0
+    assert L.zq_linear_unfused_workspace_bytes(3, 4, 20) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(X=None), NULL), (dict(Wq=None), NULL), (dict(ws=None), WS), (dict(wsb=4096), WS),
+    (dict(ws=A + 16), ALIGN), (dict(K=40), SHAPE), (dict(act=4), DTYPE), (dict(X=UNALIGNED), ALIGN),
+])
+def test_unfused_validation(L, kw, want):
+    a = dict(X=A, Wq=A, M=16, N=256, K=256, ws=A, wsb=1 << 30, act=0)
+    a.update(kw)
+    assert L.zq_linear_w8a8_unfused(a["X"], 1, 1, None, None, 1e-5, a["Wq"], A, 128, None,
+                                    a["act"], a["M"], a["N"], a["K"], a["ws"], a["wsb"], A,
+                                    None) == want
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="checks the no-GPU error path")
