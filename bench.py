@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the unfused-order comparison (prefill workloads)")
+    ap.add_argument("--no-ffn", action="store_true",
+                    help="skip the chained FFN block timing (bert_ffn_up)")
     ap.add_argument("--cpu-seconds", type=float, default=5.0,
                     help="repeat full oracle passes until this much wall time has passed")
     ap.add_argument("--calib-copy-mb", type=float, default=0.0,
@@ -288,6 +290,48 @@ def main():
                     "kernel": gemm_kernel, "avg_launch_us": round(gemm_ms * 1e3, 3),
                     "algorithmic_ops_per_launch": ops}
 
+    # ---- chained FFN block (BERT FFN-up shape): FFN-up then FFN-down (W2 [K x N] drawn
+    # like W), as one zq_ffn_w8a8 call against two zq_linear_w8a8 calls
+    ffn = None
+    if w.name == "bert_ffn_up" and not args.no_ffn:
+        g2 = torch.Generator(device="cpu").manual_seed(1)
+        W2 = (0.02 * torch.randn((K, N), generator=g2, dtype=torch.float32)).to(dev)
+        W2q, s_w2 = zq.quantize_weights_grouped(W2, G)
+        b2 = (0.01 * torch.randn((K,), generator=g2, dtype=torch.float32)).to(dev)
+        del W2
+        H = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ws_ffn = torch.empty(zq.ffn_workspace_bytes(M, K, N), dtype=torch.uint8, device=dev)
+        ws_lin2 = torch.empty(zq.linear_workspace_bytes(M, N), dtype=torch.uint8, device=dev)
+        Yb = [torch.empty((M, K), dtype=torch.float16, device=dev) for _ in range(nsets)]
+
+        def block_chained(i):
+            s = sets[i % nsets]
+            zq.ffn_w8a8(s["X"], s["Wq"], s["s_w"], G, W2q, s_w2, G, g_arg, b_arg, w.eps, bias, b2,
+                        workspace=ws_ffn, out=Yb[i % nsets])
+
+        def block_two_calls(i):
+            s = sets[i % nsets]
+            zq.linear_w8a8(s["X"], s["Wq"], s["s_w"], G, w.pre, g_arg, b_arg, w.eps, bias, w.act,
+                           workspace=s["ws"], out=H)
+            zq.linear_w8a8(H, W2q, s_w2, G, zq.PRE_NONE, None, None, w.eps, b2, zq.ACT_NONE,
+                           workspace=ws_lin2, out=Yb[i % nsets])
+
+        res = {}
+        for name, fn in (("chained", block_chained), ("two_calls", block_two_calls)):
+            for i in range(nsets):
+                fn(i)
+            g = graph_of(torch, fn, args.steps)
+            time_graph(torch, g)
+            res[name] = time_graph(torch, g)[0] / args.steps
+            del g
+        torch.cuda.synchronize()
+        ops_blk = 2.0 * 2.0 * M * N * K
+        ffn = {"block": f"FFN {K}->{N}->{K}, {M} tokens",
+               "chained_us": round(res["chained"] * 1e3, 3),
+               "two_calls_us": round(res["two_calls"] * 1e3, 3),
+               "chained_TOPS": round(ops_blk / (res["chained"] * 1e-3) / 1e12, 2)}
+        del ws_ffn, ws_lin2, Yb, H, W2q, s_w2, b2
+
     # ---- CPU oracle on the host cores (a reported baseline, not the target)
     cpu = None
     if not args.no_cpu_baseline:
@@ -337,6 +381,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ablation": ablation,
+        "ffn_block": ffn,
     }
     print(json.dumps(out), flush=True)
 

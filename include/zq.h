@@ -256,6 +256,33 @@ zq_status zq_linear_w8a8_unfused(const void *X, zq_dtype x_dtype, zq_pre pre,
 size_t zq_linear_unfused_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * zq_ffn_w8a8 -- a transformer FFN block, chained on one stream:
+ *   H = GeLU(s_x1 s_w1 (quant(LN(X)) W1q^T) + b1)       [M x F] fp16   (FFN-up)
+ *   Y =      s_x2 s_w2 (quant(H)     W2q^T) + b2        [M x K] fp16   (FFN-down)
+ * i.e. zq_linear_w8a8 with LayerNorm and the GeLU epilogue, then
+ * zq_linear_w8a8 without a pre-op on H ([ZQN] flowchart: LN+Quantize,
+ * GeMM+DeQuantize, GeLU, Quantize, GeMM+DeQuantize; [T36] 1.2.2).  The
+ * FFN-up GEMM's epilogue also folds max |H[m, :]| of each of its tiles into a
+ * per-token buffer (atomic max), so H's per-token quantizer needs no
+ * reduction pass; the result equals the two zq_linear_w8a8 calls bit for bit.
+ *
+ *   X [M x K] (ZQ_F16 / ZQ_F32); gamma, beta [K] or NULL; W1q [F x K] int8 with
+ *   w1_scales [F / group_rows1] and bias1 [F] or NULL; W2q [K x F] int8 with
+ *   w2_scales [K / group_rows2] and bias2 [K] or NULL; Y [M x K] fp16.
+ *   workspace  zq_ffn_workspace_bytes(M, K, F) bytes, 256-byte aligned,
+ *              overwritten (H, codes and scales of both layers).
+ * Requires each layer to meet zq_linear_w8a8's rules.
+ */
+zq_status zq_ffn_w8a8(const void *X, zq_dtype x_dtype, const float *gamma, const float *beta,
+                      float eps, const int8_t *W1q, const float *w1_scales, int64_t group_rows1,
+                      const float *bias1, const int8_t *W2q, const float *w2_scales,
+                      int64_t group_rows2, const float *bias2, int64_t M, int64_t K, int64_t F,
+                      void *workspace, size_t workspace_bytes, void *Y, hipStream_t stream);
+
+/* Bytes of workspace zq_ffn_w8a8 needs; 0 for sizes it would reject. */
+size_t zq_ffn_workspace_bytes(int64_t M, int64_t K, int64_t F);
+
+/*
  * zq_smoothquant_factors -- offline SmoothQuant calibration and LayerNorm fold.
  * [SQ] 2.2: Y = (X diag(s)^-1)(diag(s) W), s per input channel; [SQ] 3.2:
  * the factors are computed offline from activation statistics.

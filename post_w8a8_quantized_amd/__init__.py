@@ -29,6 +29,8 @@ from ._binding import (  # noqa: F401
     PRE_NONE,
     ZQError,
     exported_symbols,
+    ffn_w8a8,
+    ffn_workspace_bytes,
     library,
     library_path,
     linear_w8a8,
@@ -48,7 +50,8 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "ACT_GELU", "ACT_NONE", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "PRE_GELU",
-    "PRE_LAYERNORM", "PRE_NONE", "ZQError", "exported_symbols", "library", "library_path",
+    "PRE_LAYERNORM", "PRE_NONE", "ZQError", "exported_symbols", "ffn_w8a8", "ffn_workspace_bytes",
+    "library", "library_path",
     "linear_unfused_workspace_bytes", "linear_w8a8", "linear_w8a8_packed", "linear_w8a8_unfused",
     "linear_workspace_bytes", "ln_quant_per_token",
     "pack_weights", "packed_weights_bytes", "quantize_weights_grouped", "smoothquant_factors",

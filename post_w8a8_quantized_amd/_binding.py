@@ -50,6 +50,9 @@ _SIGS = {
     "zq_linear_w8a8_unfused": (_i, [_p, _i, _i, _p, _p, _f, _p, _p, _i64, _p, _i, _i64, _i64, _i64,
                                     _p, _sz, _p, _p]),
     "zq_linear_unfused_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "zq_ffn_w8a8": (_i, [_p, _i, _p, _p, _f, _p, _p, _i64, _p, _p, _p, _i64, _p, _i64, _i64, _i64,
+                         _p, _sz, _p, _p]),
+    "zq_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "zq_pack_weights": (_i, [_p, _i64, _i64, _p, _p]),
     "zq_w8a8_gemm_dequant_packed": (_i, [_p, _p, _p, _p, _i64, _p, _i, _i64, _i64, _i64, _p, _i,
                                          _p]),
@@ -256,6 +259,39 @@ def linear_w8a8_unfused(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tenso
     _call("zq_linear_w8a8_unfused", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps,
           _ptr(Wq), _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(workspace),
           workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
+    return Y
+
+
+def ffn_workspace_bytes(M: int, K: int, F: int) -> int:
+    return int(library().zq_ffn_workspace_bytes(M, K, F))
+
+
+def ffn_w8a8(X: torch.Tensor, W1q: torch.Tensor, w1_scales: torch.Tensor, group_rows1: int,
+             W2q: torch.Tensor, w2_scales: torch.Tensor, group_rows2: int, gamma=None, beta=None,
+             eps: float = 1e-5, bias1=None, bias2=None, workspace: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None):
+    """FFN block: H = GeLU(linear(LN(X), W1) + b1), Y = linear(H, W2) + b2, chained; fp16 [M, K]."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    _need(W1q, "W1q", (torch.int8,), None, X.device)
+    F = W1q.shape[0]
+    if W1q.shape[1] != K:
+        raise ValueError(f"W1q has K={W1q.shape[1]}, X has K={K}")
+    _need(W2q, "W2q", (torch.int8,), (K, F), X.device)
+    _need(w1_scales, "w1_scales", (torch.float32,), (F // group_rows1,), X.device)
+    _need(w2_scales, "w2_scales", (torch.float32,), (K // group_rows2,), X.device)
+    for name, t, n in (("gamma", gamma, K), ("beta", beta, K), ("bias1", bias1, F),
+                       ("bias2", bias2, K)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (n,), X.device)
+    need = ffn_workspace_bytes(M, K, F)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    Y = torch.empty((M, K), dtype=torch.float16, device=X.device) if out is None else out
+    _call("zq_ffn_w8a8", _ptr(X), _fdtype(X), _ptr(gamma), _ptr(beta), eps, _ptr(W1q),
+          _ptr(w1_scales), group_rows1, _ptr(bias1), _ptr(W2q), _ptr(w2_scales), group_rows2,
+          _ptr(bias2), M, K, F, _ptr(workspace), workspace.numel() * workspace.element_size(),
+          _ptr(Y), _stream(X))
     return Y
 
 

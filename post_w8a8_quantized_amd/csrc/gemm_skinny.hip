@@ -58,7 +58,7 @@ template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED, bool OUT_I32>
 __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int act, int M, int N,
-    int K, void *__restrict__ Y)
+    int K, void *__restrict__ Y, uint32_t *__restrict__ row_amax)
 {
     constexpr int WR = 16 * RG;            // weight rows per workgroup
     constexpr int XR = 16 * MT;            // token rows (padded to 16s)
@@ -253,6 +253,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
                     o[i] = (_Float16)v;
                 }
                 *reinterpret_cast<h4 *>(static_cast<_Float16 *>(Y) + (int64_t)m * N + nn) = o;
+                if (row_amax) {
+                    // max |fp16 output| of the row, for a per-token quantizer downstream
+                    const float r = fmaxf(fmaxf(fabsf((float)o[0]), fabsf((float)o[1])),
+                                          fmaxf(fabsf((float)o[2]), fabsf((float)o[3])));
+                    atomic_max_nonneg(row_amax + m, r);
+                }
             }
         }
     }
@@ -261,16 +267,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
 template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED = false>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
-                      void *Y, bool out_i32, hipStream_t stream)
+                      void *Y, bool out_i32, hipStream_t stream, uint32_t *row_amax = nullptr)
 {
     const dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)));
     const dim3 block(kThreads);
     if (out_i32)
         hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, true>), grid, block, 0, stream, Xq,
-                           sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
+                           sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y, row_amax);
     else
         hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, false>), grid, block, 0, stream,
-                           Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y);
+                           Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y, row_amax);
     return hipGetLastError();
 }
 
@@ -312,11 +318,11 @@ int skinny_cfg()
 hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                               const float *w_scales, int64_t G, const float *bias, int act,
                               int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
-                              hipStream_t stream)
+                              hipStream_t stream, uint32_t *row_amax)
 {
 #define ZQ_SK(MT, RG, BKB, NS, NT)                                                               \
     launch_cfg<MT, RG, BKB, NS, NT>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,        \
-                                    out_i32, stream)
+                                    out_i32, stream, row_amax)
     // 32 weight rows per workgroup (two row groups) fills 256 CUs at N = 8192.
     // Configurations: slab bytes per row x pipeline depth, nt = weight stream
     // loaded with the non-temporal policy.

@@ -121,7 +121,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                                    waves_per_simd<BM, BN, WM, WN>()))) void k_gemm_tiled(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int M, int N, int K,
-    void *__restrict__ Y, int tiles_m, int tiles_n)
+    void *__restrict__ Y, int tiles_m, int tiles_n, uint32_t *__restrict__ row_amax)
 {
     using C = Cfg<BM, BN, WM, WN, BK, NSTAGE>;
     // One LDS object per slab buffer, referenced statically from an unrolled
@@ -322,10 +322,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
         (wb == 0 ? lds0 : wb == 1 ? lds1 : wb == 2 ? lds2 : lds3) + (wave / NSTAGE) * 32 * RS;
     _Float16 *const Yh = static_cast<_Float16 *>(Y);
     const bool rows16 = (N & 7) == 0;            // 16-byte aligned rows of Y
+    // With row_amax, the tile also folds max |fp16 output| of each of its rows
+    // into row_amax[m] (float bits; an atomic max after the two lanes that
+    // hold a row have combined theirs), for a per-token quantizer downstream.
     auto epilogue = [&](auto checked) {
         constexpr bool CHECK = decltype(checked)::value;
 #pragma unroll
         for (int b = 0; b < C::FM; b++) {
+            float rmax = 0.0f;
 #pragma unroll
             for (int a = 0; a < C::FN; a++) {
 #pragma unroll
@@ -344,8 +348,19 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                             v = gelu_fast(v);
                         o[i] = (_Float16)v;
                     }
+                    if (!CHECK || n0 + nl < N) {
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            rmax = fmaxf(rmax, fabsf((float)o[i]));
+                    }
                     *reinterpret_cast<h4 *>(stage_out + frow * RS + 2 * nw) = o;
                 }
+            }
+            if (row_amax) {
+                rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+                const int m = m0 + wm * C::TWM + b * 32 + frow;
+                if (fhalf == 0 && (!CHECK || m < M))
+                    atomic_max_nonneg(row_amax + m, rmax);
             }
 #pragma unroll
             for (int j = 0; j < 32 * CPR_OUT / 64; j++) {
@@ -379,7 +394,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
 template <int BM, int BN, int WM, int WN, int BK, int NSTAGE>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
-                      void *Y, bool out_i32, hipStream_t stream)
+                      void *Y, bool out_i32, hipStream_t stream, uint32_t *row_amax)
 {
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
@@ -388,7 +403,7 @@ hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const
 #define ZQ_GEMM_LAUNCH(I32, A)                                                                    \
     hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, BK, NSTAGE, I32, A>), grid, block, 0, stream, \
                        Xq, sx, \
-                       Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y, tiles_m, tiles_n)
+                       Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y, tiles_m, tiles_n, row_amax)
     if (out_i32)
         ZQ_GEMM_LAUNCH(true, 0);
     else if (act == 1)
@@ -446,11 +461,11 @@ int pick_tile(int64_t M, int64_t N)
 hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                              const float *w_scales, int64_t G, const float *bias, int act,
                              int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
-                             hipStream_t stream)
+                             hipStream_t stream, uint32_t *row_amax)
 {
 #define ZQ_CFG(BM, BN, WM, WN, BK, NS)                                                           \
     launch_cfg<BM, BN, WM, WN, BK, NS>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,      \
-                                       out_i32, stream)
+                                       out_i32, stream, row_amax)
     switch (pick_tile(M, N)) {
     case 0: return ZQ_CFG(256, 256, 2, 2, 64, 4);
     case 1: return ZQ_CFG(256, 256, 2, 2, 128, 2);

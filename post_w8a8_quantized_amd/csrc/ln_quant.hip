@@ -18,6 +18,8 @@
 #include "zq_device.h"
 #include "zq_kernels.h"
 
+#include <algorithm>
+
 namespace zq {
 namespace {
 
@@ -82,7 +84,7 @@ template <typename T, int NCH, int WPT, int TPB, bool OUT_F16 = false>
 __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
     const T *__restrict__ X, int M, int K, int pre, const float *__restrict__ gamma,
     const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx,
-    _Float16 *__restrict__ Y16)
+    _Float16 *__restrict__ Y16, uint32_t *__restrict__ zero_rows)
 {
     constexpr int TT = kWave * WPT;  // threads per token
     const int wave = threadIdx.x / kWave;
@@ -92,6 +94,8 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
     const int64_t m = (int64_t)blockIdx.x * TPB + tok_in_blk;
     const bool live = m < M;
     const int nchunks = K / 8;
+    if (zero_rows && live && t == 0)
+        zero_rows[m] = 0u;
 
     __shared__ float red[TPB][WPT > 1 ? WPT : 1];
 
@@ -324,7 +328,8 @@ __device__ __forceinline__ float block_reduce(float v, float *red)
 template <typename T, int PRE>
 __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
     const T *__restrict__ X, int M, int K, int nseg, const float *__restrict__ gamma,
-    const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx)
+    const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx,
+    uint32_t *__restrict__ zero_rows)
 {
     __shared__ float red[kSegThreads / kWave];
     const int j = blockIdx.x / 8;
@@ -332,6 +337,8 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
     const int64_t m = (int64_t)(j / nseg) * 8 + blockIdx.x % 8;
     if (m >= M)
         return;
+    if (zero_rows && seg == 0 && threadIdx.x == 0)
+        zero_rows[m] = 0u;
     const T *xrow = X + m * (int64_t)K;
     const int nch = K / 8;
     const int own = seg * kSegThreads + threadIdx.x;  // this thread's chunk
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
 template <typename T, int WPT, int TPB, bool OUT_F16 = false>
 hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
                       const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
-                      _Float16 *Y16 = nullptr)
+                      _Float16 *Y16 = nullptr, uint32_t *zero_rows = nullptr)
 {
     const int64_t nchunks = K / 8;
     const int64_t per = (nchunks + kWave * WPT - 1) / (kWave * WPT);
@@ -489,7 +496,7 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
 #define ZQ_LNQ_CASE(n)                                                                          \
     if (per <= n) {                                                                             \
         hipLaunchKernelGGL((k_ln_quant<T, n, WPT, TPB, OUT_F16>), grid, block, 0, stream, X,    \
-                           (int)M, (int)K, pre, gamma, beta, eps, Xq, sx, Y16);                 \
+                           (int)M, (int)K, pre, gamma, beta, eps, Xq, sx, Y16, zero_rows);      \
         return hipGetLastError();                                                               \
     }
     ZQ_LNQ_CASE(1)
@@ -507,7 +514,8 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
 
 template <typename T>
 hipError_t launch_typed(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
-                        const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream)
+                        const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
+                        uint32_t *zero_rows)
 {
     // Few tokens with long rows: spread each row over ceil(K / 2048) workgroups.
     if (M <= kRowSegMaxM && K >= kRowSegMinK) {
@@ -515,7 +523,7 @@ hipError_t launch_typed(const T *X, int64_t M, int64_t K, int pre, const float *
         const dim3 grid((unsigned)(8 * ((M + 7) / 8) * nseg));
 #define ZQ_ROWSEG(P)                                                                              \
     hipLaunchKernelGGL((k_rowseg_quant<T, P>), grid, dim3(kSegThreads), 0, stream, X, (int)M,     \
-                       (int)K, nseg, gamma, beta, eps, Xq, sx)
+                       (int)K, nseg, gamma, beta, eps, Xq, sx, zero_rows)
         if (pre == 1)
             ZQ_ROWSEG(1);
         else if (pre == 2)
@@ -528,9 +536,11 @@ hipError_t launch_typed(const T *X, int64_t M, int64_t K, int pre, const float *
     // Rows up to 64 lanes x 16 chunks x 8 = 8192 elements: one wave per token,
     // four tokens per block.
     if (K <= 8192)
-        return launch_cfg<T, 1, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream);
+        return launch_cfg<T, 1, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream, nullptr,
+                                   zero_rows);
     // Otherwise 16 waves per token.
-    return launch_cfg<T, 16, 1>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream);
+    return launch_cfg<T, 16, 1>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream, nullptr,
+                                zero_rows);
 }
 
 }  // namespace
@@ -555,13 +565,49 @@ hipError_t launch_ln_to_f16(const void *X, bool x_f16, int64_t M, int64_t K, int
 
 hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                            const float *gamma, const float *beta, float eps, int8_t *Xq,
-                           float *x_scales, hipStream_t stream)
+                           float *x_scales, hipStream_t stream, uint32_t *zero_rows)
 {
     if (x_f16)
         return launch_typed(static_cast<const _Float16 *>(X), M, K, pre, gamma, beta, eps, Xq,
-                            x_scales, stream);
+                            x_scales, stream, zero_rows);
     return launch_typed(static_cast<const float *>(X), M, K, pre, gamma, beta, eps, Xq, x_scales,
-                        stream);
+                        stream, zero_rows);
+}
+
+// Codes of fp16 rows whose absmax is already known (row_amax holds the float
+// bits of max |y| per row, non-negative): s = fl32(a / 127) as the prologue
+// computes it, then the same quantizer.  One thread per 8-element chunk.
+namespace {
+__global__ __launch_bounds__(256) void k_quant_known(const _Float16 *__restrict__ Y, int M, int K,
+                                                     const uint32_t *__restrict__ row_amax,
+                                                     int8_t *__restrict__ Xq,
+                                                     float *__restrict__ sx)
+{
+    const int cpr = K / 8;
+    const int64_t total = (int64_t)M * cpr;
+    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = c / cpr;
+        const float scale = __uint_as_float(row_amax[m]) / 127.0f;
+        const bool fast = rcp_quant_ok(scale);
+        const float rs = fast ? 1.0f / scale : 0.0f;
+        float y[8];
+        Chunk<_Float16>::load(Y + c * 8, y);
+        *reinterpret_cast<uint2 *>(Xq + c * 8) = quant8(y, scale, rs, fast);
+        if (c % cpr == 0)
+            sx[m] = scale;
+    }
+}
+}  // namespace
+
+hipError_t launch_quant_known(const _Float16 *Y, int64_t M, int64_t K, const uint32_t *row_amax,
+                              int8_t *Xq, float *x_scales, hipStream_t stream)
+{
+    const int64_t total = M * (K / 8);
+    const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+    hipLaunchKernelGGL(k_quant_known, dim3((unsigned)blocks), dim3(256), 0, stream, Y, (int)M,
+                       (int)K, row_amax, Xq, x_scales);
+    return hipGetLastError();
 }
 
 }  // namespace zq

@@ -349,6 +349,84 @@ ZQ_API zq_status zq_linear_w8a8_unfused(const void *X, zq_dtype x_dtype, zq_pre 
                                       stream));
 }
 
+// Workspace of zq_ffn_w8a8: codes1 [M*K] | scales1 [M] | H fp16 [M*F] | row absmax [M] |
+// codes2 [M*F] | scales2 [M], each part starting on a 256-byte boundary.
+ZQ_API size_t zq_ffn_workspace_bytes(int64_t M, int64_t K, int64_t F)
+{
+    if (M < 1 || !k_ok(K) || !k_ok(F) || M > INT32_MAX || M * K > (int64_t)1 << 40 ||
+        M * F > (int64_t)1 << 39)
+        return 0;
+    const size_t m = (size_t)M;
+    return round_up(m * K, 256) + round_up(4 * m, 256) + round_up(2 * m * F, 256) +
+           round_up(4 * m, 256) + round_up(m * F, 256) + round_up(4 * m, 256);
+}
+
+ZQ_API zq_status zq_ffn_w8a8(const void *X, zq_dtype x_dtype, const float *gamma,
+                             const float *beta, float eps, const int8_t *W1q,
+                             const float *w1_scales, int64_t group_rows1, const float *bias1,
+                             const int8_t *W2q, const float *w2_scales, int64_t group_rows2,
+                             const float *bias2, int64_t M, int64_t K, int64_t F,
+                             void *workspace, size_t workspace_bytes, void *Y,
+                             hipStream_t stream)
+{
+    if (!X || !W1q || !w1_scales || !W2q || !w2_scales || !Y)
+        return ZQ_ERR_NULL;
+    if (!workspace)
+        return ZQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return ZQ_ERR_ALIGN;
+    const size_t need = zq_ffn_workspace_bytes(M, K, F);
+    const size_t m = (size_t)(M > 0 ? M : 0);
+    const size_t mk = m * (size_t)(K > 0 ? K : 0), mf = m * (size_t)(F > 0 ? F : 0);
+    char *ws = static_cast<char *>(workspace);
+    size_t off = 0;
+    int8_t *Xq1 = reinterpret_cast<int8_t *>(ws + off);
+    off += round_up(mk, 256);
+    float *sx1 = reinterpret_cast<float *>(ws + off);
+    off += round_up(4 * m, 256);
+    _Float16 *H = reinterpret_cast<_Float16 *>(ws + off);
+    off += round_up(2 * mf, 256);
+    uint32_t *amax = reinterpret_cast<uint32_t *>(ws + off);
+    off += round_up(4 * m, 256);
+    int8_t *Xq2 = reinterpret_cast<int8_t *>(ws + off);
+    off += round_up(mf, 256);
+    float *sx2 = reinterpret_cast<float *>(ws + off);
+    zq_status st = check_prologue(X, x_dtype, M, K, ZQ_PRE_LAYERNORM, gamma, beta, Xq1, sx1);
+    if (st != ZQ_OK)
+        return st;
+    st = check_gemm(Xq1, sx1, W1q, w1_scales, group_rows1, ZQ_ACT_GELU, M, F, K, H, ZQ_F16, bias1);
+    if (st != ZQ_OK)
+        return st;
+    st = check_gemm(Xq2, sx2, W2q, w2_scales, group_rows2, ZQ_ACT_NONE, M, K, F, Y, ZQ_F16, bias2);
+    if (st != ZQ_OK)
+        return st;
+    if (need == 0)
+        return ZQ_ERR_SHAPE;
+    if (workspace_bytes < need)
+        return ZQ_ERR_WORKSPACE;
+    clear_stale_error();
+    // FFN-up: LN + quantize (clearing the row absmax buffer on the way) ...
+    st = map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, ZQ_PRE_LAYERNORM, gamma, beta,
+                                     eps, Xq1, sx1, stream, amax));
+    if (st != ZQ_OK)
+        return st;
+    // ... GEMM + bias + GeLU, whose epilogue also folds max |H[m, :]| into amax ...
+    if (M <= kSkinnyMaxM)
+        st = map_hip(zq::launch_gemm_skinny(Xq1, sx1, W1q, w1_scales, group_rows1, bias1,
+                                            ZQ_ACT_GELU, M, F, K, H, false, stream, amax));
+    else
+        st = map_hip(zq::launch_gemm_tiled(Xq1, sx1, W1q, w1_scales, group_rows1, bias1,
+                                           ZQ_ACT_GELU, M, F, K, H, false, stream, amax));
+    if (st != ZQ_OK)
+        return st;
+    // FFN-down: quantize H with the absmax already known, then GEMM + bias.
+    st = map_hip(zq::launch_quant_known(H, M, F, amax, Xq2, sx2, stream));
+    if (st != ZQ_OK)
+        return st;
+    return gemm_dispatch(Xq2, sx2, W2q, w2_scales, group_rows2, bias2, ZQ_ACT_NONE, M, K, F, Y,
+                         ZQ_F16, ZQ_PATH_AUTO, stream);
+}
+
 ZQ_API size_t zq_smoothquant_workspace_bytes(int64_t M, int64_t K)
 {
     if (M < 1 || !k_ok(K) || M > INT32_MAX)

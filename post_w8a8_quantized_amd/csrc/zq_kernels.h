@@ -9,9 +9,16 @@
 namespace zq {
 
 // Prologue: LN / GeLU / none in fp32, then per-token absmax quantization.
+// zero_rows (optional, M entries) is cleared on the way (a per-token absmax
+// buffer that a following GEMM epilogue fills with atomics).
 hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                            const float *gamma, const float *beta, float eps,
-                           int8_t *Xq, float *x_scales, hipStream_t stream);
+                           int8_t *Xq, float *x_scales, hipStream_t stream,
+                           uint32_t *zero_rows = nullptr);
+
+// Quantization of fp16 rows whose per-row absmax (float bits) is already known.
+hipError_t launch_quant_known(const _Float16 *Y, int64_t M, int64_t K, const uint32_t *row_amax,
+                              int8_t *Xq, float *x_scales, hipStream_t stream);
 
 // The op alone, its result stored as fp16 (the unfused order).
 hipError_t launch_ln_to_f16(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
@@ -25,16 +32,18 @@ hipError_t launch_dequant(const int32_t *acc, const float *x_scales, const float
 
 // Tiled MFMA GEMM (prefill shapes) with the fused dequant epilogue.
 // out_i32 selects the raw-accumulator test mode.
+// row_amax (optional, fp16 output only): atomic max of |Y[m, :]| per row, as
+// float bits; the caller clears it first.
 hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                              const float *w_scales, int64_t G, const float *bias, int act,
                              int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
-                             hipStream_t stream);
+                             hipStream_t stream, uint32_t *row_amax = nullptr);
 
 // Weight-streaming MFMA GEMM for M <= 32 (decode shapes), same epilogue.
 hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                               const float *w_scales, int64_t G, const float *bias, int act,
                               int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
-                              hipStream_t stream);
+                              hipStream_t stream, uint32_t *row_amax = nullptr);
 
 // The same kernel reading weights in the packed layout of launch_pack_weights.
 hipError_t launch_gemm_skinny_packed(const int8_t *Xq, const float *x_scales, const int8_t *Wp,

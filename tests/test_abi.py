@@ -26,7 +26,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = zq.exported_symbols()
-    assert len(names) == 15
+    assert len(names) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", zq.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -206,6 +206,28 @@ def test_unfused_validation(L, kw, want):
     assert L.zq_linear_w8a8_unfused(a["X"], 1, 1, None, None, 1e-5, a["Wq"], A, 128, None,
                                     a["act"], a["M"], a["N"], a["K"], a["ws"], a["wsb"], A,
                                     None) == want
+
+
+def test_ffn_workspace_sizes(L):
+    r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    M, K, F = 4096, 768, 3072
+    assert L.zq_ffn_workspace_bytes(M, K, F) == \
+        r(M * K) + r(4 * M) + r(2 * M * F) + r(4 * M) + r(M * F) + r(4 * M)
+    assert L.zq_ffn_workspace_bytes(1, 16, 16) == 6 * 256
+    assert L.zq_ffn_workspace_bytes(1, 16, 24) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(X=None), NULL), (dict(W1=None), NULL), (dict(W2=None), NULL), (dict(ws=None), WS),
+    (dict(wsb=4096), WS), (dict(F=40), SHAPE), (dict(G2=100), SHAPE), (dict(G1=5), SHAPE),
+    (dict(X=UNALIGNED), ALIGN), (dict(W2=UNALIGNED), ALIGN),
+])
+def test_ffn_validation(L, kw, want):
+    a = dict(X=A, W1=A, W2=A, G1=128, G2=128, M=16, K=256, F=1024, ws=A, wsb=1 << 30)
+    a.update(kw)
+    assert L.zq_ffn_w8a8(a["X"], 1, None, None, 1e-5, a["W1"], A, a["G1"], None, a["W2"], A,
+                         a["G2"], None, a["M"], a["K"], a["F"], a["ws"], a["wsb"], A,
+                         None) == want
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="checks the no-GPU error path")
