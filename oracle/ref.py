@@ -33,6 +33,13 @@ _SIGS = {
     "zqref_preop": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _p]),
     "zqref_quantize_rows": (_i, [_p, _i64, _i64, _p, _p]),
     "zqref_round_to_f16": (_i, [_p, _i64, _p]),
+    "zqref_e4m3_to_f64": (ctypes.c_double, [ctypes.c_uint8]),
+    "zqref_f64_to_e4m3": (ctypes.c_uint8, [ctypes.c_double]),
+    "zqref_pow2_scale": (ctypes.c_float, [ctypes.c_float]),
+    "zqref_quantize_rows_fp8": (_i, [_p, _i64, _i64, _p, _p]),
+    "zqref_quantize_groups_fp8": (_i, [_p, _i64, _i64, _i64, _p, _p]),
+    "zqref_gemm_fp8": (_i, [_p, _p, _i64, _i64, _i64, _p]),
+    "zqref_epilogue_f64acc": (_i, [_p, _p, _p, _i64, _p, _i, _i64, _i64, _p]),
     "zqref_prologue": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _p, _p, _p]),
     "zqref_quantize_groups": (_i, [_p, _i64, _i64, _i64, _p, _p]),
     "zqref_smooth_factors": (_i, [_p, _i, _i64, _i64, _f, _p, _i64, _p]),
@@ -148,6 +155,75 @@ def unfused_prologue(X: np.ndarray, pre: int, gamma=None, beta=None, eps: float 
     LN/GeLU -> FP16 tensor in memory -> separate per-token quantization.
     Returns (Xq int8 [M,K], s_x fp32 [M])."""
     return quantize_rows(round_to_f16(preop(X, pre, gamma, beta, eps)))
+
+
+# ---- FP8 variant (ZeroQuant-FP: FP8 E4M3 codes, power-of-two scales) ----
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    L = lib()
+    return np.array([L.zqref_e4m3_to_f64(int(c)) for c in np.asarray(codes, np.uint8).ravel()])
+
+
+def f64_to_e4m3(v) -> np.ndarray:
+    L = lib()
+    return np.array([L.zqref_f64_to_e4m3(float(x)) for x in np.asarray(v).ravel()], np.uint8)
+
+
+def pow2_scale(a: float) -> float:
+    return float(lib().zqref_pow2_scale(float(np.float32(a))))
+
+
+def quantize_rows_fp8(Y: np.ndarray):
+    """Per-row FP8 E4M3 codes with power-of-two scales -> (uint8 codes, fp32 scales)."""
+    Y = np.ascontiguousarray(Y, dtype=np.float32)
+    M, K = Y.shape
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty(M, dtype=np.float32)
+    _check(lib().zqref_quantize_rows_fp8(_ptr(Y), M, K, _ptr(q), _ptr(s)), "zqref_quantize_rows_fp8")
+    return q, s
+
+
+def prologue_fp8(X: np.ndarray, pre: int, gamma=None, beta=None, eps: float = 1e-5):
+    """LN/GeLU in fp32 then per-token FP8 codes with power-of-two scales."""
+    return quantize_rows_fp8(preop(X, pre, gamma, beta, eps))
+
+
+def quantize_groups_fp8(W: np.ndarray, G: int):
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), dtype=np.uint8)
+    s = np.empty(N // G, dtype=np.float32)
+    _check(lib().zqref_quantize_groups_fp8(_ptr(W), N, K, G, _ptr(q), _ptr(s)),
+           "zqref_quantize_groups_fp8")
+    return q, s
+
+
+def gemm_fp8(Xq: np.ndarray, Wq: np.ndarray) -> np.ndarray:
+    """acc = dec(Xq) dec(Wq)^T summed in fp64."""
+    Xq = np.ascontiguousarray(Xq, dtype=np.uint8)
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    acc = np.empty((M, N), dtype=np.float64)
+    _check(lib().zqref_gemm_fp8(_ptr(Xq), _ptr(Wq), M, N, K, _ptr(acc)), "zqref_gemm_fp8")
+    return acc
+
+
+def epilogue_f64acc(acc: np.ndarray, s_x, s_w, G: int, bias=None, act: int = ACT_NONE):
+    acc = np.ascontiguousarray(acc, dtype=np.float64)
+    M, N = acc.shape
+    Y = np.empty((M, N), dtype=np.uint16)
+    _check(lib().zqref_epilogue_f64acc(_ptr(acc), _ptr(np.ascontiguousarray(s_x, np.float32)),
+                                       _ptr(np.ascontiguousarray(s_w, np.float32)), G,
+                                       _ptr(None if bias is None else np.ascontiguousarray(bias, np.float32)),
+                                       act, M, N, _ptr(Y)), "zqref_epilogue_f64acc")
+    return Y.view(np.float16)
+
+
+def linear_fp8(X, pre, gamma, beta, eps, Wq8, s_w, G, bias, act):
+    """The FP8 layer on all tokens -> (Y fp16, codes, scales)."""
+    q, s = prologue_fp8(X, pre, gamma, beta, eps)
+    return epilogue_f64acc(gemm_fp8(q, Wq8), s, s_w, G, bias, act), q, s
 
 
 def prologue(X: np.ndarray, pre: int, gamma=None, beta=None, eps: float = 1e-5,

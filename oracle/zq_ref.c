@@ -385,6 +385,144 @@ int zqref_epilogue(const int32_t *acc, const float *s_x, const float *s_w, int64
     return ZQREF_OK;
 }
 
+/* ---- The FP8 variant ----
+ *
+ * [T36] 2 (ZeroQuant-FP): FP8 activations; every scale factor a power of
+ * two, kept within one compute group.  Codes are the OCP 8-bit E4M3 format
+ * (1 sign bit, 4 exponent bits with bias 7, 3 fraction bits; no infinities;
+ * 0x7F and 0xFF are NaN; largest finite value 1.75 * 2^8 = 448; subnormals
+ * f/8 * 2^-6).  Reading: the scale of a vector with absmax a > 0 is the
+ * smallest power of two 2^e with a <= 448 * 2^e (nothing is clipped); a = 0
+ * gives scale 0 and all codes 0.  A value y is coded as the E4M3 value
+ * nearest to y / 2^e (an exact fp32 scaling), ties to even.
+ */
+
+double zqref_e4m3_to_f64(uint8_t c)
+{
+    const int sign = c >> 7, e = (c >> 3) & 15, f = c & 7;
+    if (e == 15 && f == 7)
+        return NAN;
+    const double v = e == 0 ? ldexp((double)f, -9)          /* f/8 * 2^-6 */
+                            : ldexp((double)(8 + f), e - 10); /* (1 + f/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* Nearest E4M3 value, ties to even; |v| above 448 saturates to 448. */
+uint8_t zqref_f64_to_e4m3(double v)
+{
+    const uint8_t sign = signbit(v) ? 0x80 : 0;
+    const double a = fabs(v);
+    if (isnan(v))
+        return 0x7f;
+    if (a >= 448.0)
+        return sign | 0x7e;
+    if (a < ldexp(1.0, -6)) {                      /* subnormal range: multiples of 2^-9 */
+        const double q = nearbyint(ldexp(a, 9));   /* exact scaling, one rounding */
+        return sign | (uint8_t)q;                  /* q == 8 encodes 2^-6 */
+    }
+    int e;
+    frexp(a, &e);                                  /* a = m 2^e, m in [0.5, 1) */
+    e -= 1;                                        /* a = m' 2^e, m' in [1, 2) */
+    double q = nearbyint(ldexp(a, 3 - e));         /* 4-bit significand, in [8, 16] */
+    if (q >= 16.0) {
+        q = 8.0;
+        e += 1;
+    }
+    if (e > 8 || (e == 8 && q > 14.0))             /* above 448 after rounding */
+        return sign | 0x7e;
+    return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
+}
+
+/* Smallest power of two 2^e with a <= 448 * 2^e (a > 0), else 0. */
+float zqref_pow2_scale(float a)
+{
+    if (!(a > 0.0f))
+        return 0.0f;
+    int e;
+    frexp((double)a, &e);          /* 2^(e-1) <= a < 2^e */
+    e -= 8;                        /* 448 * 2^e >= 256 * 2^e ... start near the answer */
+    while (448.0 * ldexp(1.0, e) < (double)a)
+        e++;
+    while (448.0 * ldexp(1.0, e - 1) >= (double)a)
+        e--;
+    return (float)ldexp(1.0, e);
+}
+
+static float pow2_quantize(const float *v, int64_t n, uint8_t *q)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; i++)
+        a = fmaxf(a, fabsf(v[i]));
+    const float s = zqref_pow2_scale(a);
+    for (int64_t i = 0; i < n; i++)
+        q[i] = s == 0.0f ? 0 : zqref_f64_to_e4m3((double)(v[i] / s));  /* exact division */
+    return s;
+}
+
+/* Per-token FP8 codes of fp32 rows. */
+int zqref_quantize_rows_fp8(const float *Y, int64_t M, int64_t K, uint8_t *q, float *s)
+{
+    if (!Y || !q || !s || M < 0 || K < 1)
+        return ZQREF_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        s[m] = pow2_quantize(Y + m * K, K, q + m * K);
+    return ZQREF_OK;
+}
+
+/* Group-wise FP8 codes of weights: G consecutive output rows by all K columns. */
+int zqref_quantize_groups_fp8(const float *W, int64_t N, int64_t K, int64_t G, uint8_t *q,
+                              float *s)
+{
+    if (!W || !q || !s || N < 1 || K < 1 || G < 1 || N % G)
+        return ZQREF_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < N / G; g++)
+        s[g] = pow2_quantize(W + g * G * K, G * K, q + g * G * K);
+    return ZQREF_OK;
+}
+
+/* acc[m,n] = sum_k dec(Xq[m,k]) dec(Wq[n,k]) in fp64 (each product is exact). */
+int zqref_gemm_fp8(const uint8_t *Xq, const uint8_t *Wq, int64_t M, int64_t N, int64_t K,
+                   double *acc)
+{
+    if (!Xq || !Wq || !acc || M < 0 || N < 1 || K < 1)
+        return ZQREF_ERR_ARG;
+    double lut[256];
+    for (int c = 0; c < 256; c++)
+        lut[c] = zqref_e4m3_to_f64((uint8_t)c);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            double t = 0.0;
+            for (int64_t k = 0; k < K; k++)
+                t += lut[Xq[m * K + k]] * lut[Wq[n * K + k]];
+            acc[m * N + n] = t;
+        }
+    return ZQREF_OK;
+}
+
+/* The dequantizing epilogue on fp64 accumulators (as zqref_epilogue). */
+int zqref_epilogue_f64acc(const double *acc, const float *s_x, const float *s_w, int64_t G,
+                          const float *bias, int act, int64_t M, int64_t N, uint16_t *Y)
+{
+    if (!acc || !s_x || !s_w || !Y || G < 1 || N % G || M < 0 || N < 1)
+        return ZQREF_ERR_ARG;
+    if (act != ACT_NONE && act != ACT_GELU)
+        return ZQREF_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            double v = (double)s_x[m] * (double)s_w[n / G] * acc[m * N + n];
+            if (bias)
+                v += (double)bias[n];
+            if (act == ACT_GELU)
+                v = gelu64(v);
+            Y[m * N + n] = zqref_f64_to_f16(v);
+        }
+    return ZQREF_OK;
+}
+
 /* ---- The whole layer on a subset of tokens ---- */
 
 /*

@@ -363,6 +363,113 @@ def pin_unfused_prologue_brute_force():
             assert list(q[m]) == qb and float(s[m]) == sb
 
 
+def _golden_e4m3():
+    dec, enc = [], []
+    for line in open(os.path.join(GOLDEN, "e4m3_values.txt"), encoding="utf-8"):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        a, b = (t.strip() for t in line.split("|"))
+        if a.startswith("="):
+            enc.append((float(a[1:]), int(b, 16)))
+        else:
+            dec.append((int(a, 16), float(b)))
+    return dec, enc
+
+
+def pin_e4m3_golden():
+    """E4M3 codes <-> values from the format definition, incl. ties to even."""
+    dec, enc = _golden_e4m3()
+    for c, v in dec:
+        got = ref.e4m3_to_f64([c])[0]
+        assert (np.isnan(v) and np.isnan(got)) or (got == v and np.signbit(got) == np.signbit(v)), c
+    for v, c in enc:
+        assert ref.f64_to_e4m3([v])[0] == c, v
+
+
+def pin_e4m3_against_torch():
+    """All 256 codes decoded, and fp32 values (random, ties, subnormals, up to 448)
+    encoded, against torch's own float8_e4m3fn conversion."""
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = ref.e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    rng = np.random.default_rng(31)
+    v = (rng.standard_normal(5000) * np.exp(2 * rng.standard_normal(5000))).astype(np.float32)
+    v = np.clip(v, -448, 448)
+    mids = ((want[:126] + want[1:127]) / 2).astype(np.float32)   # exact midpoints
+    v = np.concatenate([v, mids, -mids]).astype(np.float32)
+    tw = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ref.f64_to_e4m3(v.astype(np.float64)), tw)
+
+
+def pin_pow2_scale_properties():
+    """s = 2^e is a power of two, a <= 448 s, and s / 2 would clip (a > 224 s)."""
+    rng = np.random.default_rng(32)
+    for a in np.concatenate([np.exp(rng.uniform(-30, 30, 500)), [448.0, 448.00003, 1.0, 224.0]]):
+        a = float(np.float32(a))
+        s = ref.pow2_scale(a)
+        m, e = math.frexp(s)
+        assert m == 0.5, (a, s)
+        assert a <= 448.0 * s and a > 224.0 * s, (a, s)
+    assert ref.pow2_scale(0.0) == 0.0
+
+
+def pin_fp8_quantizer_brute_force():
+    """Each code is the nearest E4M3 value to y / s (ties to even), found by
+    searching all finite codes; the absmax element lands in (224, 448]."""
+    rng = np.random.default_rng(33)
+    Y = (rng.standard_normal((4, 64)) * np.exp(rng.standard_normal((4, 1)) * 3)).astype(np.float32)
+    Y[3] = 0
+    q, s = ref.quantize_rows_fp8(Y)
+    vals = ref.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    fin = [c for c in range(256) if not np.isnan(vals[c])]
+    for m in range(4):
+        if s[m] == 0:
+            assert np.all(q[m] == 0)
+            continue
+        for k in range(64):
+            t = float(Y[m, k]) / float(s[m])
+            best = min(fin, key=lambda c: (abs(vals[c] - t), (c & 1), c >= 128))
+            assert abs(vals[q[m, k]] - t) == abs(vals[best] - t), (m, k)
+            if abs(vals[q[m, k]] - t) == abs(vals[best] - t) and vals[q[m, k]] != vals[best]:
+                assert q[m, k] & 1 == 0          # a tie goes to the even code
+        assert 224.0 < np.max(np.abs(vals[q[m]])) <= 448.0
+
+
+def pin_fp8_gemm_exact_sums():
+    """fp64 accumulation of E4M3 products against exact rational sums."""
+    from fractions import Fraction
+    rng = np.random.default_rng(34)
+    Xq = rng.integers(0, 256, (3, 40)).astype(np.uint8)
+    Wq = rng.integers(0, 256, (5, 40)).astype(np.uint8)
+    Xq[(Xq & 0x7F) == 0x7F] = 0
+    Wq[(Wq & 0x7F) == 0x7F] = 0
+    acc = ref.gemm_fp8(Xq, Wq)
+    vals = ref.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    for m in range(3):
+        for n in range(5):
+            exact = sum(Fraction(vals[a]) * Fraction(vals[b]) for a, b in zip(Xq[m], Wq[n]))
+            assert acc[m, n] == float(exact)
+
+
+def pin_fp8_epilogue_reduces_to_int_epilogue():
+    """On integer-valued accumulators the fp64-accumulator epilogue equals the
+    int32 one exactly."""
+    rng = np.random.default_rng(35)
+    acc = rng.integers(-100000, 100000, (7, 32)).astype(np.int32)
+    s_x = (np.exp(rng.standard_normal(7)) * 0.01).astype(np.float32)
+    s_w = (np.exp(rng.standard_normal(4)) * 1e-3).astype(np.float32)
+    b = (0.1 * rng.standard_normal(32)).astype(np.float32)
+    for act in (ref.ACT_NONE, ref.ACT_GELU):
+        a = ref.epilogue(acc, s_x, s_w, 8, b, act)
+        c = ref.epilogue_f64acc(acc.astype(np.float64), s_x, s_w, 8, b, act)
+        assert np.array_equal(a.view(np.uint16), c.view(np.uint16))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
