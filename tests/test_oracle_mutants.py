@@ -26,7 +26,8 @@ MUTANTS = {
     "gelu_wrong_scale": ("return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));",
                          "return 0.5 * x * (1.0 + erf(x / 2.0));"),
     "gemm_transposed_w": ("(int64_t)Wq[n * K + k]", "(int64_t)Wq[k * N + n]"),
-    "group_index_modulo": ("(double)s_w[n / G]", "(double)s_w[n % (N / G)]"),
+    "group_index_modulo": ("(double)s_w[n / G] * (double)acc[m * N + n]",
+                           "(double)s_w[n % (N / G)] * (double)acc[m * N + n]"),
     "bias_dropped": ("                v += (double)bias[n];\n            if (act == ACT_GELU)\n                v = gelu64(v);\n            if (Y_f64)",
                      "                v += 0.0;\n            if (act == ACT_GELU)\n                v = gelu64(v);\n            if (Y_f64)"),
     "fp16_truncates": ("double q = nearbyint(ldexp(a, 10 - e));", "double q = floor(ldexp(a, 10 - e));"),
