@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the unfused-order comparison (prefill workloads)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 (E4M3, power-of-two scales) variant timing")
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip the chained FFN block timing (bert_ffn_up)")
     ap.add_argument("--cpu-seconds", type=float, default=5.0,
@@ -332,6 +334,35 @@ def main():
                "chained_TOPS": round(ops_blk / (res["chained"] * 1e-3) / 1e12, 2)}
         del ws_ffn, ws_lin2, Yb, H, W2q, s_w2, b2
 
+    # ---- FP8 variant of the same layer (E4M3 codes, power-of-two scales), weights
+    # quantized offline (and packed at decode shapes), same rotated inputs
+    fp8 = None
+    if not args.no_fp8:
+        Wd8 = torch.from_numpy(inp.W).to(dev)
+        W8, s_w8 = zq.quantize_weights_grouped_fp8(Wd8, G, smooth)
+        del Wd8
+        if decode:
+            W8 = zq.pack_weights(W8)
+        W8s = [W8] + [W8.clone() for _ in range(nsets - 1)]   # rotated like the int8 weights
+        Y8 = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+        def layer_fp8(i):
+            s = sets[i % nsets]
+            zq.linear_w8a8_fp8(s["X"], W8s[i % nsets], s_w8, G, w.pre, g_arg, b_arg, w.eps, bias,
+                               w.act, workspace=s["ws"], out=Y8, N=N, packed=decode)
+
+        for i in range(nsets):
+            layer_fp8(i)
+        g8 = graph_of(torch, layer_fp8, args.steps)
+        time_graph(torch, g8)
+        ms8 = time_graph(torch, g8)[0] / args.steps
+        del g8, W8, W8s, Y8
+        torch.cuda.synchronize()
+        fp8 = {"layer_step_us": round(ms8 * 1e3, 3),
+               "value": round((bytes_layer / (ms8 * 1e-3) / 1e9) if decode
+                              else (ops / (ms8 * 1e-3) / 1e12), 2),
+               "unit": "GB/s" if decode else "TOPS"}
+
     # ---- CPU oracle on the host cores (a reported baseline, not the target)
     cpu = None
     if not args.no_cpu_baseline:
@@ -382,6 +413,7 @@ def main():
         "cpu_baseline": cpu,
         "ablation": ablation,
         "ffn_block": ffn,
+        "fp8_variant": fp8,
     }
     print(json.dumps(out), flush=True)
 

@@ -283,6 +283,51 @@ zq_status zq_ffn_w8a8(const void *X, zq_dtype x_dtype, const float *gamma, const
 size_t zq_ffn_workspace_bytes(int64_t M, int64_t K, int64_t F);
 
 /*
+ * FP8 variant ("探秘Transformer系列之（36）--- 大模型量化方案", the ZeroQuant-FP
+ * paragraph: FP8 activations; every scale factor a power of two, kept within
+ * one compute group).  Codes are OCP 8-bit E4M3 ("FN": bias 7, no
+ * infinities, largest finite 448) stored one per byte; scales are powers of
+ * two: for a vector with absmax a > 0 the scale is the smallest 2^e with
+ * a <= 448 * 2^e (nothing clips), and a code is the E4M3 value nearest to
+ * v / 2^e (an exact scaling), ties to even; a = 0 gives scale 0 and codes 0.
+ * Activations: one scale per token, after the fused LN/GeLU (as the int8
+ * prologue).  Weights: one scale per group of G output rows (as the int8
+ * weights).  The GEMM multiplies the codes on the FP8 matrix cores with fp32
+ * accumulation (not exact, unlike the int8 path), then the same epilogue:
+ * Y = fp16(s_x[m] s_w[n / G] acc + bias[n]), optional GeLU.  Shapes,
+ * alignment and workspace rules are those of the int8 calls.
+ */
+zq_status zq_quantize_weights_grouped_fp8(const void *W, zq_dtype w_dtype, const float *smooth,
+                                          int64_t N, int64_t K, int64_t group_rows,
+                                          uint8_t *Wq8, float *w_scales, hipStream_t stream);
+
+zq_status zq_ln_quant_per_token_fp8(const void *X, zq_dtype x_dtype, int64_t M, int64_t K,
+                                    zq_pre pre, const float *gamma, const float *beta, float eps,
+                                    uint8_t *Xq8, float *x_scales, hipStream_t stream);
+
+/* y_dtype ZQ_F16 (the product) or ZQ_F32: Y receives the raw fp32
+ * accumulators (test mode; scales, bias and act ignored). */
+zq_status zq_fp8_gemm_dequant(const uint8_t *Xq8, const float *x_scales, const uint8_t *Wq8,
+                              const float *w_scales, int64_t group_rows, const float *bias,
+                              zq_act act, int64_t M, int64_t N, int64_t K, void *Y,
+                              zq_dtype y_dtype, hipStream_t stream);
+
+/* The FP8 layer; workspace as zq_linear_workspace_bytes(M, K). */
+zq_status zq_linear_w8a8_fp8(const void *X, zq_dtype x_dtype, zq_pre pre, const float *gamma,
+                             const float *beta, float eps, const uint8_t *Wq8,
+                             const float *w_scales, int64_t group_rows, const float *bias,
+                             zq_act act, int64_t M, int64_t N, int64_t K, void *workspace,
+                             size_t workspace_bytes, void *Y, hipStream_t stream);
+
+/* As zq_linear_w8a8_fp8 with the codes packed by zq_pack_weights; M <= 32. */
+zq_status zq_linear_w8a8_fp8_packed(const void *X, zq_dtype x_dtype, zq_pre pre,
+                                    const float *gamma, const float *beta, float eps,
+                                    const uint8_t *Wp8, const float *w_scales,
+                                    int64_t group_rows, const float *bias, zq_act act, int64_t M,
+                                    int64_t N, int64_t K, void *workspace,
+                                    size_t workspace_bytes, void *Y, hipStream_t stream);
+
+/*
  * zq_smoothquant_factors -- offline SmoothQuant calibration and LayerNorm fold.
  * [SQ] 2.2: Y = (X diag(s)^-1)(diag(s) W), s per input channel; [SQ] 3.2:
  * the factors are computed offline from activation statistics.

@@ -31,17 +31,21 @@ from ._binding import (  # noqa: F401
     exported_symbols,
     ffn_w8a8,
     ffn_workspace_bytes,
+    fp8_gemm_dequant,
     library,
     library_path,
     linear_w8a8,
     linear_unfused_workspace_bytes,
+    linear_w8a8_fp8,
     linear_w8a8_packed,
     linear_w8a8_unfused,
     linear_workspace_bytes,
     ln_quant_per_token,
+    ln_quant_per_token_fp8,
     pack_weights,
     packed_weights_bytes,
     quantize_weights_grouped,
+    quantize_weights_grouped_fp8,
     smoothquant_factors,
     smoothquant_workspace_bytes,
     w8a8_gemm_dequant,
@@ -51,6 +55,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "ACT_GELU", "ACT_NONE", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "PRE_GELU",
     "PRE_LAYERNORM", "PRE_NONE", "ZQError", "exported_symbols", "ffn_w8a8", "ffn_workspace_bytes",
+    "fp8_gemm_dequant", "linear_w8a8_fp8", "ln_quant_per_token_fp8", "quantize_weights_grouped_fp8",
     "library", "library_path",
     "linear_unfused_workspace_bytes", "linear_w8a8", "linear_w8a8_packed", "linear_w8a8_unfused",
     "linear_workspace_bytes", "ln_quant_per_token",

@@ -53,6 +53,13 @@ _SIGS = {
     "zq_ffn_w8a8": (_i, [_p, _i, _p, _p, _f, _p, _p, _i64, _p, _p, _p, _i64, _p, _i64, _i64, _i64,
                          _p, _sz, _p, _p]),
     "zq_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "zq_quantize_weights_grouped_fp8": (_i, [_p, _i, _p, _i64, _i64, _i64, _p, _p, _p]),
+    "zq_ln_quant_per_token_fp8": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _p, _p, _p]),
+    "zq_fp8_gemm_dequant": (_i, [_p, _p, _p, _p, _i64, _p, _i, _i64, _i64, _i64, _p, _i, _p]),
+    "zq_linear_w8a8_fp8": (_i, [_p, _i, _i, _p, _p, _f, _p, _p, _i64, _p, _i, _i64, _i64, _i64,
+                                _p, _sz, _p, _p]),
+    "zq_linear_w8a8_fp8_packed": (_i, [_p, _i, _i, _p, _p, _f, _p, _p, _i64, _p, _i, _i64, _i64,
+                                       _i64, _p, _sz, _p, _p]),
     "zq_pack_weights": (_i, [_p, _i64, _i64, _p, _p]),
     "zq_w8a8_gemm_dequant_packed": (_i, [_p, _p, _p, _p, _i64, _p, _i, _i64, _i64, _i64, _p, _i,
                                          _p]),
@@ -295,6 +302,94 @@ def ffn_w8a8(X: torch.Tensor, W1q: torch.Tensor, w1_scales: torch.Tensor, group_
     return Y
 
 
+# ---- FP8 variant: OCP E4M3 codes (torch.uint8 tensors), power-of-two scales ----
+
+def quantize_weights_grouped_fp8(W: torch.Tensor, group_rows: int,
+                                 smooth: Optional[torch.Tensor] = None):
+    """Offline group-wise FP8 codes of W [N, K] -> (uint8 codes [N, K], fp32 scales [N/G])."""
+    _need(W, "W", (torch.float32, torch.float16))
+    N, K = W.shape
+    if smooth is not None:
+        _need(smooth, "smooth", (torch.float32,), (K,), W.device)
+    Wq = torch.empty((N, K), dtype=torch.uint8, device=W.device)
+    s_w = torch.empty((max(N // group_rows, 1),), dtype=torch.float32, device=W.device)
+    _call("zq_quantize_weights_grouped_fp8", _ptr(W), _fdtype(W), _ptr(smooth), N, K, group_rows,
+          _ptr(Wq), _ptr(s_w), _stream(W))
+    return Wq, s_w
+
+
+def ln_quant_per_token_fp8(X: torch.Tensor, pre: int = PRE_LAYERNORM, gamma=None, beta=None,
+                           eps: float = 1e-5):
+    """Fused LN/GeLU + per-token FP8 codes -> (uint8 codes [M, K], fp32 power-of-two scales [M])."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    Xq = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    s_x = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _call("zq_ln_quant_per_token_fp8", _ptr(X), _fdtype(X), M, K, pre, _ptr(gamma), _ptr(beta),
+          eps, _ptr(Xq), _ptr(s_x), _stream(X))
+    return Xq, s_x
+
+
+def fp8_gemm_dequant(Xq: torch.Tensor, x_scales: Optional[torch.Tensor], Wq: torch.Tensor,
+                     w_scales: Optional[torch.Tensor], group_rows: int, bias=None,
+                     act: int = ACT_NONE, out_dtype: torch.dtype = torch.float16):
+    """FP8 GEMM + dequant -> fp16 [M, N]; out_dtype=torch.float32 returns the raw accumulators."""
+    _need(Xq, "Xq", (torch.uint8,))
+    M, K = Xq.shape
+    _need(Wq, "Wq", (torch.uint8,), None, Xq.device)
+    N = Wq.shape[0]
+    if out_dtype == torch.float16:
+        _need(x_scales, "x_scales", (torch.float32,), (M,), Xq.device)
+        _need(w_scales, "w_scales", (torch.float32,), (N // group_rows,), Xq.device)
+        ydt = F16
+    elif out_dtype == torch.float32:
+        ydt = F32
+    else:
+        raise TypeError("out_dtype must be torch.float16 or torch.float32")
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), (N,), Xq.device)
+    Y = torch.empty((M, N), dtype=out_dtype, device=Xq.device)
+    _call("zq_fp8_gemm_dequant", _ptr(Xq), _ptr(x_scales), _ptr(Wq), _ptr(w_scales), group_rows,
+          _ptr(bias), act, M, N, K, _ptr(Y), ydt, _stream(Xq))
+    return Y
+
+
+def linear_w8a8_fp8(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor, group_rows: int,
+                    pre: int = PRE_LAYERNORM, gamma=None, beta=None, eps: float = 1e-5, bias=None,
+                    act: int = ACT_NONE, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, N: Optional[int] = None,
+                    packed: bool = False):
+    """The FP8 layer -> fp16 [M, N].  With packed=True, Wq is zq_pack_weights' layout of the
+    codes (M <= 32) and N must be given."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    if packed:
+        if N is None:
+            raise ValueError("packed weights need N")
+        _need_packed(Wq.view(torch.int8), N, K, X.device)
+    else:
+        _need(Wq, "Wq", (torch.uint8,), None, X.device)
+        N = Wq.shape[0]
+    _need(w_scales, "w_scales", (torch.float32,), (N // group_rows,), X.device)
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), (N,), X.device)
+    need = linear_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _call("zq_linear_w8a8_fp8_packed" if packed else "zq_linear_w8a8_fp8", _ptr(X), _fdtype(X),
+          pre, _ptr(gamma), _ptr(beta), eps, _ptr(Wq), _ptr(w_scales), group_rows, _ptr(bias),
+          act, M, N, K, _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(Y),
+          _stream(X))
+    return Y
+
+
 def packed_weights_bytes(N: int, K: int) -> int:
     return int(library().zq_packed_weights_bytes(N, K))
 
@@ -303,13 +398,13 @@ def pack_weights(Wq: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.
     """Offline re-layout of Wq int8 [N, K] into the packed layout zq.h defines
     (32-row x 512-byte blocks); returns a 1-D int8 tensor of
     packed_weights_bytes(N, K) bytes.  The packed calls take N explicitly."""
-    _need(Wq, "Wq", (torch.int8,))
+    _need(Wq, "Wq", (torch.int8, torch.uint8))
     N, K = Wq.shape
     nbytes = packed_weights_bytes(N, K)
     if nbytes == 0:
         raise ZQError("zq_pack_weights", 2)
-    Wp = torch.empty((nbytes,), dtype=torch.int8, device=Wq.device) if out is None else out
-    _need(Wp, "Wp", (torch.int8,), (nbytes,), Wq.device)
+    Wp = torch.empty((nbytes,), dtype=Wq.dtype, device=Wq.device) if out is None else out
+    _need(Wp, "Wp", (torch.int8, torch.uint8), (nbytes,), Wq.device)
     _call("zq_pack_weights", _ptr(Wq), N, K, _ptr(Wp), _stream(Wq))
     return Wp
 

@@ -54,7 +54,10 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED, bool OUT_I32>
+// F8: the operands are OCP E4M3 codes and the product is
+// v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales), accumulating in fp32;
+// OUT_I32 then writes the raw fp32 accumulators.
+template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED, bool OUT_I32, bool F8 = false>
 __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int act, int M, int N,
@@ -69,7 +72,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     static_assert(CPR >= 16 && (XR * CPR) % 256 == 0, "DMAs split evenly over the four waves");
     constexpr int PER_WAVE = LW + LX;
     constexpr int STAGE = ROWS * BKB;
-    constexpr int KB = BKB / 64;           // 64-byte MFMA k blocks per slab
+    constexpr int KB = BKB / (F8 ? 128 : 64);  // MFMA k blocks per slab (64 or 128 bytes)
+    static_assert(KB % 4 == 0, "the four waves share each slab's k blocks evenly");
+    using Acc = std::conditional_t<F8, v4f, v4i>;
+    using Frag = std::conditional_t<F8, v8i, v4i>;
     static_assert(NS >= 2 && NS <= 8, "pipeline depth");
     static_assert(4 * RG * MT * 64 * 16 <= STAGE, "partial sums fit in one slab buffer");
     static_assert(!PACKED || (WR == kPackRows && BKB == kPackBytes), "packed blocks are slabs");
@@ -144,31 +150,55 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     const int r16 = lane & 15;
     const int kq = lane >> 4;
 
-    v4i acc[RG][MT];
+    Acc acc[RG][MT];
 #pragma unroll
     for (int g = 0; g < RG; g++)
 #pragma unroll
         for (int t = 0; t < MT; t++)
-            acc[g][t] = v4i{0, 0, 0, 0};
+            acc[g][t] = Acc{};
 
     // Wave w takes k blocks w, w + 4, ... of each slab.
     auto compute = [&](const int8_t *buf) {
 #pragma unroll
         for (int i = 0; i < KB / 4; i++) {
             const int kb = wave + 4 * i;
-            const int off = 16 * ((4 * kb + kq) ^ r16);
-            v4i a[RG], b[MT];
+            Frag a[RG], b[MT];
+            if constexpr (F8) {
+                // lane (r16, kq) holds bytes 32 kq .. +32 of the 128-byte block: chunks
+                // 8 kb + 2 kq and the next, each at its own swizzled slot
+                const int c0 = 8 * kb + 2 * kq;
+                const int off0 = 16 * (c0 ^ r16), off1 = 16 * ((c0 + 1) ^ r16);
+                auto two = [&](const int8_t *row) {
+                    const v4i lo = *reinterpret_cast<const v4i *>(row + off0);
+                    const v4i hi = *reinterpret_cast<const v4i *>(row + off1);
+                    return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                };
 #pragma unroll
-            for (int g = 0; g < RG; g++)
-                a[g] = *reinterpret_cast<const v4i *>(buf + (16 * g + r16) * BKB + off);
-#pragma unroll
-            for (int t = 0; t < MT; t++)
-                b[t] = *reinterpret_cast<const v4i *>(buf + (WR + 16 * t + r16) * BKB + off);
-#pragma unroll
-            for (int g = 0; g < RG; g++)
+                for (int g = 0; g < RG; g++)
+                    a[g] = two(buf + (16 * g + r16) * BKB);
 #pragma unroll
                 for (int t = 0; t < MT; t++)
-                    acc[g][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[g], b[t], acc[g][t], 0, 0, 0);
+                    b[t] = two(buf + (WR + 16 * t + r16) * BKB);
+            } else {
+                const int off = 16 * ((4 * kb + kq) ^ r16);
+#pragma unroll
+                for (int g = 0; g < RG; g++)
+                    a[g] = *reinterpret_cast<const v4i *>(buf + (16 * g + r16) * BKB + off);
+#pragma unroll
+                for (int t = 0; t < MT; t++)
+                    b[t] = *reinterpret_cast<const v4i *>(buf + (WR + 16 * t + r16) * BKB + off);
+            }
+#pragma unroll
+            for (int g = 0; g < RG; g++)
+#pragma unroll
+                for (int t = 0; t < MT; t++) {
+                    if constexpr (F8)
+                        acc[g][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            a[g], b[t], acc[g][t], 0, 0, 0, 127, 0, 127);
+                    else
+                        acc[g][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[g], b[t], acc[g][t], 0,
+                                                                          0, 0);
+                }
         }
     };
     auto barrier = [] {
@@ -214,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     barrier();
 
     // Partial sums of the four waves go through buf0 (free now).
-    v4i *part = reinterpret_cast<v4i *>(buf0);   // [wave][g][t][lane]
+    Acc *part = reinterpret_cast<Acc *>(buf0);   // [wave][g][t][lane]
 #pragma unroll
     for (int g = 0; g < RG; g++)
 #pragma unroll
@@ -231,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
             continue;
 #pragma unroll
         for (int t = 0; t < MT; t++) {
-            v4i sum = part[((0 * RG + g) * MT + t) * kWave + lane];
+            Acc sum = part[((0 * RG + g) * MT + t) * kWave + lane];
 #pragma unroll
             for (int w = 1; w < 4; w++)
                 sum += part[((w * RG + g) * MT + t) * kWave + lane];
@@ -240,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
             if (m >= M || nn >= N)
                 continue;
             if constexpr (OUT_I32) {
-                *reinterpret_cast<v4i *>(static_cast<int32_t *>(Y) + (int64_t)m * N + nn) = sum;
+                *reinterpret_cast<Acc *>(static_cast<int32_t *>(Y) + (int64_t)m * N + nn) = sum;
             } else {
                 const float sxm = sx[m];
                 h4 o;
@@ -264,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     }
 }
 
-template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED = false>
+template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED = false, bool F8 = false>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
                       void *Y, bool out_i32, hipStream_t stream, uint32_t *row_amax = nullptr)
@@ -272,10 +302,10 @@ hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const
     const dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)));
     const dim3 block(kThreads);
     if (out_i32)
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, true>), grid, block, 0, stream, Xq,
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, true, F8>), grid, block, 0, stream, Xq,
                            sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y, row_amax);
     else
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, false>), grid, block, 0, stream,
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, false, F8>), grid, block, 0, stream,
                            Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y, row_amax);
     return hipGetLastError();
 }
@@ -360,6 +390,20 @@ hipError_t launch_gemm_skinny_packed(const int8_t *Xq, const float *x_scales, co
                                                            M, N, K, Y, out_i32, stream);
     return launch_cfg<2, 2, kPackBytes, 4, true, true>(Xq, x_scales, Wp, w_scales, G, bias, act, M,
                                                        N, K, Y, out_i32, stream);
+}
+
+hipError_t launch_gemm_skinny_fp8(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                  const float *w_scales, int64_t G, const float *bias, int act,
+                                  int64_t M, int64_t N, int64_t K, void *Y, bool out_raw,
+                                  bool packed, hipStream_t stream)
+{
+#define ZQ_SK8(MT, P)                                                                             \
+    launch_cfg<MT, 2, kPackBytes, 4, true, P, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M,   \
+                                                     N, K, Y, out_raw, stream)
+    if (packed)
+        return M <= 16 ? ZQ_SK8(1, true) : ZQ_SK8(2, true);
+    return M <= 16 ? ZQ_SK8(1, false) : ZQ_SK8(2, false);
+#undef ZQ_SK8
 }
 
 int64_t packed_weights_bytes(int64_t N, int64_t K)

@@ -115,7 +115,10 @@ constexpr int waves_per_simd()
     return (WM * WN == 8 || BM * BN < 256 * 128) ? 2 : 1;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool OUT_I32, int ACT>
+// F8: the operands are OCP E4M3 codes and the product is
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) accumulating in fp32;
+// OUT_I32 then writes the raw fp32 accumulators.
+template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool OUT_I32, int ACT, bool F8>
 __global__ __launch_bounds__(WM *WN * 64)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                                    waves_per_simd<BM, BN, WM, WN>()))) void k_gemm_tiled(
@@ -195,21 +198,43 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
     const int xbase = (wm * C::TWM + frow) * BK;
     const int wbase = BM * BK + (wn * C::TWN + frow) * BK;
 
-    v16i acc[C::FN][C::FM];
+    // int8: a k-step is 32 bytes of K, lane (frow, fhalf) holds bytes 16 fhalf .. +16
+    // (one chunk).  FP8: a k-step is 64 bytes, lane holds bytes 32 fhalf .. +32 (two
+    // chunks, each at its own swizzled position).
+    constexpr int KS = F8 ? BK / 64 : BK / 32;
+    using Acc = std::conditional_t<F8, v16f, v16i>;
+    using Frag = std::conditional_t<F8, v8i, v4i>;
+    Acc acc[C::FN][C::FM];
 #pragma unroll
     for (int a = 0; a < C::FN; a++)
 #pragma unroll
         for (int b = 0; b < C::FM; b++)
-            acc[a][b] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+            acc[a][b] = Acc{};
 
-    auto load_frags = [&](const int8_t *stage, int ks, v4i (&fx)[C::FM], v4i (&fw)[C::FN]) {
-        const int off = ((2 * ks + fhalf) ^ sw_l) << 4;
+    auto load_frags = [&](const int8_t *stage, int ks, Frag (&fx)[C::FM], Frag (&fw)[C::FN]) {
+        if constexpr (F8) {
+            const int c0 = 4 * ks + 2 * fhalf;
+            const int off0 = (c0 ^ sw_l) << 4, off1 = ((c0 + 1) ^ sw_l) << 4;
+            auto two = [&](const int8_t *row) {
+                const v4i lo = *reinterpret_cast<const v4i *>(row + off0);
+                const v4i hi = *reinterpret_cast<const v4i *>(row + off1);
+                return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            };
 #pragma unroll
-        for (int b = 0; b < C::FM; b++)
-            fx[b] = *reinterpret_cast<const v4i *>(stage + xbase + b * 32 * BK + off);
+            for (int b = 0; b < C::FM; b++)
+                fx[b] = two(stage + xbase + b * 32 * BK);
 #pragma unroll
-        for (int a = 0; a < C::FN; a++)
-            fw[a] = *reinterpret_cast<const v4i *>(stage + wbase + a * 32 * BK + off);
+            for (int a = 0; a < C::FN; a++)
+                fw[a] = two(stage + wbase + a * 32 * BK);
+        } else {
+            const int off = ((2 * ks + fhalf) ^ sw_l) << 4;
+#pragma unroll
+            for (int b = 0; b < C::FM; b++)
+                fx[b] = *reinterpret_cast<const v4i *>(stage + xbase + b * 32 * BK + off);
+#pragma unroll
+            for (int a = 0; a < C::FN; a++)
+                fw[a] = *reinterpret_cast<const v4i *>(stage + wbase + a * 32 * BK + off);
+        }
     };
 
     int8_t *const bufs[4] = {lds0, lds1, lds2, lds3};
@@ -236,7 +261,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
     wait_vmcnt<(NSTAGE - 1) * PER_SLAB>();
     barrier();
 
-    v4i fx[2][C::FM], fw[2][C::FN];
+    Frag fx[2][C::FM], fw[2][C::FN];
     load_frags(bufs[0], 0, fx[0], fw[0]);
 
     // One slab: KS MFMA k-steps.  The LDS reads for the next k-step are issued
@@ -247,8 +272,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
     auto slab = [&](int kt, auto S) {
         constexpr int s = decltype(S)::value;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ks++) {
-            if (ks + 1 < C::KS) {
+        for (int ks = 0; ks < KS; ks++) {
+            if (ks + 1 < KS) {
                 // The reads feeding this k-step were issued a k-step ago and have
                 // returned; waiting for them here, before the next reads go out,
                 // lets the MFMAs below start without an LDS wait.
@@ -265,12 +290,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
             for (int a = 0; a < C::FN; a++)
 #pragma unroll
                 for (int b = 0; b < C::FM; b++)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[ks & 1][a], fx[ks & 1][b],
-                                                                      acc[a][b], 0, 0, 0);
+                    if constexpr (F8)
+                        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fw[ks & 1][a], fx[ks & 1][b], acc[a][b], 0, 0, 0, 127, 0, 127);
+                    else
+                        acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            fw[ks & 1][a], fx[ks & 1][b], acc[a][b], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    static_assert(C::KS % 2 == 0, "fragment buffers alternate within a slab");
+    static_assert(KS % 2 == 0, "fragment buffers alternate within a slab");
     for (int kt = 0; kt < nkp; kt += NSTAGE) {
         slab(kt, std::integral_constant<int, 0>{});
         slab(kt + 1, std::integral_constant<int, 1>{});
@@ -299,9 +328,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                     const int n = n0 + wn * C::TWN + a * 32 + 8 * q + 4 * fhalf;
                     if (m >= M || n >= N)
                         continue;
-                    v4i o = {acc[a][b][4 * q + 0], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
-                             acc[a][b][4 * q + 3]};
-                    *reinterpret_cast<v4i *>(static_cast<int32_t *>(Y) + (int64_t)m * N + n) = o;
+                    using Raw4 = std::conditional_t<F8, v4f, v4i>;
+                    const Raw4 o = {acc[a][b][4 * q + 0], acc[a][b][4 * q + 1],
+                                    acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
+                    *reinterpret_cast<Raw4 *>(static_cast<int32_t *>(Y) + (int64_t)m * N + n) = o;
                 }
         }
         return;
@@ -391,7 +421,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
         epilogue(std::true_type{});
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NSTAGE>
+template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool F8 = false>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
                       void *Y, bool out_i32, hipStream_t stream, uint32_t *row_amax)
@@ -401,7 +431,8 @@ hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const
     const dim3 grid((unsigned)(tiles_m * tiles_n));
     const dim3 block(WM * WN * 64);
 #define ZQ_GEMM_LAUNCH(I32, A)                                                                    \
-    hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, BK, NSTAGE, I32, A>), grid, block, 0, stream, \
+    hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, BK, NSTAGE, I32, A, F8>), grid, block, 0,     \
+                       stream,                                                                    \
                        Xq, sx, \
                        Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y, tiles_m, tiles_n, row_amax)
     if (out_i32)
@@ -477,6 +508,25 @@ hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8
     default: return ZQ_CFG(128, 128, 2, 2, 64, 4);
     }
 #undef ZQ_CFG
+}
+
+hipError_t launch_gemm_tiled_fp8(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                 const float *w_scales, int64_t G, const float *bias, int act,
+                                 int64_t M, int64_t N, int64_t K, void *Y, bool out_raw,
+                                 hipStream_t stream)
+{
+    // FP8 k-steps are 64 bytes: only the 128-byte slab configurations apply
+    // (two k-steps per slab).  The FP8 fragments are twice as wide, so the
+    // 256x256 tile would not fit the registers of two waves per SIMD: its
+    // problems take 256x192; 128x128 covers small problems.
+#define ZQ_CFG8(BM, BN, WM, WN)                                                                   \
+    launch_cfg<BM, BN, WM, WN, 128, 2, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K,   \
+                                             Y, out_raw, stream, nullptr)
+    const int t = pick_tile(M, N);
+    if (t == 6 || t == 7)
+        return ZQ_CFG8(256, 192, 4, 2);
+    return ZQ_CFG8(128, 128, 2, 2);
+#undef ZQ_CFG8
 }
 
 }  // namespace zq

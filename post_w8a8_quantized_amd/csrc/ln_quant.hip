@@ -76,11 +76,22 @@ __device__ __forceinline__ uint2 quant8(const float (&y)[8], float s, float rs, 
     return packed;
 }
 
+// FP8 codes of 8 values with power-of-two scale 2^e (all 0 when the scale is 0).
+__device__ __forceinline__ uint2 quant8_fp8(const float (&y)[8], float scale, int e)
+{
+    uint2 packed = {0u, 0u};
+    if (scale != 0.0f) {
+        packed.x = fp8x4(y[0], y[1], y[2], y[3], e);
+        packed.y = fp8x4(y[4], y[5], y[6], y[7], e);
+    }
+    return packed;
+}
+
 // Block = TPB tokens x WPT waves per token.  Thread t of a token owns chunks
 // t, t + 64*WPT, ... (NCH of them).  With OUT_F16 the kernel stops after the
 // op and stores y as fp16 to Y16 (the unfused order, where a separate step
 // quantizes that tensor); Xq and sx are then unused.
-template <typename T, int NCH, int WPT, int TPB, bool OUT_F16 = false>
+template <typename T, int NCH, int WPT, int TPB, bool OUT_F16 = false, bool FP8 = false>
 __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
     const T *__restrict__ X, int M, int K, int pre, const float *__restrict__ gamma,
     const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx,
@@ -212,6 +223,22 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
         for (int e = 0; e < 8; e++)
             a = fmaxf(a, fabsf(y[i][e]));
     a = token_reduce(a, true);
+    if constexpr (FP8) {
+        int e;
+        const float scale = fp8_scale(a, e);
+        if (!live)
+            return;
+        int8_t *qrow = Xq + m * (int64_t)K;
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + TT * i;
+            if (c < nchunks)
+                *reinterpret_cast<uint2 *>(qrow + (int64_t)c * 8) = quant8_fp8(y[i], scale, e);
+        }
+        if (t == 0)
+            sx[m] = scale;
+        return;
+    }
     const float scale = a / 127.0f;
     const bool fast = rcp_quant_ok(scale);
     const float rs = fast ? 1.0f / scale : 0.0f;
@@ -325,7 +352,7 @@ __device__ __forceinline__ float block_reduce(float v, float *red)
 // 1-D grid of 8 * ceil(M / 8) * nseg workgroups.  Workgroup b runs on XCD
 // b % 8; token m's workgroups all get b % 8 == m % 8, so the token's row is
 // fetched into one L2 and re-read from there.
-template <typename T, int PRE>
+template <typename T, int PRE, bool FP8>
 __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
     const T *__restrict__ X, int M, int K, int nseg, const float *__restrict__ gamma,
     const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx,
@@ -445,8 +472,9 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
         }
     }
 
-    const float scale = a / 127.0f;
-    const bool fast = rcp_quant_ok(scale);
+    int e = 0;
+    const float scale = FP8 ? fp8_scale(a, e) : a / 127.0f;
+    const bool fast = !FP8 && rcp_quant_ok(scale);
     const float rs = fast ? 1.0f / scale : 0.0f;
     if (own < nch) {
         float y[8];
@@ -478,13 +506,14 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
             for (int e = 0; e < 8; e++)
                 y[e] = mine[e];
         }
-        *reinterpret_cast<uint2 *>(Xq + m * K + (int64_t)own * 8) = quant8(y, scale, rs, fast);
+        *reinterpret_cast<uint2 *>(Xq + m * K + (int64_t)own * 8) =
+            FP8 ? quant8_fp8(y, scale, e) : quant8(y, scale, rs, fast);
     }
     if (seg == 0 && threadIdx.x == 0)
         sx[m] = scale;
 }
 
-template <typename T, int WPT, int TPB, bool OUT_F16 = false>
+template <typename T, int WPT, int TPB, bool OUT_F16 = false, bool FP8 = false>
 hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
                       const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
                       _Float16 *Y16 = nullptr, uint32_t *zero_rows = nullptr)
@@ -495,7 +524,8 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
     const dim3 block(kWave * WPT * TPB);
 #define ZQ_LNQ_CASE(n)                                                                          \
     if (per <= n) {                                                                             \
-        hipLaunchKernelGGL((k_ln_quant<T, n, WPT, TPB, OUT_F16>), grid, block, 0, stream, X,    \
+        hipLaunchKernelGGL((k_ln_quant<T, n, WPT, TPB, OUT_F16, FP8>), grid, block, 0, stream, \
+                           X,                                                                   \
                            (int)M, (int)K, pre, gamma, beta, eps, Xq, sx, Y16, zero_rows);      \
         return hipGetLastError();                                                               \
     }
@@ -515,26 +545,40 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
 template <typename T>
 hipError_t launch_typed(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
                         const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
-                        uint32_t *zero_rows)
+                        uint32_t *zero_rows, bool fp8)
 {
     // Few tokens with long rows: spread each row over ceil(K / 2048) workgroups.
     if (M <= kRowSegMaxM && K >= kRowSegMinK) {
         const int nseg = (int)((K + kSegElems - 1) / kSegElems);
         const dim3 grid((unsigned)(8 * ((M + 7) / 8) * nseg));
-#define ZQ_ROWSEG(P)                                                                              \
-    hipLaunchKernelGGL((k_rowseg_quant<T, P>), grid, dim3(kSegThreads), 0, stream, X, (int)M,     \
+#define ZQ_ROWSEG(P, F)                                                                           \
+    hipLaunchKernelGGL((k_rowseg_quant<T, P, F>), grid, dim3(kSegThreads), 0, stream, X, (int)M,  \
                        (int)K, nseg, gamma, beta, eps, Xq, sx, zero_rows)
-        if (pre == 1)
-            ZQ_ROWSEG(1);
-        else if (pre == 2)
-            ZQ_ROWSEG(2);
-        else
-            ZQ_ROWSEG(0);
+        if (fp8) {
+            if (pre == 1)
+                ZQ_ROWSEG(1, true);
+            else if (pre == 2)
+                ZQ_ROWSEG(2, true);
+            else
+                ZQ_ROWSEG(0, true);
+        } else {
+            if (pre == 1)
+                ZQ_ROWSEG(1, false);
+            else if (pre == 2)
+                ZQ_ROWSEG(2, false);
+            else
+                ZQ_ROWSEG(0, false);
+        }
 #undef ZQ_ROWSEG
         return hipGetLastError();
     }
     // Rows up to 64 lanes x 16 chunks x 8 = 8192 elements: one wave per token,
     // four tokens per block.
+    if (fp8)
+        return K <= 8192 ? launch_cfg<T, 1, 4, false, true>(X, M, K, pre, gamma, beta, eps, Xq, sx,
+                                                            stream, nullptr, zero_rows)
+                         : launch_cfg<T, 16, 1, false, true>(X, M, K, pre, gamma, beta, eps, Xq,
+                                                             sx, stream, nullptr, zero_rows);
     if (K <= 8192)
         return launch_cfg<T, 1, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream, nullptr,
                                    zero_rows);
@@ -565,13 +609,13 @@ hipError_t launch_ln_to_f16(const void *X, bool x_f16, int64_t M, int64_t K, int
 
 hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                            const float *gamma, const float *beta, float eps, int8_t *Xq,
-                           float *x_scales, hipStream_t stream, uint32_t *zero_rows)
+                           float *x_scales, hipStream_t stream, uint32_t *zero_rows, bool fp8)
 {
     if (x_f16)
         return launch_typed(static_cast<const _Float16 *>(X), M, K, pre, gamma, beta, eps, Xq,
-                            x_scales, stream, zero_rows);
+                            x_scales, stream, zero_rows, fp8);
     return launch_typed(static_cast<const float *>(X), M, K, pre, gamma, beta, eps, Xq, x_scales,
-                        stream, zero_rows);
+                        stream, zero_rows, fp8);
 }
 
 // Codes of fp16 rows whose absmax is already known (row_amax holds the float

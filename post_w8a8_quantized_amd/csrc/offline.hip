@@ -83,6 +83,38 @@ __global__ __launch_bounds__(kThreads) void k_wgroup_quant(const T *__restrict__
     }
 }
 
+// FP8 codes of the group: power-of-two scale 2^e from the group's absmax.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_wgroup_quant_fp8(const T *__restrict__ W,
+                                                               const float *__restrict__ smooth,
+                                                               int K, int G, int blocks_per_row,
+                                                               const uint32_t *__restrict__ amax,
+                                                               uint8_t *__restrict__ Wq)
+{
+    const int64_t n = blockIdx.x / blocks_per_row;
+    const int j0 = (blockIdx.x % blocks_per_row) * kThreads * 4;
+    int e;
+    const float s = fp8_scale(__uint_as_float(amax[n / G]), e);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int j = j0 + i * kThreads + threadIdx.x;
+        if (j < K) {
+            const float v = w_elem(W, smooth, n, K, j);
+            Wq[n * K + j] = s == 0.0f ? 0 : (uint8_t)(fp8x4(v, 0.0f, 0.0f, 0.0f, e) & 0xff);
+        }
+    }
+}
+
+__global__ void k_wgroup_scales_fp8(const uint32_t *__restrict__ amax, float *__restrict__ s_w,
+                                    int64_t ng)
+{
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g < ng) {
+        int e;
+        s_w[g] = fp8_scale(__uint_as_float(amax[g]), e);
+    }
+}
+
 __global__ void k_wgroup_scales(const uint32_t *__restrict__ amax, float *__restrict__ s_w, int64_t ng)
 {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -92,7 +124,7 @@ __global__ void k_wgroup_scales(const uint32_t *__restrict__ amax, float *__rest
 
 template <typename T>
 hipError_t quantize_typed(const T *W, const float *smooth, int64_t N, int64_t K, int64_t G,
-                          int8_t *Wq, float *w_scales, hipStream_t stream)
+                          int8_t *Wq, float *w_scales, hipStream_t stream, bool fp8)
 {
     const int64_t ng = N / G;
     // The scale array doubles as the group-max scratch: bits of |W'|max.
@@ -103,10 +135,17 @@ hipError_t quantize_typed(const T *W, const float *smooth, int64_t N, int64_t K,
     const dim3 grid((unsigned)(N * bpr));
     hipLaunchKernelGGL(k_wgroup_absmax<T>, grid, dim3(kThreads), 0, stream, W, smooth, (int)K,
                        (int)G, bpr, amax);
-    hipLaunchKernelGGL(k_wgroup_quant<T>, grid, dim3(kThreads), 0, stream, W, smooth, (int)K,
-                       (int)G, bpr, amax, Wq);
-    hipLaunchKernelGGL(k_wgroup_scales, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, stream,
-                       amax, w_scales, ng);
+    if (fp8) {
+        hipLaunchKernelGGL(k_wgroup_quant_fp8<T>, grid, dim3(kThreads), 0, stream, W, smooth,
+                           (int)K, (int)G, bpr, amax, reinterpret_cast<uint8_t *>(Wq));
+        hipLaunchKernelGGL(k_wgroup_scales_fp8, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0,
+                           stream, amax, w_scales, ng);
+    } else {
+        hipLaunchKernelGGL(k_wgroup_quant<T>, grid, dim3(kThreads), 0, stream, W, smooth, (int)K,
+                           (int)G, bpr, amax, Wq);
+        hipLaunchKernelGGL(k_wgroup_scales, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0,
+                           stream, amax, w_scales, ng);
+    }
     return hipGetLastError();
 }
 
@@ -224,11 +263,13 @@ hipError_t smooth_typed(const TX *X, int64_t M, int64_t K, float eps, const TW *
 
 hipError_t launch_quantize_weights(const void *W, bool w_f16, const float *smooth, int64_t N,
                                    int64_t K, int64_t G, int8_t *Wq, float *w_scales,
-                                   hipStream_t stream)
+                                   hipStream_t stream, bool fp8)
 {
     if (w_f16)
-        return quantize_typed(static_cast<const _Float16 *>(W), smooth, N, K, G, Wq, w_scales, stream);
-    return quantize_typed(static_cast<const float *>(W), smooth, N, K, G, Wq, w_scales, stream);
+        return quantize_typed(static_cast<const _Float16 *>(W), smooth, N, K, G, Wq, w_scales,
+                              stream, fp8);
+    return quantize_typed(static_cast<const float *>(W), smooth, N, K, G, Wq, w_scales, stream,
+                          fp8);
 }
 
 hipError_t launch_smooth_factors(const void *X, bool x_f16, int64_t M, int64_t K, float eps,

@@ -427,6 +427,156 @@ ZQ_API zq_status zq_ffn_w8a8(const void *X, zq_dtype x_dtype, const float *gamma
                          ZQ_F16, ZQ_PATH_AUTO, stream);
 }
 
+// ---- FP8 variant (OCP E4M3 codes, power-of-two scales) ----
+
+ZQ_API zq_status zq_quantize_weights_grouped_fp8(const void *W, zq_dtype w_dtype,
+                                                 const float *smooth, int64_t N, int64_t K,
+                                                 int64_t group_rows, uint8_t *Wq8,
+                                                 float *w_scales, hipStream_t stream)
+{
+    if (!W || !Wq8 || !w_scales)
+        return ZQ_ERR_NULL;
+    if (w_dtype != ZQ_F32 && w_dtype != ZQ_F16)
+        return ZQ_ERR_DTYPE;
+    if (N < 1 || !k_ok(K) || group_rows < 1 || N % group_rows != 0 || N > INT32_MAX ||
+        N * K > (int64_t)1 << 40)
+        return ZQ_ERR_SHAPE;
+    if (!aligned16(W) || !aligned16(Wq8))
+        return ZQ_ERR_ALIGN;
+    clear_stale_error();
+    return map_hip(zq::launch_quantize_weights(W, w_dtype == ZQ_F16, smooth, N, K, group_rows,
+                                               reinterpret_cast<int8_t *>(Wq8), w_scales, stream,
+                                               true));
+}
+
+ZQ_API zq_status zq_ln_quant_per_token_fp8(const void *X, zq_dtype x_dtype, int64_t M, int64_t K,
+                                           zq_pre pre, const float *gamma, const float *beta,
+                                           float eps, uint8_t *Xq8, float *x_scales,
+                                           hipStream_t stream)
+{
+    int8_t *Xq = reinterpret_cast<int8_t *>(Xq8);
+    zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta, Xq, x_scales);
+    if (st != ZQ_OK)
+        return st;
+    clear_stale_error();
+    return map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
+                                       pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
+                                       pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, Xq,
+                                       x_scales, stream, nullptr, true));
+}
+
+namespace {
+
+zq_status fp8_gemm(const uint8_t *Xq8, const float *x_scales, const uint8_t *Wq8,
+                   const float *w_scales, int64_t G, const float *bias, zq_act act, int64_t M,
+                   int64_t N, int64_t K, void *Y, zq_dtype y_dtype, bool packed,
+                   hipStream_t stream)
+{
+    const int8_t *Xq = reinterpret_cast<const int8_t *>(Xq8);
+    const int8_t *Wq = reinterpret_cast<const int8_t *>(Wq8);
+    const bool raw = y_dtype == ZQ_F32;
+    if (packed || M <= kSkinnyMaxM)
+        return map_hip(zq::launch_gemm_skinny_fp8(Xq, x_scales, Wq, w_scales, G, bias, (int)act,
+                                                  M, N, K, Y, raw, packed, stream));
+    return map_hip(zq::launch_gemm_tiled_fp8(Xq, x_scales, Wq, w_scales, G, bias, (int)act, M, N,
+                                             K, Y, raw, stream));
+}
+
+zq_status check_fp8_gemm(const uint8_t *Xq8, const float *x_scales, const uint8_t *Wq8,
+                         const float *w_scales, int64_t G, zq_act act, int64_t M, int64_t N,
+                         int64_t K, const void *Y, zq_dtype y_dtype, const float *bias)
+{
+    if (y_dtype != ZQ_F16 && y_dtype != ZQ_F32)
+        return ZQ_ERR_DTYPE;
+    // The shape, alignment and pointer rules are those of the int8 GEMM (the
+    // raw fp32 accumulators take the place of its int32 test mode).
+    return check_gemm(reinterpret_cast<const int8_t *>(Xq8), x_scales,
+                      reinterpret_cast<const int8_t *>(Wq8), w_scales, G, act, M, N, K, Y,
+                      y_dtype == ZQ_F32 ? ZQ_I32 : ZQ_F16, bias);
+}
+
+}  // namespace
+
+ZQ_API zq_status zq_fp8_gemm_dequant(const uint8_t *Xq8, const float *x_scales,
+                                     const uint8_t *Wq8, const float *w_scales,
+                                     int64_t group_rows, const float *bias, zq_act act,
+                                     int64_t M, int64_t N, int64_t K, void *Y, zq_dtype y_dtype,
+                                     hipStream_t stream)
+{
+    zq_status st = check_fp8_gemm(Xq8, x_scales, Wq8, w_scales, group_rows, act, M, N, K, Y,
+                                  y_dtype, bias);
+    if (st != ZQ_OK)
+        return st;
+    clear_stale_error();
+    return fp8_gemm(Xq8, x_scales, Wq8, w_scales, group_rows, bias, act, M, N, K, Y, y_dtype,
+                    false, stream);
+}
+
+namespace {
+
+zq_status linear_fp8_impl(const void *X, zq_dtype x_dtype, zq_pre pre, const float *gamma,
+                          const float *beta, float eps, const uint8_t *Wq8,
+                          const float *w_scales, int64_t group_rows, const float *bias,
+                          zq_act act, int64_t M, int64_t N, int64_t K, void *workspace,
+                          size_t workspace_bytes, void *Y, bool packed, hipStream_t stream)
+{
+    if (!X || !Wq8 || !w_scales || !Y)
+        return ZQ_ERR_NULL;
+    if (!workspace)
+        return ZQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return ZQ_ERR_ALIGN;
+    const size_t need = zq_linear_workspace_bytes(M, K);
+    const size_t codes_bytes = round_up((size_t)(M > 0 && K > 0 ? M * K : 0), 256);
+    uint8_t *Xq8 = static_cast<uint8_t *>(workspace);
+    float *x_scales = reinterpret_cast<float *>(static_cast<char *>(workspace) + codes_bytes);
+    zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta,
+                                  reinterpret_cast<int8_t *>(Xq8), x_scales);
+    if (st != ZQ_OK)
+        return st;
+    st = check_fp8_gemm(Xq8, x_scales, Wq8, w_scales, group_rows, act, M, N, K, Y, ZQ_F16, bias);
+    if (st != ZQ_OK)
+        return st;
+    if (packed && M > kSkinnyMaxM)
+        return ZQ_ERR_SHAPE;
+    if (workspace_bytes < need)
+        return ZQ_ERR_WORKSPACE;
+    clear_stale_error();
+    st = map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
+                                     pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
+                                     pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps,
+                                     reinterpret_cast<int8_t *>(Xq8), x_scales, stream, nullptr,
+                                     true));
+    if (st != ZQ_OK)
+        return st;
+    return fp8_gemm(Xq8, x_scales, Wq8, w_scales, group_rows, bias, act, M, N, K, Y, ZQ_F16,
+                    packed, stream);
+}
+
+}  // namespace
+
+ZQ_API zq_status zq_linear_w8a8_fp8(const void *X, zq_dtype x_dtype, zq_pre pre,
+                                    const float *gamma, const float *beta, float eps,
+                                    const uint8_t *Wq8, const float *w_scales, int64_t group_rows,
+                                    const float *bias, zq_act act, int64_t M, int64_t N,
+                                    int64_t K, void *workspace, size_t workspace_bytes, void *Y,
+                                    hipStream_t stream)
+{
+    return linear_fp8_impl(X, x_dtype, pre, gamma, beta, eps, Wq8, w_scales, group_rows, bias,
+                           act, M, N, K, workspace, workspace_bytes, Y, false, stream);
+}
+
+ZQ_API zq_status zq_linear_w8a8_fp8_packed(const void *X, zq_dtype x_dtype, zq_pre pre,
+                                           const float *gamma, const float *beta, float eps,
+                                           const uint8_t *Wp8, const float *w_scales,
+                                           int64_t group_rows, const float *bias, zq_act act,
+                                           int64_t M, int64_t N, int64_t K, void *workspace,
+                                           size_t workspace_bytes, void *Y, hipStream_t stream)
+{
+    return linear_fp8_impl(X, x_dtype, pre, gamma, beta, eps, Wp8, w_scales, group_rows, bias,
+                           act, M, N, K, workspace, workspace_bytes, Y, true, stream);
+}
+
 ZQ_API size_t zq_smoothquant_workspace_bytes(int64_t M, int64_t K)
 {
     if (M < 1 || !k_ok(K) || M > INT32_MAX)

@@ -8,6 +8,9 @@ namespace zq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
@@ -108,6 +111,44 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d)
 {
     return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
            ((uint32_t)(d & 0xff) << 24);
+}
+
+// ---- FP8 codes (OCP E4M3: bias 7, no infinities, largest finite 448) with
+// power-of-two scales ("探秘Transformer系列之（36）--- 大模型量化方案", the ZeroQuant-FP
+// paragraph: FP8 activations, every scale a power of two). ----
+
+// Exponent e of the smallest power of two with a <= 448 * 2^e, for a > 0;
+// exact (fp64 comparisons of exact values).
+__device__ __forceinline__ int fp8_scale_exp(float a)
+{
+    int e;
+    frexp((double)a, &e);
+    e -= 8;
+    while (448.0 * ldexp(1.0, e) < (double)a)
+        e++;
+    while (448.0 * ldexp(1.0, e - 1) >= (double)a)
+        e--;
+    return e;
+}
+
+// Scale 2^e of a vector with absmax a (0 when a is 0 or 2^e is below the fp32 range).
+__device__ __forceinline__ float fp8_scale(float a, int &e)
+{
+    if (!(a > 0.0f)) {
+        e = 0;
+        return 0.0f;
+    }
+    e = fp8_scale_exp(a);
+    return (float)ldexp(1.0, e);
+}
+
+// Four E4M3 codes of y * 2^-e (|y * 2^-e| <= 448; exact scaling, then the
+// hardware conversion: nearest, ties to even), little-endian in a word.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, int e)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(a, -e), ldexpf(b, -e), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(c, -e), ldexpf(d, -e), w, true);
+    return (uint32_t)w;
 }
 
 // Wave-wide reductions without LDS: DPP within each 16-lane row (quad

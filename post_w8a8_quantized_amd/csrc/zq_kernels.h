@@ -8,13 +8,14 @@
 
 namespace zq {
 
-// Prologue: LN / GeLU / none in fp32, then per-token absmax quantization.
+// Prologue: LN / GeLU / none in fp32, then per-token absmax quantization
+// (int8 codes, or with fp8 OCP E4M3 codes and power-of-two scales).
 // zero_rows (optional, M entries) is cleared on the way (a per-token absmax
 // buffer that a following GEMM epilogue fills with atomics).
 hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                            const float *gamma, const float *beta, float eps,
                            int8_t *Xq, float *x_scales, hipStream_t stream,
-                           uint32_t *zero_rows = nullptr);
+                           uint32_t *zero_rows = nullptr, bool fp8 = false);
 
 // Quantization of fp16 rows whose per-row absmax (float bits) is already known.
 hipError_t launch_quant_known(const _Float16 *Y, int64_t M, int64_t K, const uint32_t *row_amax,
@@ -39,6 +40,13 @@ hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8
                              int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
                              hipStream_t stream, uint32_t *row_amax = nullptr);
 
+// The FP8 variant of the tiled GEMM: OCP E4M3 operands, fp32 accumulation,
+// same epilogue; out_raw writes the fp32 accumulators.
+hipError_t launch_gemm_tiled_fp8(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                 const float *w_scales, int64_t G, const float *bias, int act,
+                                 int64_t M, int64_t N, int64_t K, void *Y, bool out_raw,
+                                 hipStream_t stream);
+
 // Weight-streaming MFMA GEMM for M <= 32 (decode shapes), same epilogue.
 hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                               const float *w_scales, int64_t G, const float *bias, int act,
@@ -51,6 +59,12 @@ hipError_t launch_gemm_skinny_packed(const int8_t *Xq, const float *x_scales, co
                                      int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
                                      hipStream_t stream);
 
+// The FP8 variant of the weight-streaming GEMM (row-major or packed weights).
+hipError_t launch_gemm_skinny_fp8(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                  const float *w_scales, int64_t G, const float *bias, int act,
+                                  int64_t M, int64_t N, int64_t K, void *Y, bool out_raw,
+                                  bool packed, hipStream_t stream);
+
 // Offline re-layout of Wq [N x K] into 32-row x 512-byte blocks (zero padded)
 // that the weight-streaming kernel reads as contiguous 16 KB runs.
 int64_t packed_weights_bytes(int64_t N, int64_t K);
@@ -58,9 +72,10 @@ hipError_t launch_pack_weights(const int8_t *Wq, int64_t N, int64_t K, int8_t *W
                                hipStream_t stream);
 
 // Offline group-wise weight quantization (optionally W * diag(smooth)).
+// With fp8: OCP E4M3 codes and power-of-two group scales.
 hipError_t launch_quantize_weights(const void *W, bool w_f16, const float *smooth,
                                    int64_t N, int64_t K, int64_t G, int8_t *Wq,
-                                   float *w_scales, hipStream_t stream);
+                                   float *w_scales, hipStream_t stream, bool fp8 = false);
 
 // Offline SmoothQuant factors and LayerNorm fold.  ws holds 2*M floats of
 // per-token statistics followed by 2*K uint32 channel maxima.

@@ -26,7 +26,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = zq.exported_symbols()
-    assert len(names) == 17
+    assert len(names) == 22
     out = subprocess.run(["nm", "-D", "--defined-only", zq.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}

@@ -1,0 +1,149 @@
+"""FP8 variant (OCP E4M3 codes, power-of-two scales) against the oracle: weight
+codes and scales exact, activation codes within one code step on near-ties,
+the FP8 GEMM's fp32 accumulators within a bound set by the sum of |products|,
+the layer's fp16 output within the output tolerance, packed and row-major
+weight-streaming results identical."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import ref
+from tests._match import assert_scales, assert_y, say
+from zq_workloads import WORKLOADS, make_inputs, random_affine
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def zq():
+    import post_w8a8_quantized_amd as m
+    assert torch.cuda.is_available(), "a GPU device node exists but torch sees no GPU"
+    m.library()
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_fp8_codes(got, want):
+    """Same byte, or the neighbouring code of the same sign (a near-tie decided
+    on a value one fp32 ulp away), on at most max(1, 1e-4 n) elements."""
+    g = got.astype(np.int16)
+    w = want.astype(np.int16)
+    off = g != w
+    same_sign = (g & 0x80) == (w & 0x80)
+    assert np.all(np.abs(g - w)[off] <= 1) and np.all(same_sign[off]), "codes differ by more than one step"
+    assert off.sum() <= max(1, int(1e-4 * g.size)), f"{off.sum()} codes differ"
+
+
+def random_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38      # no NaN codes
+    return c
+
+
+@pytest.mark.parametrize("N,K,G,dt,smooth", [(256, 512, 64, np.float32, False),
+                                             (384, 768, 128, np.float16, True),
+                                             (96, 208, 1, np.float32, False)])
+def test_fp8_weights_exact(zq, N, K, G, dt, smooth):
+    say("fp8 weights", N, K, G, dt.__name__, smooth)
+    rng = np.random.default_rng(N + K)
+    W = (0.02 * rng.standard_normal((N, K)) * np.exp(rng.standard_normal((N, 1)))).astype(dt)
+    s = (np.exp(0.5 * rng.standard_normal(K))).astype(np.float32) if smooth else None
+    Wq, sw = zq.quantize_weights_grouped_fp8(dev(W), G, None if s is None else dev(s))
+    Wf = W.astype(np.float32)
+    if s is not None:
+        Wf = ref.fold_weights(Wf, s)
+    q_ref, s_ref = ref.quantize_groups_fp8(Wf, G)
+    assert np.array_equal(host(Wq), q_ref)
+    assert np.array_equal(host(sw), s_ref)
+
+
+@pytest.mark.parametrize("M,K,pre,dt,affine", [
+    (16, 256, ref.PRE_LAYERNORM, np.float32, False),
+    (200, 768, ref.PRE_LAYERNORM, np.float16, True),
+    (37, 4096, ref.PRE_GELU, np.float16, False),
+    (16, 28672, ref.PRE_GELU, np.float16, False),      # row over many workgroups
+    (5, 10240, ref.PRE_LAYERNORM, np.float16, True),   # 16 waves per token
+    (50, 1040, ref.PRE_NONE, np.float16, False),
+])
+def test_fp8_prologue(zq, M, K, pre, dt, affine):
+    say("fp8 prologue", M, K, pre, dt.__name__)
+    rng = np.random.default_rng(M + K + pre)
+    X = (rng.standard_normal((M, K)) * np.exp(2 * rng.standard_normal((M, 1)))).astype(dt)
+    X[min(3, M - 1)] = 0
+    g, b = random_affine(rng, K) if affine else (None, None)
+    q, s = zq.ln_quant_per_token_fp8(dev(X), pre, None if g is None else dev(g),
+                                     None if b is None else dev(b), 1e-5)
+    q_ref, s_ref = ref.prologue_fp8(X, pre, g, b, 1e-5)
+    if pre == ref.PRE_NONE:
+        assert np.array_equal(host(q), q_ref) and np.array_equal(host(s), s_ref)
+    else:
+        assert_fp8_codes(host(q), q_ref)
+        assert_scales(host(s), s_ref)
+        assert set(np.unique(np.log2(host(s)[host(s) > 0]) % 1)) <= {0.0}   # powers of two
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (300, 260, 384), (40, 192, 4096),
+                                   (16, 256, 512), (5, 100, 1024), (32, 132, 4096)])
+def test_fp8_gemm_accumulators(zq, M, N, K):
+    """Raw fp32 accumulators of the FP8 matrix cores against the fp64 sum.  The
+    matrix cores add each block of 64 (32x32x64) or 128 (16x16x128) products
+    with less than fp32 alignment precision: on random codes, whose products
+    span 2^-18 .. 2^17 within one dot product, the error measured on MI355X
+    reaches 1.6e-4 of the sum of |products| (median 1e-5).  Bound: 2^-12 of it."""
+    say("fp8 gemm acc", M, N, K)
+    rng = np.random.default_rng(M * 3 + N + K)
+    Xq = random_codes(rng, (M, K))
+    Wq = random_codes(rng, (N, K))
+    acc = host(zq.fp8_gemm_dequant(dev(Xq), None, dev(Wq), None, 4, out_dtype=torch.float32))
+    want = ref.gemm_fp8(Xq, Wq)
+    bound = ref.gemm_fp8(Xq & 0x7F, Wq & 0x7F) * 2.0 ** -12 + 1e-30
+    assert np.all(np.abs(acc.astype(np.float64) - want) <= bound)
+
+
+@pytest.mark.parametrize("M,N,K,G,act", [(200, 384, 768, 64, 1), (16, 256, 1024, 64, 0),
+                                         (33, 132, 512, 4, 1)])
+def test_fp8_gemm_epilogue(zq, M, N, K, G, act):
+    say("fp8 gemm epilogue", M, N, K, G, act)
+    rng = np.random.default_rng(M + N + K + act)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    q_ref, s_ref = ref.quantize_rows_fp8(X)
+    wq_ref, sw_ref = ref.quantize_groups_fp8(W, G)
+    bias = (0.01 * rng.standard_normal(N)).astype(np.float32)
+    Y = host(zq.fp8_gemm_dequant(dev(q_ref), dev(s_ref), dev(wq_ref), dev(sw_ref), G, dev(bias),
+                                 act))
+    assert_y(Y, ref.epilogue_f64acc(ref.gemm_fp8(q_ref, wq_ref), s_ref, sw_ref, G, bias, act))
+
+
+@pytest.mark.parametrize("name", ["tiny", "bert_ffn_up", "decode_ffn_down"])
+def test_fp8_layer_workloads(zq, name):
+    """The FP8 layer at the workload's size (tokens sampled for the oracle),
+    and at decode shapes packed codes give the row-major result bit for bit."""
+    w = WORKLOADS[name]
+    say("fp8 layer", name)
+    inp = make_inputs(w)
+    Wq, sw = zq.quantize_weights_grouped_fp8(dev(inp.W), w.group_rows)
+    bias = None if inp.bias is None else dev(inp.bias)
+    kw = dict(pre=w.pre, gamma=dev(inp.gamma), beta=dev(inp.beta), eps=w.eps, bias=bias,
+              act=w.act)
+    Y = host(zq.linear_w8a8_fp8(dev(inp.X), Wq, sw, w.group_rows, **kw))
+    rows = np.unique(np.concatenate([np.arange(0, w.M, max(1, w.M // 40)), [w.M - 1]]))
+    q_ref, s_ref = ref.prologue_fp8(inp.X[rows], w.pre, inp.gamma, inp.beta, w.eps)
+    Y_ref = ref.epilogue_f64acc(ref.gemm_fp8(q_ref, host(Wq)), s_ref, host(sw), w.group_rows,
+                                inp.bias, w.act)
+    assert_y(Y[rows], Y_ref)
+    if w.M <= 32:
+        Wp = zq.pack_weights(Wq)
+        Yp = host(zq.linear_w8a8_fp8(dev(inp.X), Wp, sw, w.group_rows, N=w.N, packed=True, **kw))
+        assert np.array_equal(Yp.view(np.uint16), Y.view(np.uint16))
