@@ -84,3 +84,46 @@ def linear(X, pre, gamma, beta, eps, W, G, bias, act):
     return (np.array(Xq, dtype=np.int8), np.array(s_x, dtype=np.float32),
             np.array(Wq, dtype=np.int8), np.array(s_w, dtype=np.float32),
             np.array(acc, dtype=np.int64), Y)
+
+
+def linear_decomp(X, pre, gamma, beta, eps, alpha, W, G, bias, act):
+    """LLM.int8() mixed-precision decomposition ("探秘Transformer系列之（36）" 1.1,
+    "方案" and "混合精度分解"), written separately from the C oracle:
+    outlier columns are those where some |y| exceeds alpha; they are taken in
+    FP16 on both sides; the rest are absmax-quantized per token and per weight
+    group; the two partial products are summed exactly (math.fsum) and
+    rounded to fp16 once.  Returns (cols, Xq, s_x, Y_fp16)."""
+    X = np.asarray(X)
+    W = np.asarray(W, dtype=np.float32)
+    M, K = X.shape
+    N = W.shape[0]
+    rows = [preop_row(X[m].astype(np.float64), pre, gamma, beta, eps) for m in range(M)]
+    cols = [j for j in range(K) if any(abs(rows[m][j]) > alpha for m in range(M))]
+    outl = set(cols)
+    Xq, s_x = [], []
+    for m in range(M):
+        keep = [rows[m][j] if j not in outl else 0.0 for j in range(K)]
+        q, s = quantize_vec(keep)
+        Xq.append(q)
+        s_x.append(s)
+    Wq, s_w = [None] * N, []
+    for g in range(N // G):
+        q, s = quantize_vec([float(v) for v in W[g * G:(g + 1) * G].ravel()])
+        s_w.append(s)
+        for i in range(G):
+            Wq[g * G + i] = q[i * K:(i + 1) * K]
+    h = lambda v: float(np.float16(v))      # numpy's own nearest-even fp16 rounding
+    Y = np.empty((M, N), dtype=np.float16)
+    for m in range(M):
+        for n in range(N):
+            acc = sum(Xq[m][k] * Wq[n][k] for k in range(K))
+            terms = [s_x[m] * s_w[n // G] * acc]
+            terms += [h(rows[m][j]) * h(W[n, j]) for j in cols]
+            if bias is not None:
+                terms.append(float(bias[n]))
+            v = math.fsum(terms)
+            if act == ACT_GELU:
+                v = 0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0)))
+            Y[m, n] = np.float16(v)
+    return (np.array(cols, dtype=np.int32), np.array(Xq, dtype=np.int8),
+            np.array(s_x, dtype=np.float32), Y)

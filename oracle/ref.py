@@ -51,6 +51,12 @@ _SIGS = {
                                _i64, _p, _i64, _p, _p, _p]),
     "zqref_linear_float_rows": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _p, _p, _i, _i64,
                                      _p, _i64, _p]),
+    "zqref_outlier_columns": (_i, [_p, _i64, _i64, _f, _p, _p]),
+    "zqref_quantize_rows_excluding": (_i, [_p, _i64, _i64, _p, _i64, _p, _p]),
+    "zqref_decomp_epilogue": (_i, [_p, _p, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i, _i64, _i64,
+                                   _p, _p]),
+    "zqref_linear_decomp_rows": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _f, _p, _p, _i64, _p,
+                                      _p, _i, _i64, _p, _i64, _p, _p, _p, _p, _p]),
 }
 
 
@@ -338,3 +344,79 @@ def linear_float_rows(X, pre, gamma, beta, eps, W, bias, act, rows):
                                          eps, _ptr(W), _ptr(bias), act, N, _ptr(rows),
                                          rows.shape[0], _ptr(Y)), "zqref_linear_float_rows")
     return Y
+
+
+# ---- LLM.int8() mixed-precision decomposition (outlier columns in FP16) ----
+
+def outlier_columns(Y: np.ndarray, alpha: float) -> np.ndarray:
+    """Ascending int32 indices j with max_m |Y[m, j]| > alpha."""
+    Y = np.ascontiguousarray(Y, dtype=np.float32)
+    M, K = Y.shape
+    cols = np.empty(K, dtype=np.int32)
+    P = ctypes.c_int64(0)
+    _check(lib().zqref_outlier_columns(_ptr(Y), M, K, alpha, _ptr(cols), ctypes.byref(P)),
+           "zqref_outlier_columns")
+    return cols[:P.value].copy()
+
+
+def quantize_rows_excluding(Y: np.ndarray, cols: np.ndarray):
+    """Per-row absmax quantization over the columns outside `cols`; code 0 in
+    those columns -> (int8 codes, fp32 scales)."""
+    Y = np.ascontiguousarray(Y, dtype=np.float32)
+    M, K = Y.shape
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    q = np.empty((M, K), dtype=np.int8)
+    s = np.empty(M, dtype=np.float32)
+    _check(lib().zqref_quantize_rows_excluding(_ptr(Y), M, K, _ptr(cols), cols.shape[0], _ptr(q),
+                                               _ptr(s)), "zqref_quantize_rows_excluding")
+    return q, s
+
+
+def decomp_epilogue(acc, s_x, s_w, G: int, Y, cols, W, bias=None, act: int = ACT_NONE,
+                    return_f64: bool = False):
+    """Dequantized INT8 part + FP16 outlier part + bias (+GeLU) -> fp16."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    M, N = acc.shape
+    Y = np.ascontiguousarray(Y, dtype=np.float32)
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    K = Y.shape[1]
+    out = np.empty((M, N), dtype=np.uint16)
+    out64 = np.empty((M, N), dtype=np.float64) if return_f64 else None
+    _check(lib().zqref_decomp_epilogue(_ptr(acc), _ptr(np.ascontiguousarray(s_x, np.float32)),
+                                       _ptr(np.ascontiguousarray(s_w, np.float32)), G, _ptr(Y), K,
+                                       _ptr(cols), cols.shape[0], _ptr(W), _ptr(bias), act, M, N,
+                                       _ptr(out), _ptr(out64)), "zqref_decomp_epilogue")
+    Yh = out.view(np.float16)
+    return (Yh, out64) if return_f64 else Yh
+
+
+def linear_decomp(X, pre, gamma, beta, eps, alpha, Wq, s_w, G, W, bias, act,
+                  return_f64: bool = False):
+    """The decomposed layer on all tokens -> (Y fp16, codes, scales, outlier columns)."""
+    Y = preop(X, pre, gamma, beta, eps)
+    cols = outlier_columns(Y, alpha)
+    Xq, s_x = quantize_rows_excluding(Y, cols)
+    out = decomp_epilogue(gemm_i32(Xq, Wq), s_x, s_w, G, Y, cols, W, bias, act, return_f64)
+    return out, Xq, s_x, cols
+
+
+def linear_decomp_rows(X, pre, gamma, beta, eps, alpha, Wq, s_w, G, W, bias, act, rows):
+    """The decomposed layer for the tokens in `rows` (the outlier set still
+    comes from every token) -> (Y fp16 [R,N], codes [R,K], scales [R], columns)."""
+    X = np.ascontiguousarray(X)
+    M, K = X.shape
+    N = Wq.shape[0]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    cols = np.empty(K, dtype=np.int32)
+    P = ctypes.c_int64(0)
+    Xq = np.empty((R, K), dtype=np.int8)
+    s_x = np.empty(R, dtype=np.float32)
+    Y = np.empty((R, N), dtype=np.uint16)
+    _check(lib().zqref_linear_decomp_rows(
+        _ptr(X), _x_args(X), M, K, pre, _ptr(gamma), _ptr(beta), eps, alpha,
+        _ptr(np.ascontiguousarray(Wq, np.int8)), _ptr(np.ascontiguousarray(s_w, np.float32)), G,
+        _ptr(np.ascontiguousarray(W, np.float32)), _ptr(bias), act, N, _ptr(rows), R, _ptr(cols),
+        ctypes.byref(P), _ptr(Xq), _ptr(s_x), _ptr(Y)), "zqref_linear_decomp_rows")
+    return Y.view(np.float16), Xq, s_x, cols[:P.value].copy()

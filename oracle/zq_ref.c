@@ -607,3 +607,170 @@ int zqref_linear_float_rows(const void *X, int x_is_f16, int64_t M, int64_t K, i
     free(Y);
     return rc;
 }
+
+/* ---- The LLM.int8() mixed-precision decomposition ----
+ *
+ * [T36] 1.1 LLM.int8(), "方案" and "混合精度分解": the matmul input is split
+ * by column.  A column is an outlier dimension when some token's value there
+ * exceeds the threshold alpha in magnitude (alpha = 6.0 is the page's
+ * setting); the set O of such columns is found at run time over the whole
+ * batch.  Columns in O are kept in FP16 on both sides and multiplied in high
+ * precision (W16A16); the other columns are quantized vector-wise, each token
+ * row with its own absmax, multiplied in INT8, and the INT32 product is
+ * dequantized.  The two partial products are added into one FP16 result.
+ *
+ * Readings: "exceeds" is strict, |y| > alpha; the token absmax runs over the
+ * columns outside O only, and the INT8 operand holds code 0 in the columns
+ * of O; the INT8 weights are the layer's offline group-wise codes (G = 1 is
+ * the page's per-output-channel scale), made over all K since O is not known
+ * offline; the FP16 operands are fp16(y) and fp16(W), nearest with ties to
+ * even; both partial products, the bias and the GeLU epilogue are summed in
+ * fp64 and rounded to FP16 once.
+ */
+
+/* O = { j : max_m |Y[m, j]| > alpha }, ascending; *P = |O|. */
+int zqref_outlier_columns(const float *Y, int64_t M, int64_t K, float alpha,
+                          int32_t *cols, int64_t *P)
+{
+    if (!Y || !cols || !P || M < 0 || K < 1)
+        return ZQREF_ERR_ARG;
+    int64_t n = 0;
+    for (int64_t j = 0; j < K; j++) {
+        int hit = 0;
+        for (int64_t m = 0; m < M && !hit; m++)
+            hit = fabsf(Y[m * K + j]) > alpha;
+        if (hit)
+            cols[n++] = (int32_t)j;
+    }
+    *P = n;
+    return ZQREF_OK;
+}
+
+/* Vector-wise quantization of each row of Y over the columns outside O:
+ * a = max_{j not in O} |y_j|, s = fl32(a / 127), q_j as in absmax_quantize;
+ * q_j = 0 for j in O. */
+int zqref_quantize_rows_excluding(const float *Y, int64_t M, int64_t K, const int32_t *cols,
+                                  int64_t P, int8_t *Xq, float *s_x)
+{
+    if (!Y || !Xq || !s_x || M < 0 || K < 1 || P < 0 || (P > 0 && !cols))
+        return ZQREF_ERR_ARG;
+    char *in_o = (char *)calloc((size_t)K, 1);
+    if (!in_o)
+        return ZQREF_ERR_ARG;
+    for (int64_t p = 0; p < P; p++) {
+        if (cols[p] < 0 || cols[p] >= K) {
+            free(in_o);
+            return ZQREF_ERR_ARG;
+        }
+        in_o[cols[p]] = 1;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        const float *y = Y + m * K;
+        float a = 0.0f;
+        for (int64_t j = 0; j < K; j++)
+            if (!in_o[j] && fabsf(y[j]) > a)
+                a = fabsf(y[j]);
+        float s = a / 127.0f;
+        s_x[m] = s;
+        for (int64_t j = 0; j < K; j++) {
+            if (in_o[j] || s == 0.0f) {
+                Xq[m * K + j] = 0;
+                continue;
+            }
+            float r = nearbyintf(y[j] / s);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            Xq[m * K + j] = (int8_t)r;
+        }
+    }
+    free(in_o);
+    return ZQREF_OK;
+}
+
+/*
+ * The decomposed epilogue: for token m and output n,
+ *   v = s_x[m] s_w[n/G] acc[m,n] + sum_{p<P} fp16(Y[m, O_p]) fp16(W[n, O_p]) + b[n]
+ * in fp64, then GeLU if asked, then one rounding to fp16.  Y is the op's
+ * output [M x K] (fp32), W the unquantized weights [N x K] (fp32 or widened
+ * fp16).  Y_f64 (optional) receives v before the rounding.
+ */
+int zqref_decomp_epilogue(const int32_t *acc, const float *s_x, const float *s_w, int64_t G,
+                          const float *Y, int64_t K, const int32_t *cols, int64_t P,
+                          const float *W, const float *bias, int act, int64_t M, int64_t N,
+                          uint16_t *Yout, double *Y_f64)
+{
+    if (!acc || !s_x || !s_w || !Yout || G < 1 || N % G || M < 0 || N < 1 || K < 1 || P < 0)
+        return ZQREF_ERR_ARG;
+    if (P > 0 && (!Y || !W || !cols))
+        return ZQREF_ERR_ARG;
+    if (act != ACT_NONE && act != ACT_GELU)
+        return ZQREF_ERR_ARG;
+    for (int64_t p = 0; p < P; p++)
+        if (cols[p] < 0 || cols[p] >= K)
+            return ZQREF_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            double v = (double)s_x[m] * (double)s_w[n / G] * (double)acc[m * N + n];
+            for (int64_t p = 0; p < P; p++) {
+                const int64_t j = cols[p];
+                double a = (double)zqref_f16_to_f32(zqref_f64_to_f16((double)Y[m * K + j]));
+                double w = (double)zqref_f16_to_f32(zqref_f64_to_f16((double)W[n * K + j]));
+                v += a * w;
+            }
+            if (bias)
+                v += (double)bias[n];
+            if (act == ACT_GELU)
+                v = gelu64(v);
+            if (Y_f64)
+                Y_f64[m * N + n] = v;
+            Yout[m * N + n] = zqref_f64_to_f16(v);
+        }
+    }
+    return ZQREF_OK;
+}
+
+/*
+ * The decomposed layer for the tokens listed in rows[0..R).  The outlier set
+ * depends on every token of the batch, so the op runs over all M tokens to
+ * find O (cols[0..*P)); each listed token then follows the steps above.
+ * Outputs: cols [K] (first *P used), Xq_out [R x K], s_x_out [R], Y_out [R x N].
+ */
+int zqref_linear_decomp_rows(const void *X, int x_is_f16, int64_t M, int64_t K, int pre,
+                             const float *gamma, const float *beta, float eps, float alpha,
+                             const int8_t *Wq, const float *s_w, int64_t G, const float *W,
+                             const float *bias, int act, int64_t N, const int64_t *rows, int64_t R,
+                             int32_t *cols, int64_t *P, int8_t *Xq_out, float *s_x_out,
+                             uint16_t *Y_out)
+{
+    if (!X || !Wq || !s_w || !W || !rows || !cols || !P || !Xq_out || !s_x_out || !Y_out ||
+        R < 0 || M < 1 || K < 1 || N < 1)
+        return ZQREF_ERR_ARG;
+    for (int64_t r = 0; r < R; r++)
+        if (rows[r] < 0 || rows[r] >= M)
+            return ZQREF_ERR_ARG;
+    float *Y = (float *)malloc(sizeof(float) * (size_t)(M * K));
+    float *Ys = (float *)malloc(sizeof(float) * (size_t)(R * K > 0 ? R * K : 1));
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(R * N > 0 ? R * N : 1));
+    int rc = ZQREF_ERR_ARG;
+    if (Y && Ys && acc) {
+        rc = zqref_preop(X, x_is_f16, M, K, pre, gamma, beta, eps, Y);
+        if (rc == ZQREF_OK)
+            rc = zqref_outlier_columns(Y, M, K, alpha, cols, P);
+        if (rc == ZQREF_OK) {
+            for (int64_t r = 0; r < R; r++)
+                memcpy(Ys + r * K, Y + rows[r] * K, sizeof(float) * (size_t)K);
+            rc = zqref_quantize_rows_excluding(Ys, R, K, cols, *P, Xq_out, s_x_out);
+        }
+        if (rc == ZQREF_OK)
+            rc = zqref_gemm_i32(Xq_out, Wq, R, N, K, acc);
+        if (rc == ZQREF_OK)
+            rc = zqref_decomp_epilogue(acc, s_x_out, s_w, G, Ys, K, cols, *P, W, bias, act, R, N,
+                                       Y_out, NULL);
+    }
+    free(Y);
+    free(Ys);
+    free(acc);
+    return rc;
+}

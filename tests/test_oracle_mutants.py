@@ -19,18 +19,27 @@ from tests import test_oracle_pins as pins
 
 MUTANTS = {
     "round_half_away": ("float r = nearbyintf(t);", "float r = roundf(t);"),
-    "scale_over_128": ("float s = a / 127.0f;", "float s = a / 128.0f;"),
+    "scale_over_128": ("float s = a / 127.0f;\n    for (int64_t i = 0;", "float s = a / 128.0f;\n    for (int64_t i = 0;"),
     "unbiased_variance": ("double var = ss / (double)K;", "double var = ss / (double)(K - 1);"),
     "eps_dropped": ("double r = 1.0 / sqrt(var + (double)eps);", "double r = 1.0 / sqrt(var);"),
     "beta_sign": ("* r * g + b);", "* r * g - b);"),
     "gelu_wrong_scale": ("return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));",
                          "return 0.5 * x * (1.0 + erf(x / 2.0));"),
     "gemm_transposed_w": ("(int64_t)Wq[n * K + k]", "(int64_t)Wq[k * N + n]"),
-    "group_index_modulo": ("(double)s_w[n / G] * (double)acc[m * N + n]",
-                           "(double)s_w[n % (N / G)] * (double)acc[m * N + n]"),
-    "bias_dropped": ("                v += (double)bias[n];\n            if (act == ACT_GELU)\n                v = gelu64(v);\n            if (Y_f64)",
-                     "                v += 0.0;\n            if (act == ACT_GELU)\n                v = gelu64(v);\n            if (Y_f64)"),
+    "group_index_modulo": ("(double)s_w[n / G] * (double)acc[m * N + n];\n            if (bias)",
+                           "(double)s_w[n % (N / G)] * (double)acc[m * N + n];\n            if (bias)"),
+    "bias_dropped": ("(double)acc[m * N + n];\n            if (bias)\n                v += (double)bias[n];",
+                     "(double)acc[m * N + n];\n            if (bias)\n                v += 0.0;"),
     "fp16_truncates": ("double q = nearbyint(ldexp(a, 10 - e));", "double q = floor(ldexp(a, 10 - e));"),
+    "outlier_test_inclusive": ("hit = fabsf(Y[m * K + j]) > alpha;", "hit = fabsf(Y[m * K + j]) >= alpha;"),
+    "outlier_test_signed": ("hit = fabsf(Y[m * K + j]) > alpha;", "hit = Y[m * K + j] > alpha;"),
+    "outlier_absmax_counted": ("if (!in_o[j] && fabsf(y[j]) > a)", "if (fabsf(y[j]) > a)"),
+    "outlier_term_dropped": ("                v += a * w;\n", "                v += 0.0 * a * w;\n"),
+    "outlier_weight_unrounded": ("double w = (double)zqref_f16_to_f32(zqref_f64_to_f16((double)W[n * K + j]));",
+                                 "double w = (double)W[n * K + j];"),
+    "outlier_weight_transposed": ("zqref_f64_to_f16((double)W[n * K + j])", "zqref_f64_to_f16((double)W[j * N + n])"),
+    "outlier_act_unrounded": ("double a = (double)zqref_f16_to_f32(zqref_f64_to_f16((double)Y[m * K + j]));",
+                              "double a = (double)Y[m * K + j];"),
     "smooth_inverted": ("(float)sqrt(a / w)", "(float)sqrt(w / a)"),
     "fold_weight_divides": ("(double)W[n * K + j] * (double)s[j]", "(double)W[n * K + j] / (double)s[j]"),
     "group_absmax_first_row": ("s_w[g] = absmax_quantize(W + g * G * K, G * K, Wq + g * G * K);",

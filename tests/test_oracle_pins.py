@@ -470,6 +470,154 @@ def pin_fp8_epilogue_reduces_to_int_epilogue():
         assert np.array_equal(a.view(np.uint16), c.view(np.uint16))
 
 
+# --------------------------------------------------------------------------
+# LLM.int8() mixed-precision decomposition ("探秘Transformer系列之（36）" 1.1)
+# --------------------------------------------------------------------------
+
+def _decomp_case(seed, M, K, N, n_out, scale=40.0, x_dtype=np.float32):
+    """Tokens N(0,1) with n_out fixed columns scaled up (the outlier pattern
+    the page describes: a few systematic feature dimensions)."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K))
+    cols = np.sort(rng.choice(K, n_out, replace=False))
+    X[:, cols] *= scale
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    bias = (0.01 * rng.standard_normal(N)).astype(np.float32)
+    return X.astype(x_dtype), W, bias, cols
+
+
+def pin_decomp_no_outliers_is_fused_layer():
+    """With alpha above every |y| the set O is empty and the decomposed layer
+    is the fused W8A8 layer, bit for bit."""
+    for seed, pre, act, G in ((40, ref.PRE_LAYERNORM, ref.ACT_NONE, 1),
+                              (41, ref.PRE_GELU, ref.ACT_GELU, 4),
+                              (42, ref.PRE_NONE, ref.ACT_NONE, 2)):
+        X, W, bias, _ = _decomp_case(seed, 6, 64, 8, 2)
+        Wq, s_w = ref.quantize_groups(W, G)
+        Yd, q, s, cols = ref.linear_decomp(X, pre, None, None, 1e-5, 1e30, Wq, s_w, G, W, bias, act)
+        Yf, qf, sf = ref.linear(X, pre, None, None, 1e-5, Wq, s_w, G, bias, act)
+        assert cols.size == 0
+        assert np.array_equal(q, qf) and np.array_equal(s, sf)
+        assert np.array_equal(Yd.view(np.uint16), Yf.view(np.uint16))
+
+
+def pin_decomp_all_outliers_is_fp16_matmul():
+    """With alpha below 0 every column is in O: no INT8 part is left (codes and
+    scales 0) and the result is the FP16 matmul fp16(y) fp16(W)^T + b, here
+    evaluated with numpy's fp16 casts and a float64 matmul."""
+    from scipy.special import erf
+    X, W, bias, _ = _decomp_case(43, 5, 96, 12, 3)
+    for act in (ref.ACT_NONE, ref.ACT_GELU):
+        Wq, s_w = ref.quantize_groups(W, 3)
+        (Yd, Y64), q, s, cols = ref.linear_decomp(X, ref.PRE_LAYERNORM, None, None, 1e-5, -1.0, Wq,
+                                                  s_w, 3, W, bias, act, return_f64=True)
+        assert np.array_equal(cols, np.arange(96))
+        assert not q.any() and not s.any()
+        y = ref.preop(X, ref.PRE_LAYERNORM).astype(np.float16).astype(np.float64)
+        w = W.astype(np.float16).astype(np.float64)
+        want = y @ w.T + bias.astype(np.float64)
+        mag = np.abs(y) @ np.abs(w).T + np.abs(bias)
+        if act == ref.ACT_GELU:
+            want = 0.5 * want * (1.0 + erf(want / np.sqrt(2.0)))
+        assert np.all(np.abs(Y64 - want) <= 1e-12 * mag)
+
+
+def pin_decomp_outlier_set():
+    """O is exactly the planted columns; the test is on magnitude and strict:
+    a column whose largest |y| is exactly alpha stays out, the next float
+    above alpha (or a negative value below -alpha) is in."""
+    rng = np.random.default_rng(44)
+    Y = rng.uniform(-5.9, 5.9, (9, 40)).astype(np.float32)
+    Y[3, 7] = 6.5
+    Y[0, 11] = -6.5
+    Y[8, 20] = np.float32(6.0)
+    Y[5, 21] = np.nextafter(np.float32(6.0), np.float32(np.inf))
+    Y[2, 33] = -np.nextafter(np.float32(6.0), np.float32(np.inf))
+    assert np.array_equal(ref.outlier_columns(Y, 6.0), [7, 11, 21, 33])
+    assert ref.outlier_columns(Y, 1e9).size == 0
+    assert np.array_equal(ref.outlier_columns(Y, -1.0), np.arange(40))
+
+
+def pin_decomp_quantizer_skips_outlier_columns():
+    """Quantizing outside O equals quantizing the row with the O columns set
+    to 0 (the absmax and every other code are unchanged by a zero), and the
+    codes in O are 0.  The outlier carries the row's absmax here, so counting
+    it would change the scale."""
+    X, _, _, cols = _decomp_case(45, 7, 80, 4, 3)
+    Y = ref.preop(X, ref.PRE_LAYERNORM)
+    q, s = ref.quantize_rows_excluding(Y, cols)
+    Z = Y.copy()
+    Z[:, cols] = 0.0
+    qz, sz = ref.quantize_rows(Z)
+    assert np.array_equal(q, qz) and np.array_equal(s, sz)
+    assert not q[:, cols].any()
+    _, s_all = ref.quantize_rows(Y)
+    assert np.all(s < s_all)
+
+
+def pin_decomp_error_bound():
+    """Against the unquantized layer in fp64: each INT8 operand is within half
+    a step of its value ("Integer Quantization: Deep Dive", 量化误差), each
+    FP16 operand within half an fp16 ulp, so
+      |Y - Y_float| <= sum_{j not in O} (s_x/2 |w| + |y| s_w/2 + s_x s_w/4)
+                       + sum_{j in O} (|y - y16| |w16| + |y| |w - w16|)
+    before the output rounding (act = none, compared in fp64)."""
+    X, W, bias, planted = _decomp_case(46, 8, 128, 16, 4)
+    G = 4
+    Wq, s_w = ref.quantize_groups(W, G)
+    (Yd, Y64), q, s_x, cols = ref.linear_decomp(X, ref.PRE_LAYERNORM, None, None, 1e-5, 6.0, Wq,
+                                                s_w, G, W, bias, ref.ACT_NONE, return_f64=True)
+    assert np.array_equal(cols, planted)
+    y = ref.preop(X, ref.PRE_LAYERNORM).astype(np.float64)
+    w = W.astype(np.float64)
+    want = y @ w.T + bias
+    inl = np.setdiff1d(np.arange(128), cols)
+    sw_n = np.repeat(s_w.astype(np.float64), G)
+    sx = s_x.astype(np.float64)[:, None]
+    b_int = (sx / 2) * np.abs(w[:, inl]).sum(1)[None, :] + np.abs(y[:, inl]).sum(1)[:, None] * sw_n / 2 \
+        + inl.size * sx * sw_n / 4
+    y16 = y[:, cols].astype(np.float16).astype(np.float64)
+    w16 = w[:, cols].astype(np.float16).astype(np.float64)
+    b_out = np.abs(y[:, cols] - y16) @ np.abs(w16).T + np.abs(y[:, cols]) @ np.abs(w[:, cols] - w16).T
+    err = np.abs(Y64 - want)
+    assert np.all(err <= (b_int + b_out) * (1 + 1e-6) + 1e-12)
+    # the outlier columns carry most of the output here: dropping them breaks the bound
+    assert np.max(np.abs(y[:, cols] @ w[:, cols].T)) > 10 * np.max(b_int + b_out)
+
+
+def pin_decomp_brute_force():
+    """The C oracle and the pure-Python brute force agree on the outlier set,
+    codes and scales exactly and on the fp16 output bit for bit."""
+    # (LayerNorm bounds every |y| by sqrt(K - 1), so its case needs K > 37 and
+    # a column that dominates the row's variance.)
+    for seed, M, K, N, G, pre, act, n_out, sc, dt in (
+            (47, 4, 64, 6, 2, ref.PRE_LAYERNORM, ref.ACT_NONE, 1, 40.0, np.float32),
+            (48, 3, 32, 4, 1, ref.PRE_GELU, ref.ACT_GELU, 3, 8.0, np.float16),
+            (49, 5, 16, 8, 4, ref.PRE_NONE, ref.ACT_NONE, 1, 8.0, np.float32)):
+        X, W, bias, _ = _decomp_case(seed, M, K, N, n_out, scale=sc, x_dtype=dt)
+        Wq, s_w = ref.quantize_groups(W, G)
+        Yd, q, s, cols = ref.linear_decomp(X, pre, None, None, 1e-5, 6.0, Wq, s_w, G, W, bias, act)
+        bc, bq, bs, bY = brute.linear_decomp(X, pre, None, None, 1e-5, 6.0, W, G, bias, act)
+        assert cols.size > 0, seed
+        assert np.array_equal(cols, bc) and np.array_equal(q, bq) and np.array_equal(s, bs), seed
+        assert np.array_equal(Yd.view(np.uint16), bY.view(np.uint16)), seed
+
+
+def pin_decomp_rows_subset():
+    """The row-subset form finds O from every token and then gives exactly the
+    listed rows of the full result."""
+    X, W, bias, _ = _decomp_case(50, 12, 64, 8, 2, x_dtype=np.float16)
+    Wq, s_w = ref.quantize_groups(W, 2)
+    Yd, q, s, cols = ref.linear_decomp(X, ref.PRE_LAYERNORM, None, None, 1e-5, 6.0, Wq, s_w, 2, W,
+                                       bias, ref.ACT_GELU)
+    rows = np.array([11, 0, 5])
+    Yr, qr, sr, cr = ref.linear_decomp_rows(X, ref.PRE_LAYERNORM, None, None, 1e-5, 6.0, Wq, s_w, 2,
+                                            W, bias, ref.ACT_GELU, rows)
+    assert np.array_equal(cr, cols) and cols.size > 0
+    assert np.array_equal(qr, q[rows]) and np.array_equal(sr, s[rows])
+    assert np.array_equal(Yr.view(np.uint16), Yd[rows].view(np.uint16))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
