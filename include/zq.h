@@ -328,6 +328,72 @@ zq_status zq_linear_w8a8_fp8_packed(const void *X, zq_dtype x_dtype, zq_pre pre,
                                     size_t workspace_bytes, void *Y, hipStream_t stream);
 
 /*
+ * Mixed-precision decomposition ("探秘Transformer系列之（36）--- 大模型量化方案"
+ * 1.1 LLM.int8(), "方案" and "混合精度分解"): the alternative to the SmoothQuant
+ * fold for activations with outlier feature dimensions.
+ *
+ *   y = LN / GeLU / x as in zq_ln_quant_per_token (fp32).
+ *   O = { j : |y[m, j]| > alpha for some token m of the batch }, ascending
+ *       (strict; alpha = 6.0 is the page's setting; a NaN alpha selects no
+ *       column, a negative one every column).
+ *   INT8 part: per token, s_x[m] = fl32(max_{j not in O} |y[m, j]| / 127) and
+ *       codes as usual on the columns outside O, code 0 on the columns in O;
+ *       the weights are the layer's group-wise int8 codes (group_rows = 1 is
+ *       the page's per-output-channel scale), quantized over all K offline.
+ *   FP16 part: sum_{j in O} fp16(y[m, j]) * fp16(W[n, j]), from the fp16
+ *       weights W16t (zq_pack_outlier_weights).
+ *   Y[m, n] = fp16(act(s_x[m] s_w[n / G] acc[m, n] + fp16 part + bias[n])),
+ *       the sum and the GeLU in fp32.
+ *
+ * Device layouts:
+ *   slot  int32 [K], 16-byte aligned: position of column j in O, or -1.
+ *   cols  int32 [K + 1]: cols[0] = |O|, cols[1 .. |O|] the columns of O.
+ *   XO    fp16 [M x K], 16-byte aligned: token m's value of the p-th column
+ *         of O at XO[m * K + p], p < |O| (the rest of each row is not used;
+ *         the row length K is the bound on |O|).
+ *   W16t  fp16 [K x N], 16-byte aligned: W transposed (input-channel major),
+ *         so each outlier column is one contiguous run of N values.
+ * Shapes, alignment and error rules are those of the int8 calls; Y is fp16.
+ */
+
+/* Offline: W [N x K] (ZQ_F32 / ZQ_F16) -> W16t [K x N] fp16, nearest-even. */
+zq_status zq_pack_outlier_weights(const void *W, zq_dtype w_dtype, int64_t N, int64_t K,
+                                  void *W16t, hipStream_t stream);
+
+/* The outlier set of a batch: writes slot and cols (slot is also the scratch
+ * of the search). */
+zq_status zq_outlier_columns(const void *X, zq_dtype x_dtype, int64_t M, int64_t K, zq_pre pre,
+                             const float *gamma, const float *beta, float eps, float alpha,
+                             int32_t *slot, int32_t *cols, hipStream_t stream);
+
+/* The prologue of the INT8 part (codes, scales) plus the outlier values XO,
+ * given slot from zq_outlier_columns for the same batch. */
+zq_status zq_ln_quant_decomp(const void *X, zq_dtype x_dtype, int64_t M, int64_t K, zq_pre pre,
+                             const float *gamma, const float *beta, float eps,
+                             const int32_t *slot, int8_t *Xq, float *x_scales, void *XO,
+                             hipStream_t stream);
+
+/* INT8 GEMM with the dequantization and the FP16 outlier product in its
+ * epilogue (fp16 Y). */
+zq_status zq_w8a8_gemm_decomp(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                              const float *w_scales, int64_t group_rows, const int32_t *cols,
+                              const void *XO, const void *W16t, const float *bias, zq_act act,
+                              int64_t M, int64_t N, int64_t K, void *Y, hipStream_t stream);
+
+/* The whole decomposed layer: outlier search, prologue, GEMM.  workspace is
+ * 256-byte aligned, at least zq_linear_decomp_workspace_bytes(M, K) bytes. */
+zq_status zq_linear_w8a8_decomp(const void *X, zq_dtype x_dtype, zq_pre pre, const float *gamma,
+                                const float *beta, float eps, float alpha, const int8_t *Wq,
+                                const float *w_scales, int64_t group_rows, const void *W16t,
+                                const float *bias, zq_act act, int64_t M, int64_t N, int64_t K,
+                                void *workspace, size_t workspace_bytes, void *Y,
+                                hipStream_t stream);
+
+/* slot [K] | cols [K + 1] | codes [M K] | scales [M] | XO fp16 [M K], each
+ * part rounded up to 256 bytes; 0 for invalid sizes. */
+size_t zq_linear_decomp_workspace_bytes(int64_t M, int64_t K);
+
+/*
  * zq_smoothquant_factors -- offline SmoothQuant calibration and LayerNorm fold.
  * [SQ] 2.2: Y = (X diag(s)^-1)(diag(s) W), s per input channel; [SQ] 3.2:
  * the factors are computed offline from activation statistics.

@@ -15,6 +15,8 @@ Offline weight preparation and the SmoothQuant fold are also exposed
 (`smoothquant_factors`, `quantize_weights_grouped(..., smooth=s)`), and for
 decode shapes (M <= 32) the weights can be re-laid out once with
 `pack_weights` and used by `linear_w8a8_packed` / `w8a8_gemm_dequant_packed`.
+The mixed-precision decomposition (outlier columns in fp16, LLM.int8()) is
+`linear_w8a8_decomp`, with its fp16 weights from `pack_outlier_weights`.
 """
 from __future__ import annotations
 
@@ -34,6 +36,12 @@ from ._binding import (  # noqa: F401
     fp8_gemm_dequant,
     library,
     library_path,
+    linear_decomp_workspace_bytes,
+    linear_w8a8_decomp,
+    ln_quant_decomp,
+    outlier_columns,
+    pack_outlier_weights,
+    w8a8_gemm_decomp,
     linear_w8a8,
     linear_unfused_workspace_bytes,
     linear_w8a8_fp8,
@@ -57,6 +65,8 @@ __all__ = [
     "PRE_LAYERNORM", "PRE_NONE", "ZQError", "exported_symbols", "ffn_w8a8", "ffn_workspace_bytes",
     "fp8_gemm_dequant", "linear_w8a8_fp8", "ln_quant_per_token_fp8", "quantize_weights_grouped_fp8",
     "library", "library_path",
+    "linear_decomp_workspace_bytes", "linear_w8a8_decomp", "ln_quant_decomp", "outlier_columns",
+    "pack_outlier_weights", "w8a8_gemm_decomp",
     "linear_unfused_workspace_bytes", "linear_w8a8", "linear_w8a8_packed", "linear_w8a8_unfused",
     "linear_workspace_bytes", "ln_quant_per_token",
     "pack_weights", "packed_weights_bytes", "quantize_weights_grouped", "smoothquant_factors",

@@ -61,6 +61,14 @@ _SIGS = {
     "zq_linear_w8a8_fp8_packed": (_i, [_p, _i, _i, _p, _p, _f, _p, _p, _i64, _p, _i, _i64, _i64,
                                        _i64, _p, _sz, _p, _p]),
     "zq_pack_weights": (_i, [_p, _i64, _i64, _p, _p]),
+    "zq_pack_outlier_weights": (_i, [_p, _i, _i64, _i64, _p, _p]),
+    "zq_outlier_columns": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _f, _p, _p, _p]),
+    "zq_ln_quant_decomp": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _p, _p, _p, _p, _p]),
+    "zq_w8a8_gemm_decomp": (_i, [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _i, _i64, _i64, _i64, _p,
+                                 _p]),
+    "zq_linear_w8a8_decomp": (_i, [_p, _i, _i, _p, _p, _f, _f, _p, _p, _i64, _p, _p, _i, _i64,
+                                   _i64, _i64, _p, _sz, _p, _p]),
+    "zq_linear_decomp_workspace_bytes": (_sz, [_i64, _i64]),
     "zq_w8a8_gemm_dequant_packed": (_i, [_p, _p, _p, _p, _i64, _p, _i, _i64, _i64, _i64, _p, _i,
                                          _p]),
     "zq_linear_w8a8_packed": (_i, [_p, _i, _i, _p, _p, _f, _p, _p, _i64, _p, _i, _i64, _i64, _i64,
@@ -486,3 +494,101 @@ def smoothquant_factors(X: torch.Tensor, W: torch.Tensor, eps: float = 1e-5, gam
     _call("zq_smoothquant_factors", _ptr(X), _fdtype(X), M, K, eps, _ptr(W), _fdtype(W), N,
           _ptr(gamma), _ptr(beta), _ptr(s), _ptr(g), _ptr(b), _ptr(ws), need, _stream(X))
     return s, g, b
+
+
+# ---- Mixed-precision decomposition (outlier columns in fp16) ----
+
+def pack_outlier_weights(W: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Offline: W [N, K] (fp32/fp16) -> fp16 [K, N] (W transposed, nearest-even)."""
+    _need(W, "W", (torch.float32, torch.float16))
+    N, K = W.shape
+    Wt = torch.empty((K, N), dtype=torch.float16, device=W.device) if out is None else out
+    _need(Wt, "out", (torch.float16,), (K, N), W.device)
+    _call("zq_pack_outlier_weights", _ptr(W), _fdtype(W), N, K, _ptr(Wt), _stream(W))
+    return Wt
+
+
+def outlier_columns(X: torch.Tensor, alpha: float = 6.0, pre: int = PRE_LAYERNORM, gamma=None,
+                    beta=None, eps: float = 1e-5):
+    """Outlier set of the batch -> (slot int32 [K], cols int32 [K + 1]):
+    cols[0] = |O|, cols[1:1+|O|] ascending; slot[j] = position of j in O or -1."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    slot = torch.empty((K,), dtype=torch.int32, device=X.device)
+    cols = torch.empty((K + 1,), dtype=torch.int32, device=X.device)
+    _call("zq_outlier_columns", _ptr(X), _fdtype(X), M, K, pre, _ptr(gamma), _ptr(beta), eps,
+          alpha, _ptr(slot), _ptr(cols), _stream(X))
+    return slot, cols
+
+
+def ln_quant_decomp(X: torch.Tensor, slot: torch.Tensor, pre: int = PRE_LAYERNORM, gamma=None,
+                    beta=None, eps: float = 1e-5):
+    """Prologue of the INT8 part over the non-outlier columns ->
+    (Xq int8 [M, K], s_x fp32 [M], XO fp16 [M, K]; XO[m, p] = y of the p-th outlier column)."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    _need(slot, "slot", (torch.int32,), (K,), X.device)
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    s_x = torch.empty((M,), dtype=torch.float32, device=X.device)
+    XO = torch.empty((M, K), dtype=torch.float16, device=X.device)
+    _call("zq_ln_quant_decomp", _ptr(X), _fdtype(X), M, K, pre, _ptr(gamma), _ptr(beta), eps,
+          _ptr(slot), _ptr(Xq), _ptr(s_x), _ptr(XO), _stream(X))
+    return Xq, s_x, XO
+
+
+def w8a8_gemm_decomp(Xq: torch.Tensor, x_scales: torch.Tensor, Wq: torch.Tensor,
+                     w_scales: torch.Tensor, group_rows: int, cols: torch.Tensor, XO: torch.Tensor,
+                     W16t: torch.Tensor, bias=None, act: int = ACT_NONE):
+    """INT8 GEMM + dequant + FP16 outlier product (+bias, GeLU) -> fp16 [M, N]."""
+    _need(Xq, "Xq", (torch.int8,))
+    M, K = Xq.shape
+    _need(Wq, "Wq", (torch.int8,), None, Xq.device)
+    N = Wq.shape[0]
+    _need(x_scales, "x_scales", (torch.float32,), (M,), Xq.device)
+    _need(w_scales, "w_scales", (torch.float32,), (N // group_rows,), Xq.device)
+    _need(cols, "cols", (torch.int32,), (K + 1,), Xq.device)
+    _need(XO, "XO", (torch.float16,), (M, K), Xq.device)
+    _need(W16t, "W16t", (torch.float16,), (K, N), Xq.device)
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), (N,), Xq.device)
+    Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    _call("zq_w8a8_gemm_decomp", _ptr(Xq), _ptr(x_scales), _ptr(Wq), _ptr(w_scales), group_rows,
+          _ptr(cols), _ptr(XO), _ptr(W16t), _ptr(bias), act, M, N, K, _ptr(Y), _stream(Xq))
+    return Y
+
+
+def linear_decomp_workspace_bytes(M: int, K: int) -> int:
+    return int(library().zq_linear_decomp_workspace_bytes(M, K))
+
+
+def linear_w8a8_decomp(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor, group_rows: int,
+                       W16t: torch.Tensor, alpha: float = 6.0, pre: int = PRE_LAYERNORM,
+                       gamma=None, beta=None, eps: float = 1e-5, bias=None, act: int = ACT_NONE,
+                       workspace: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None):
+    """The decomposed layer (outlier columns in fp16, the rest W8A8) -> fp16 [M, N]."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    _need(Wq, "Wq", (torch.int8,), None, X.device)
+    N = Wq.shape[0]
+    _need(w_scales, "w_scales", (torch.float32,), (N // group_rows,), X.device)
+    _need(W16t, "W16t", (torch.float16,), (K, N), X.device)
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), (N,), X.device)
+    need = linear_decomp_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _call("zq_linear_w8a8_decomp", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps, alpha,
+          _ptr(Wq), _ptr(w_scales), group_rows, _ptr(W16t), _ptr(bias), act, M, N, K,
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
+    return Y

@@ -41,7 +41,7 @@ COMMON = [
 ]
 
 SOURCES = ["zq_api.hip", "ln_quant.hip", "gemm_tiled.hip", "gemm_skinny.hip", "offline.hip",
-           "unfused.hip"]
+           "unfused.hip", "decomp.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -1,0 +1,134 @@
+// Outlier-column bookkeeping and the fp16 weight copy of the mixed-precision
+// decomposition (LLM.int8() in "探秘Transformer系列之（36）--- 大模型量化方案"
+// 1.1, "方案" and "混合精度分解": columns whose activations exceed the threshold
+// stay in fp16 on both sides, the rest go through the int8 GEMM).
+//
+// The set O is a property of the whole batch, so it is found in its own pass
+// (k_ln_quant with DEC = 1 marks slot[col] = 1) between a clear and a
+// one-workgroup compaction that turns the marks into
+//   cols[0] = |O|, cols[1 + p] = the p-th outlier column (ascending),
+//   slot[j] = p for an outlier column j, -1 otherwise.
+// Both arrays are O(K) and stay in L2 for the passes that read them.
+//
+// The fp16 weights of the outlier columns are read by column: W16t is the
+// fp16 copy of W laid out [K x N] (input channel major), so one outlier
+// column is one contiguous run of N halves and the GEMM epilogue reads the
+// 32 columns of a fragment as 64 contiguous bytes.
+#include "zq_device.h"
+#include "zq_kernels.h"
+
+#include <algorithm>
+
+namespace zq {
+namespace {
+
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t *__restrict__ p, int64_t n, int32_t v)
+{
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+constexpr int kCompactThreads = 1024;
+
+// One workgroup.  Thread t owns columns [t * per, (t + 1) * per): it counts
+// its marks, an exclusive scan over the threads (in LDS) gives its first
+// position, and it rewrites its own columns.  No column is read by one
+// thread and written by another, so the rewrite needs no further barrier.
+__global__ __launch_bounds__(kCompactThreads) void k_outlier_compact(int32_t *__restrict__ slot,
+                                                                     int K,
+                                                                     int32_t *__restrict__ cols)
+{
+    __shared__ int scan[kCompactThreads];
+    const int t = threadIdx.x;
+    const int per = (K + kCompactThreads - 1) / kCompactThreads;
+    const int j0 = min(t * per, K);
+    const int j1 = min(j0 + per, K);
+    int cnt = 0;
+    for (int j = j0; j < j1; j++)
+        cnt += slot[j] != 0;
+    scan[t] = cnt;
+    __syncthreads();
+    // Hillis-Steele inclusive scan.
+    for (int d = 1; d < kCompactThreads; d <<= 1) {
+        const int add = t >= d ? scan[t - d] : 0;
+        __syncthreads();
+        scan[t] += add;
+        __syncthreads();
+    }
+    int p = scan[t] - cnt;
+    for (int j = j0; j < j1; j++) {
+        if (slot[j] != 0) {
+            slot[j] = p;
+            cols[1 + p] = j;
+            p++;
+        } else {
+            slot[j] = -1;
+        }
+    }
+    if (t == kCompactThreads - 1)
+        cols[0] = scan[t];
+}
+
+// W [N x K] (fp32 or fp16) -> W16t [K x N] fp16 (round to nearest even), through
+// a 64 x 64 LDS tile so that both the reads (along K) and the writes (along N)
+// are coalesced.  Block (x, y) covers rows n0 = 64 x .. n0 + 63 and columns
+// k0 = 64 y .. k0 + 63.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose_to_f16(const T *__restrict__ W, int N, int K,
+                                                          _Float16 *__restrict__ Wt)
+{
+    __shared__ _Float16 tile[64][64 + 2];
+    const int n0 = blockIdx.x * 64;
+    const int k0 = blockIdx.y * 64;
+    const int tx = threadIdx.x % 64;
+    const int ty = threadIdx.x / 64;
+#pragma unroll
+    for (int r = ty; r < 64; r += 4) {
+        const int n = n0 + r, k = k0 + tx;
+        tile[r][tx] = (n < N && k < K) ? (_Float16)W[(int64_t)n * K + k] : (_Float16)0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = ty; r < 64; r += 4) {
+        const int k = k0 + r, n = n0 + tx;
+        if (k < K && n < N)
+            Wt[(int64_t)k * N + n] = tile[tx][r];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_outlier_columns(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
+                                  const float *gamma, const float *beta, float eps, float alpha,
+                                  int32_t *slot, int32_t *cols, hipStream_t stream)
+{
+    const int64_t blocks = std::min<int64_t>((K + 255) / 256, 1024);
+    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)blocks), dim3(256), 0, stream, slot, K, 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    if (M > 0) {
+        e = launch_outlier_detect(X, x_f16, M, K, pre, gamma, beta, eps, alpha, slot, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(k_outlier_compact, dim3(1), dim3(kCompactThreads), 0, stream, slot, (int)K,
+                       cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_outlier_weights(const void *W, bool w_f16, int64_t N, int64_t K,
+                                       _Float16 *Wt, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((K + 63) / 64));
+    if (w_f16)
+        hipLaunchKernelGGL(k_transpose_to_f16<_Float16>, grid, dim3(256), 0, stream,
+                           static_cast<const _Float16 *>(W), (int)N, (int)K, Wt);
+    else
+        hipLaunchKernelGGL(k_transpose_to_f16<float>, grid, dim3(256), 0, stream,
+                           static_cast<const float *>(W), (int)N, (int)K, Wt);
+    return hipGetLastError();
+}
+
+}  // namespace zq

@@ -69,6 +69,15 @@ __device__ __forceinline__ void dma16(const int8_t *src, int8_t *lds_base)
                                      (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
+// The outlier part of the mixed-precision decomposition: cols[0] = P, cols[1 + p]
+// = the p-th outlier column; xo [M x K] fp16 holds token m's value of column
+// cols[1 + p] at xo[m * K + p]; wt [K x N] fp16 is W transposed.
+struct OutlierOperands {
+    const int32_t *cols;
+    const _Float16 *xo;
+    const _Float16 *wt;
+};
+
 template <int BM, int BN, int WM, int WN, int BK, int NSTAGE>
 struct Cfg {
     static constexpr int NW = WM * WN;                // waves per workgroup
@@ -118,13 +127,22 @@ constexpr int waves_per_simd()
 // F8: the operands are OCP E4M3 codes and the product is
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) accumulating in fp32;
 // OUT_I32 then writes the raw fp32 accumulators.
-template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool OUT_I32, int ACT, bool F8>
+//
+// ODEC (fp16 output only): the mixed-precision decomposition's outlier part
+// joins the epilogue.  The int32 accumulators are dequantized in place
+// (s_x s_w acc, kept as fp32 bits in the same registers), then for every 16
+// outlier columns one v_mfma_f32_32x32x16_f16 per fragment adds
+// sum_p XO[m, p] W16t[O_p, n] onto them: W16t is the A operand and XO the
+// B operand, so the fp16 product has the int8 accumulator layout.
+template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool OUT_I32, int ACT, bool F8,
+          bool ODEC = false>
 __global__ __launch_bounds__(WM *WN * 64)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                                    waves_per_simd<BM, BN, WM, WN>()))) void k_gemm_tiled(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int M, int N, int K,
-    void *__restrict__ Y, int tiles_m, int tiles_n, uint32_t *__restrict__ row_amax)
+    void *__restrict__ Y, int tiles_m, int tiles_n, uint32_t *__restrict__ row_amax,
+    OutlierOperands dec)
 {
     using C = Cfg<BM, BN, WM, WN, BK, NSTAGE>;
     // One LDS object per slab buffer, referenced statically from an unrolled
@@ -352,6 +370,66 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
         (wb == 0 ? lds0 : wb == 1 ? lds1 : wb == 2 ? lds2 : lds3) + (wave / NSTAGE) * 32 * RS;
     _Float16 *const Yh = static_cast<_Float16 *>(Y);
     const bool rows16 = (N & 7) == 0;            // 16-byte aligned rows of Y
+
+    if constexpr (ODEC) {
+        // Dequantize in place: from here on acc holds fp32 bits.
+#pragma unroll
+        for (int a = 0; a < C::FN; a++)
+#pragma unroll
+            for (int b = 0; b < C::FM; b++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int nl = wn * C::TWN + a * 32 + 8 * (r / 4) + 4 * fhalf + r % 4;
+                    acc[a][b][r] =
+                        __float_as_int((float)acc[a][b][r] * (sxm[b] * col_scale[nl]));
+                }
+        const int P = __builtin_amdgcn_readfirstlane(dec.cols[0]);
+        for (int p0 = 0; p0 < P; p0 += 16) {
+            // Lane (frow, fhalf) holds outlier positions pb .. pb + 7.
+            const int pb = p0 + 8 * fhalf;
+            h8 xo[C::FM], wo[C::FN];
+#pragma unroll
+            for (int b = 0; b < C::FM; b++) {
+                const int m = min(m0 + wm * C::TWM + b * 32 + frow, M - 1);
+                h8 v = {};
+                if (pb < P) {
+                    // pb + 8 <= K (K and pb are multiples of 8, pb < P <= K):
+                    // the load stays inside row m; positions >= P are dropped.
+                    const h8 raw = *reinterpret_cast<const h8 *>(dec.xo + (int64_t)m * K + pb);
+#pragma unroll
+                    for (int i = 0; i < 8; i++)
+                        v[i] = pb + i < P ? raw[i] : (_Float16)0.0f;
+                }
+                xo[b] = v;
+            }
+            int oc[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                oc[i] = pb + i < P ? dec.cols[1 + pb + i] : -1;
+#pragma unroll
+            for (int a = 0; a < C::FN; a++) {
+                const int n = min(n0 + wn * C::TWN + a * 32 + frow, N - 1);
+                h8 v;
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    v[i] = oc[i] >= 0 ? dec.wt[(int64_t)oc[i] * N + n] : (_Float16)0.0f;
+                wo[a] = v;
+            }
+#pragma unroll
+            for (int a = 0; a < C::FN; a++)
+#pragma unroll
+                for (int b = 0; b < C::FM; b++) {
+                    v16f c;
+#pragma unroll
+                    for (int r = 0; r < 16; r++)
+                        c[r] = __int_as_float(acc[a][b][r]);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(wo[a], xo[b], c, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; r++)
+                        acc[a][b][r] = __float_as_int(c[r]);
+                }
+        }
+    }
     // With row_amax, the tile also folds max |fp16 output| of each of its rows
     // into row_amax[m] (float bits; an atomic max after the two lanes that
     // hold a row have combined theirs), for a per-token quantizer downstream.
@@ -373,7 +451,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                     h4 o;
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
-                        float v = fmaf((float)acc[a][b][4 * q + i], sxm[b] * csv[i], cbv[i]);
+                        float v;
+                        if constexpr (ODEC)
+                            v = __int_as_float(acc[a][b][4 * q + i]) + cbv[i];
+                        else
+                            v = fmaf((float)acc[a][b][4 * q + i], sxm[b] * csv[i], cbv[i]);
                         if constexpr (ACT == 1)
                             v = gelu_fast(v);
                         o[i] = (_Float16)v;
@@ -421,26 +503,35 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
         epilogue(std::true_type{});
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool F8 = false>
+template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool F8 = false, bool ODEC = false>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
-                      void *Y, bool out_i32, hipStream_t stream, uint32_t *row_amax)
+                      void *Y, bool out_i32, hipStream_t stream, uint32_t *row_amax,
+                      const OutlierOperands *dec = nullptr)
 {
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)(tiles_m * tiles_n));
     const dim3 block(WM * WN * 64);
-#define ZQ_GEMM_LAUNCH(I32, A)                                                                    \
-    hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, BK, NSTAGE, I32, A, F8>), grid, block, 0,     \
-                       stream,                                                                    \
-                       Xq, sx, \
-                       Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y, tiles_m, tiles_n, row_amax)
-    if (out_i32)
-        ZQ_GEMM_LAUNCH(true, 0);
-    else if (act == 1)
-        ZQ_GEMM_LAUNCH(false, 1);
-    else
-        ZQ_GEMM_LAUNCH(false, 0);
+    const OutlierOperands od = dec ? *dec : OutlierOperands{nullptr, nullptr, nullptr};
+#define ZQ_GEMM_LAUNCH(I32, A, D)                                                                 \
+    hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, BK, NSTAGE, I32, A, F8, D>), grid, block, 0,  \
+                       stream, Xq, sx, Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y, tiles_m,  \
+                       tiles_n, row_amax, od)
+    if constexpr (ODEC) {
+        static_assert(!F8, "the outlier epilogue follows the int8 GEMM");
+        if (act == 1)
+            ZQ_GEMM_LAUNCH(false, 1, true);
+        else
+            ZQ_GEMM_LAUNCH(false, 0, true);
+    } else {
+        if (out_i32)
+            ZQ_GEMM_LAUNCH(true, 0, false);
+        else if (act == 1)
+            ZQ_GEMM_LAUNCH(false, 1, false);
+        else
+            ZQ_GEMM_LAUNCH(false, 0, false);
+    }
 #undef ZQ_GEMM_LAUNCH
     return hipGetLastError();
 }
@@ -508,6 +599,24 @@ hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8
     default: return ZQ_CFG(128, 128, 2, 2, 64, 4);
     }
 #undef ZQ_CFG
+}
+
+hipError_t launch_gemm_tiled_decomp(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                    const float *w_scales, int64_t G, const float *bias, int act,
+                                    int64_t M, int64_t N, int64_t K, const int32_t *cols,
+                                    const _Float16 *XO, const _Float16 *W16t, void *Y,
+                                    hipStream_t stream)
+{
+    const OutlierOperands dec{cols, XO, W16t};
+#define ZQ_CFGD(BM, BN, WM, WN, BK, NS)                                                          \
+    launch_cfg<BM, BN, WM, WN, BK, NS, false, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, \
+                                                    N, K, Y, false, stream, nullptr, &dec)
+    switch (pick_tile(M, N)) {
+    case 6: return ZQ_CFGD(256, 256, 2, 4, 128, 2);
+    case 7: return ZQ_CFGD(256, 192, 4, 2, 128, 2);
+    default: return ZQ_CFGD(128, 128, 2, 2, 64, 4);
+    }
+#undef ZQ_CFGD
 }
 
 hipError_t launch_gemm_tiled_fp8(const int8_t *Xq, const float *x_scales, const int8_t *Wq,

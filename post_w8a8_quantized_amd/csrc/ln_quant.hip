@@ -91,11 +91,23 @@ __device__ __forceinline__ uint2 quant8_fp8(const float (&y)[8], float scale, in
 // t, t + 64*WPT, ... (NCH of them).  With OUT_F16 the kernel stops after the
 // op and stores y as fp16 to Y16 (the unfused order, where a separate step
 // quantizes that tensor); Xq and sx are then unused.
-template <typename T, int NCH, int WPT, int TPB, bool OUT_F16 = false, bool FP8 = false>
+//
+// DEC selects the two passes of the mixed-precision decomposition (outlier
+// columns kept in fp16, LLM.int8() in "探秘Transformer系列之（36）" 1.1).  Both
+// passes run this same code up to y, so they see the same bits:
+//   DEC = 1: every column holding some |y| > alpha gets slot[col] = 1 (a
+//            plain store of the same value from every writer); nothing else.
+//   DEC = 2: slot[col] is the column's position p in the outlier list, or -1.
+//            y of an outlier column goes to XO[m * K + p] as fp16 and is then
+//            set to 0, so the absmax and the codes cover the other columns only
+//            (their codes there are 0).
+template <typename T, int NCH, int WPT, int TPB, bool OUT_F16 = false, bool FP8 = false,
+          int DEC = 0>
 __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
     const T *__restrict__ X, int M, int K, int pre, const float *__restrict__ gamma,
     const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx,
-    _Float16 *__restrict__ Y16, uint32_t *__restrict__ zero_rows)
+    _Float16 *__restrict__ Y16, uint32_t *__restrict__ zero_rows, float alpha,
+    int32_t *__restrict__ slot, _Float16 *__restrict__ XO)
 {
     constexpr int TT = kWave * WPT;  // threads per token
     const int wave = threadIdx.x / kWave;
@@ -196,6 +208,41 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
 #pragma unroll
             for (int e = 0; e < 8; e++)
                 y[i][e] = gelu_erf(y[i][e]);
+    }
+
+    if constexpr (DEC == 1) {
+        if (!live)
+            return;
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + TT * i;
+            if (c < nchunks) {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    if (fabsf(y[i][e]) > alpha)
+                        slot[c * 8 + e] = 1;
+            }
+        }
+        return;
+    }
+    if constexpr (DEC == 2) {
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + TT * i;
+            if (c < nchunks) {
+                const int4 s0 = *reinterpret_cast<const int4 *>(slot + c * 8);
+                const int4 s1 = *reinterpret_cast<const int4 *>(slot + c * 8 + 4);
+                const int sl[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    if (sl[e] >= 0) {
+                        if (live)
+                            XO[m * (int64_t)K + sl[e]] = (_Float16)y[i][e];
+                        y[i][e] = 0.0f;
+                    }
+                }
+            }
+        }
     }
 
     if constexpr (OUT_F16) {
@@ -513,10 +560,11 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
         sx[m] = scale;
 }
 
-template <typename T, int WPT, int TPB, bool OUT_F16 = false, bool FP8 = false>
+template <typename T, int WPT, int TPB, bool OUT_F16 = false, bool FP8 = false, int DEC = 0>
 hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
                       const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
-                      _Float16 *Y16 = nullptr, uint32_t *zero_rows = nullptr)
+                      _Float16 *Y16 = nullptr, uint32_t *zero_rows = nullptr, float alpha = 0.0f,
+                      int32_t *slot = nullptr, _Float16 *XO = nullptr)
 {
     const int64_t nchunks = K / 8;
     const int64_t per = (nchunks + kWave * WPT - 1) / (kWave * WPT);
@@ -524,9 +572,9 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
     const dim3 block(kWave * WPT * TPB);
 #define ZQ_LNQ_CASE(n)                                                                          \
     if (per <= n) {                                                                             \
-        hipLaunchKernelGGL((k_ln_quant<T, n, WPT, TPB, OUT_F16, FP8>), grid, block, 0, stream, \
-                           X,                                                                   \
-                           (int)M, (int)K, pre, gamma, beta, eps, Xq, sx, Y16, zero_rows);      \
+        hipLaunchKernelGGL((k_ln_quant<T, n, WPT, TPB, OUT_F16, FP8, DEC>), grid, block, 0,     \
+                           stream, X, (int)M, (int)K, pre, gamma, beta, eps, Xq, sx, Y16,       \
+                           zero_rows, alpha, slot, XO);                                         \
         return hipGetLastError();                                                               \
     }
     ZQ_LNQ_CASE(1)
@@ -605,6 +653,45 @@ hipError_t launch_ln_to_f16(const void *X, bool x_f16, int64_t M, int64_t K, int
                                                     nullptr, stream, Y16)
                      : launch_cfg<float, 16, 1, true>(x, M, K, pre, gamma, beta, eps, nullptr,
                                                      nullptr, stream, Y16);
+}
+
+namespace {
+template <typename T, int DEC>
+hipError_t launch_decomp_typed(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
+                               const float *beta, float eps, float alpha, int32_t *slot,
+                               int8_t *Xq, float *sx, _Float16 *XO, hipStream_t stream)
+{
+    if (K <= 8192)
+        return launch_cfg<T, 1, 4, false, false, DEC>(X, M, K, pre, gamma, beta, eps, Xq, sx,
+                                                      stream, nullptr, nullptr, alpha, slot, XO);
+    return launch_cfg<T, 16, 1, false, false, DEC>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream,
+                                                   nullptr, nullptr, alpha, slot, XO);
+}
+}  // namespace
+
+hipError_t launch_outlier_detect(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
+                                 const float *gamma, const float *beta, float eps, float alpha,
+                                 int32_t *slot, hipStream_t stream)
+{
+    if (x_f16)
+        return launch_decomp_typed<_Float16, 1>(static_cast<const _Float16 *>(X), M, K, pre, gamma,
+                                                beta, eps, alpha, slot, nullptr, nullptr, nullptr,
+                                                stream);
+    return launch_decomp_typed<float, 1>(static_cast<const float *>(X), M, K, pre, gamma, beta,
+                                         eps, alpha, slot, nullptr, nullptr, nullptr, stream);
+}
+
+hipError_t launch_ln_quant_decomp(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
+                                  const float *gamma, const float *beta, float eps,
+                                  const int32_t *slot, int8_t *Xq, float *x_scales, _Float16 *XO,
+                                  hipStream_t stream)
+{
+    int32_t *sl = const_cast<int32_t *>(slot);  // read only in this pass
+    if (x_f16)
+        return launch_decomp_typed<_Float16, 2>(static_cast<const _Float16 *>(X), M, K, pre, gamma,
+                                                beta, eps, 0.0f, sl, Xq, x_scales, XO, stream);
+    return launch_decomp_typed<float, 2>(static_cast<const float *>(X), M, K, pre, gamma, beta,
+                                         eps, 0.0f, sl, Xq, x_scales, XO, stream);
 }
 
 hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,

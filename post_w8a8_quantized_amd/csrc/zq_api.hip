@@ -608,3 +608,146 @@ ZQ_API zq_status zq_smoothquant_factors(const void *X, zq_dtype x_dtype, int64_t
                                              N, gamma, beta, smooth, gamma_out, beta_out,
                                              workspace, stream));
 }
+
+// ---- Mixed-precision decomposition (outlier columns in fp16) ----
+
+ZQ_API zq_status zq_pack_outlier_weights(const void *W, zq_dtype w_dtype, int64_t N, int64_t K,
+                                         void *W16t, hipStream_t stream)
+{
+    if (!W || !W16t)
+        return ZQ_ERR_NULL;
+    if (w_dtype != ZQ_F32 && w_dtype != ZQ_F16)
+        return ZQ_ERR_DTYPE;
+    if (N < 1 || !k_ok(K) || N > INT32_MAX || N * K > (int64_t)1 << 40)
+        return ZQ_ERR_SHAPE;
+    if (!aligned16(W) || !aligned16(W16t))
+        return ZQ_ERR_ALIGN;
+    clear_stale_error();
+    return map_hip(zq::launch_pack_outlier_weights(W, w_dtype == ZQ_F16, N, K,
+                                                   static_cast<_Float16 *>(W16t), stream));
+}
+
+ZQ_API zq_status zq_outlier_columns(const void *X, zq_dtype x_dtype, int64_t M, int64_t K,
+                                    zq_pre pre, const float *gamma, const float *beta, float eps,
+                                    float alpha, int32_t *slot, int32_t *cols, hipStream_t stream)
+{
+    if (!slot || !cols)
+        return ZQ_ERR_NULL;
+    // The prologue's checks; the codes and scales pointers it wants are not used here.
+    zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta,
+                                  reinterpret_cast<const int8_t *>(slot),
+                                  reinterpret_cast<const float *>(slot));
+    if (st != ZQ_OK)
+        return st;
+    if (!aligned16(slot))
+        return ZQ_ERR_ALIGN;
+    clear_stale_error();
+    return map_hip(zq::launch_outlier_columns(X, x_dtype == ZQ_F16, M, K, (int)pre,
+                                              pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
+                                              pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps,
+                                              alpha, slot, cols, stream));
+}
+
+ZQ_API zq_status zq_ln_quant_decomp(const void *X, zq_dtype x_dtype, int64_t M, int64_t K,
+                                    zq_pre pre, const float *gamma, const float *beta, float eps,
+                                    const int32_t *slot, int8_t *Xq, float *x_scales, void *XO,
+                                    hipStream_t stream)
+{
+    if (!slot || !XO)
+        return ZQ_ERR_NULL;
+    zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta, Xq, x_scales);
+    if (st != ZQ_OK)
+        return st;
+    if (!aligned16(slot) || !aligned16(XO))
+        return ZQ_ERR_ALIGN;
+    clear_stale_error();
+    return map_hip(zq::launch_ln_quant_decomp(X, x_dtype == ZQ_F16, M, K, (int)pre,
+                                              pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
+                                              pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, slot,
+                                              Xq, x_scales, static_cast<_Float16 *>(XO), stream));
+}
+
+ZQ_API zq_status zq_w8a8_gemm_decomp(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                     const float *w_scales, int64_t group_rows,
+                                     const int32_t *cols, const void *XO, const void *W16t,
+                                     const float *bias, zq_act act, int64_t M, int64_t N,
+                                     int64_t K, void *Y, hipStream_t stream)
+{
+    if (!cols || !XO || !W16t)
+        return ZQ_ERR_NULL;
+    zq_status st = check_gemm(Xq, x_scales, Wq, w_scales, group_rows, act, M, N, K, Y, ZQ_F16,
+                              bias);
+    if (st != ZQ_OK)
+        return st;
+    if (!aligned16(XO) || !aligned16(W16t))
+        return ZQ_ERR_ALIGN;
+    clear_stale_error();
+    return map_hip(zq::launch_gemm_tiled_decomp(
+        Xq, x_scales, Wq, w_scales, group_rows, bias, (int)act, M, N, K, cols,
+        static_cast<const _Float16 *>(XO), static_cast<const _Float16 *>(W16t), Y, stream));
+}
+
+// Workspace of zq_linear_w8a8_decomp: slot int32 [K] | cols int32 [K + 1] |
+// codes [M*K] | scales [M] | XO fp16 [M*K], each part starting on a 256-byte boundary.
+ZQ_API size_t zq_linear_decomp_workspace_bytes(int64_t M, int64_t K)
+{
+    if (M < 1 || !k_ok(K) || M > INT32_MAX || M * K > (int64_t)1 << 40)
+        return 0;
+    return round_up(4 * (size_t)K, 256) + round_up(4 * (size_t)(K + 1), 256) +
+           round_up((size_t)(M * K), 256) + round_up(4 * (size_t)M, 256) +
+           round_up(2 * (size_t)(M * K), 256);
+}
+
+ZQ_API zq_status zq_linear_w8a8_decomp(const void *X, zq_dtype x_dtype, zq_pre pre,
+                                       const float *gamma, const float *beta, float eps,
+                                       float alpha, const int8_t *Wq, const float *w_scales,
+                                       int64_t group_rows, const void *W16t, const float *bias,
+                                       zq_act act, int64_t M, int64_t N, int64_t K,
+                                       void *workspace, size_t workspace_bytes, void *Y,
+                                       hipStream_t stream)
+{
+    if (!X || !Wq || !w_scales || !W16t || !Y)
+        return ZQ_ERR_NULL;
+    if (!workspace)
+        return ZQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return ZQ_ERR_ALIGN;
+    const size_t need = zq_linear_decomp_workspace_bytes(M, K);
+    const size_t kk = (size_t)(K > 0 ? K : 0);
+    const size_t mk = (size_t)(M > 0 && K > 0 ? M * K : 0);
+    char *ws = static_cast<char *>(workspace);
+    size_t off = 0;
+    int32_t *slot = reinterpret_cast<int32_t *>(ws + off);
+    off += round_up(4 * kk, 256);
+    int32_t *cols = reinterpret_cast<int32_t *>(ws + off);
+    off += round_up(4 * (kk + 1), 256);
+    int8_t *Xq = reinterpret_cast<int8_t *>(ws + off);
+    off += round_up(mk, 256);
+    float *x_scales = reinterpret_cast<float *>(ws + off);
+    off += round_up(4 * (size_t)(M > 0 ? M : 0), 256);
+    _Float16 *XO = reinterpret_cast<_Float16 *>(ws + off);
+    zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta, Xq, x_scales);
+    if (st != ZQ_OK)
+        return st;
+    st = check_gemm(Xq, x_scales, Wq, w_scales, group_rows, act, M, N, K, Y, ZQ_F16, bias);
+    if (st != ZQ_OK)
+        return st;
+    if (!aligned16(W16t))
+        return ZQ_ERR_ALIGN;
+    if (workspace_bytes < need)
+        return ZQ_ERR_WORKSPACE;
+    const float *g = pre == ZQ_PRE_LAYERNORM ? gamma : nullptr;
+    const float *b = pre == ZQ_PRE_LAYERNORM ? beta : nullptr;
+    clear_stale_error();
+    st = map_hip(zq::launch_outlier_columns(X, x_dtype == ZQ_F16, M, K, (int)pre, g, b, eps, alpha,
+                                            slot, cols, stream));
+    if (st != ZQ_OK)
+        return st;
+    st = map_hip(zq::launch_ln_quant_decomp(X, x_dtype == ZQ_F16, M, K, (int)pre, g, b, eps, slot,
+                                            Xq, x_scales, XO, stream));
+    if (st != ZQ_OK)
+        return st;
+    return map_hip(zq::launch_gemm_tiled_decomp(Xq, x_scales, Wq, w_scales, group_rows, bias,
+                                                (int)act, M, N, K, cols, XO,
+                                                static_cast<const _Float16 *>(W16t), Y, stream));
+}

@@ -65,6 +65,32 @@ hipError_t launch_gemm_skinny_fp8(const int8_t *Xq, const float *x_scales, const
                                   int64_t M, int64_t N, int64_t K, void *Y, bool out_raw,
                                   bool packed, hipStream_t stream);
 
+// Mixed-precision decomposition (outlier columns in fp16).
+// Outlier set: slot [K] and cols [K + 1] as k_outlier_compact leaves them
+// (cols[0] = |O|, cols[1..] ascending; slot[j] = position or -1).
+hipError_t launch_outlier_columns(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
+                                  const float *gamma, const float *beta, float eps, float alpha,
+                                  int32_t *slot, int32_t *cols, hipStream_t stream);
+// The marking pass alone (slot must be cleared first).
+hipError_t launch_outlier_detect(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
+                                 const float *gamma, const float *beta, float eps, float alpha,
+                                 int32_t *slot, hipStream_t stream);
+// Prologue over the non-outlier columns; outlier values to XO [M x K] fp16 at
+// XO[m * K + position].
+hipError_t launch_ln_quant_decomp(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
+                                  const float *gamma, const float *beta, float eps,
+                                  const int32_t *slot, int8_t *Xq, float *x_scales, _Float16 *XO,
+                                  hipStream_t stream);
+// Tiled GEMM whose epilogue adds the fp16 outlier product (fp16 output).
+hipError_t launch_gemm_tiled_decomp(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                    const float *w_scales, int64_t G, const float *bias, int act,
+                                    int64_t M, int64_t N, int64_t K, const int32_t *cols,
+                                    const _Float16 *XO, const _Float16 *W16t, void *Y,
+                                    hipStream_t stream);
+// Offline: W [N x K] (fp32 / fp16) -> W16t [K x N] fp16.
+hipError_t launch_pack_outlier_weights(const void *W, bool w_f16, int64_t N, int64_t K,
+                                       _Float16 *W16t, hipStream_t stream);
+
 // Offline re-layout of Wq [N x K] into 32-row x 512-byte blocks (zero padded)
 // that the weight-streaming kernel reads as contiguous 16 KB runs.
 int64_t packed_weights_bytes(int64_t N, int64_t K);

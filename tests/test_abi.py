@@ -26,7 +26,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = zq.exported_symbols()
-    assert len(names) == 22
+    assert len(names) == 28
     out = subprocess.run(["nm", "-D", "--defined-only", zq.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -228,6 +228,86 @@ def test_ffn_validation(L, kw, want):
     assert L.zq_ffn_w8a8(a["X"], 1, None, None, 1e-5, a["W1"], A, a["G1"], None, a["W2"], A,
                          a["G2"], None, a["M"], a["K"], a["F"], a["ws"], a["wsb"], A,
                          None) == want
+
+
+def test_decomp_workspace_sizes(L):
+    r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    M, K = 4096, 5120
+    assert L.zq_linear_decomp_workspace_bytes(M, K) == \
+        r(4 * K) + r(4 * (K + 1)) + r(M * K) + r(4 * M) + r(2 * M * K)
+    assert L.zq_linear_decomp_workspace_bytes(1, 16) == 5 * 256
+    assert L.zq_linear_decomp_workspace_bytes(0, 16) == 0
+    assert L.zq_linear_decomp_workspace_bytes(4, 24) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(X=None), NULL), (dict(Wq=None), NULL), (dict(sw=None), NULL), (dict(Wt=None), NULL),
+    (dict(Y=None), NULL), (dict(ws=None), WS), (dict(wsb=4096), WS), (dict(ws=A + 16), ALIGN),
+    (dict(K=40), SHAPE), (dict(G=100), SHAPE), (dict(M=0), SHAPE), (dict(dt=3), DTYPE),
+    (dict(pre=3), DTYPE), (dict(act=5), DTYPE), (dict(X=UNALIGNED), ALIGN),
+    (dict(Wt=UNALIGNED), ALIGN),
+])
+def test_linear_decomp_validation(L, kw, want):
+    a = dict(X=A, dt=1, pre=1, Wq=A, sw=A, G=128, Wt=A, M=16, N=256, K=256, ws=A, wsb=1 << 30,
+             Y=A, act=0)
+    a.update(kw)
+    assert L.zq_linear_w8a8_decomp(a["X"], a["dt"], a["pre"], None, None, 1e-5, 6.0, a["Wq"],
+                                   a["sw"], a["G"], a["Wt"], None, a["act"], a["M"], a["N"],
+                                   a["K"], a["ws"], a["wsb"], a["Y"], None) == want
+
+
+def test_linear_decomp_workspace_exact_size_accepted(L):
+    need = L.zq_linear_decomp_workspace_bytes(16, 256)
+    call = lambda wsb: L.zq_linear_w8a8_decomp(A, 1, 1, None, None, 1e-5, 6.0, A, A, 128, A,  # noqa: E731
+                                               None, 0, 16, 256, 256, A, wsb, A, None)
+    assert call(need) in (OK, HIP)
+    assert call(need - 1) == WS
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(X=None), NULL), (dict(slot=None), NULL), (dict(cols=None), NULL),
+    (dict(K=24), SHAPE), (dict(M=0), SHAPE), (dict(dt=2), DTYPE), (dict(pre=7), DTYPE),
+    (dict(X=UNALIGNED), ALIGN), (dict(slot=UNALIGNED), ALIGN),
+])
+def test_outlier_columns_validation(L, kw, want):
+    a = dict(X=A, dt=1, pre=1, M=16, K=256, slot=A, cols=A)
+    a.update(kw)
+    assert L.zq_outlier_columns(a["X"], a["dt"], a["M"], a["K"], a["pre"], None, None, 1e-5, 6.0,
+                                a["slot"], a["cols"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(X=None), NULL), (dict(slot=None), NULL), (dict(Xq=None), NULL), (dict(sx=None), NULL),
+    (dict(XO=None), NULL), (dict(K=24), SHAPE), (dict(XO=UNALIGNED), ALIGN),
+    (dict(slot=UNALIGNED), ALIGN), (dict(Xq=UNALIGNED), ALIGN),
+])
+def test_ln_quant_decomp_validation(L, kw, want):
+    a = dict(X=A, M=16, K=256, slot=A, Xq=A, sx=A, XO=A)
+    a.update(kw)
+    assert L.zq_ln_quant_decomp(a["X"], 1, a["M"], a["K"], 1, None, None, 1e-5, a["slot"], a["Xq"],
+                                a["sx"], a["XO"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Xq=None), NULL), (dict(sx=None), NULL), (dict(cols=None), NULL), (dict(XO=None), NULL),
+    (dict(Wt=None), NULL), (dict(Y=None), NULL), (dict(N=250, G=2), SHAPE), (dict(K=40), SHAPE),
+    (dict(act=2), DTYPE), (dict(XO=UNALIGNED), ALIGN), (dict(Wt=UNALIGNED), ALIGN),
+])
+def test_gemm_decomp_validation(L, kw, want):
+    a = dict(Xq=A, sx=A, G=128, cols=A, XO=A, Wt=A, act=0, M=16, N=256, K=256, Y=A)
+    a.update(kw)
+    assert L.zq_w8a8_gemm_decomp(a["Xq"], a["sx"], A, A, a["G"], a["cols"], a["XO"], a["Wt"], None,
+                                 a["act"], a["M"], a["N"], a["K"], a["Y"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(W=None), NULL), (dict(Wt=None), NULL), (dict(dt=2), DTYPE), (dict(N=0), SHAPE),
+    (dict(K=20), SHAPE), (dict(W=UNALIGNED), ALIGN), (dict(Wt=UNALIGNED), ALIGN),
+])
+def test_pack_outlier_weights_validation(L, kw, want):
+    a = dict(W=A, dt=0, N=256, K=256, Wt=A)
+    a.update(kw)
+    assert L.zq_pack_outlier_weights(a["W"], a["dt"], a["N"], a["K"], a["Wt"], None) == want
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="checks the no-GPU error path")
