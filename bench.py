@@ -53,6 +53,9 @@ def parse():
                     help="skip the unfused-order comparison (prefill workloads)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 (E4M3, power-of-two scales) variant timing")
+    ap.add_argument("--no-decomp", action="store_true",
+                    help="skip the outlier-workload leg (SmoothQuant fold vs the LLM.int8() "
+                         "mixed-precision decomposition)")
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip the chained FFN block timing (bert_ffn_up)")
     ap.add_argument("--cpu-seconds", type=float, default=5.0,
@@ -131,6 +134,104 @@ def calib_copy(torch, mb):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes": n, "launches": 5}), flush=True)
+
+
+def outlier_leg(torch, zq, w, make_inputs, args, dev):
+    """Times the outlier workload with the SmoothQuant fold (fused layer) and with
+    the mixed-precision decomposition, plus the decomposition's stages."""
+    inp = make_inputs(w)
+    M, N, K = w.M, w.N, w.K
+    Xd = torch.from_numpy(inp.X).to(dev)
+    Wd = torch.from_numpy(inp.W).to(dev)
+    gamma = torch.from_numpy(inp.gamma).to(dev)
+    beta = torch.from_numpy(inp.beta).to(dev)
+    alpha, G1 = 6.0, 1
+    smooth, g_s, b_s = zq.smoothquant_factors(Xd, Wd, w.eps, gamma, beta)
+    Wq_s, sw_s = zq.quantize_weights_grouped(Wd, w.group_rows, smooth)
+    Wq_d, sw_d = zq.quantize_weights_grouped(Wd, G1)
+    Wt = zq.pack_outlier_weights(Wd)
+    del Wd, smooth
+    torch.cuda.synchronize()
+    set_bytes = 2 * M * K + N * K * 4 + 2 * M * N + 3 * M * K
+    nsets = max(2, math.ceil(args.rotate_mb * 1e6 / set_bytes))
+    ws_lin = zq.linear_workspace_bytes(M, K)
+    ws_dec = zq.linear_decomp_workspace_bytes(M, K)
+    sets = []
+    for i in range(nsets):
+        sets.append(dict(
+            X=Xd if i == 0 else Xd.clone(),
+            Wq_s=Wq_s if i == 0 else Wq_s.clone(),
+            Wq_d=Wq_d if i == 0 else Wq_d.clone(),
+            Wt=Wt if i == 0 else Wt.clone(),
+            ws=torch.empty(max(ws_lin, ws_dec), dtype=torch.uint8, device=dev),
+            Y=torch.empty((M, N), dtype=torch.float16, device=dev)))
+
+    def smoothquant(i):
+        s = sets[i % nsets]
+        zq.linear_w8a8(s["X"], s["Wq_s"], sw_s, w.group_rows, w.pre, g_s, b_s, w.eps, None,
+                       w.act, workspace=s["ws"], out=s["Y"])
+
+    def decomposed(i):
+        s = sets[i % nsets]
+        zq.linear_w8a8_decomp(s["X"], s["Wq_d"], sw_d, G1, s["Wt"], alpha, w.pre, gamma, beta,
+                              w.eps, None, w.act, workspace=s["ws"], out=s["Y"])
+
+    # The stages, on the buffers zq_linear_w8a8_decomp uses (same workspace layout).
+    def parts(s):
+        r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+        ws = s["ws"]
+        o_cols = r(4 * K)
+        o_xq = o_cols + r(4 * (K + 1))
+        o_sx = o_xq + r(M * K)
+        o_xo = o_sx + r(4 * M)
+        return (ws[:4 * K].view(torch.int32), ws[o_cols:o_cols + 4 * (K + 1)].view(torch.int32),
+                ws[o_xq:o_xq + M * K].view(torch.int8).view(M, K),
+                ws[o_sx:o_sx + 4 * M].view(torch.float32),
+                ws[o_xo:o_xo + 2 * M * K].view(torch.float16).view(M, K))
+
+    def stage_columns(i):
+        s = sets[i % nsets]
+        slot, cols, _, _, _ = parts(s)
+        zq.outlier_columns(s["X"], alpha, w.pre, gamma, beta, w.eps, out=(slot, cols))
+
+    def stage_prologue(i):
+        s = sets[i % nsets]
+        slot, _, xq, sx, xo = parts(s)
+        zq.ln_quant_decomp(s["X"], slot, w.pre, gamma, beta, w.eps, out=(xq, sx, xo))
+
+    def stage_gemm(i):
+        s = sets[i % nsets]
+        _, cols, xq, sx, xo = parts(s)
+        zq.w8a8_gemm_decomp(xq, sx, s["Wq_d"], sw_d, G1, cols, xo, s["Wt"], None, w.act,
+                            out=s["Y"])
+
+    res = {}
+    for name, fn in (("smoothquant", smoothquant), ("decomposed", decomposed),
+                     ("columns", stage_columns), ("prologue", stage_prologue),
+                     ("gemm", stage_gemm)):
+        for i in range(nsets):
+            fn(i)
+        g = graph_of(torch, fn, args.steps)
+        time_graph(torch, g)
+        res[name] = time_graph(torch, g)[0] / args.steps
+        del g
+    torch.cuda.synchronize()
+    n_out = int(parts(sets[0])[1][0].item())
+    ops = 2.0 * M * N * K
+    out = {"workload": f"{w.name}: X fp16 [{M} x {K}], W [{N} x {K}], 0.5% channels x100",
+           "smoothquant_fused_us": round(res["smoothquant"] * 1e3, 3),
+           "smoothquant_TOPS": round(ops / (res["smoothquant"] * 1e-3) / 1e12, 2),
+           "decomposed_us": round(res["decomposed"] * 1e3, 3),
+           "decomposed_TOPS": round(ops / (res["decomposed"] * 1e-3) / 1e12, 2),
+           "decomposed_breakdown_us": {"outlier_columns": round(res["columns"] * 1e3, 3),
+                                       "prologue": round(res["prologue"] * 1e3, 3),
+                                       "gemm_with_fp16_part": round(res["gemm"] * 1e3, 3)},
+           "alpha": alpha, "outlier_columns": n_out,
+           "weights": {"smoothquant": f"group_rows={w.group_rows}",
+                       "decomposed": "group_rows=1 (per output channel) + fp16 [K x N] copy"}}
+    del sets, Xd, Wq_s, Wq_d, Wt
+    torch.cuda.synchronize()
+    return out
 
 
 def main():
@@ -363,6 +464,14 @@ def main():
                               else (ops / (ms8 * 1e-3) / 1e12), 2),
                "unit": "GB/s" if decode else "TOPS"}
 
+    # ---- the outlier workload (X fp16 [4096 x 5120], 0.5% of channels x100, LayerNorm;
+    # W [13824 x 5120]) under its two treatments: the SmoothQuant fold with the fused
+    # W8A8 layer (G = 128), and the mixed-precision decomposition (outlier columns in
+    # fp16, per-output-channel int8 weights, alpha = 6).  Each on its own rotated sets.
+    decomp = None
+    if not args.no_decomp:
+        decomp = outlier_leg(torch, zq, WORKLOADS["outlier_smooth"], make_inputs, args, dev)
+
     # ---- CPU oracle on the host cores (a reported baseline, not the target)
     cpu = None
     if not args.no_cpu_baseline:
@@ -414,6 +523,7 @@ def main():
         "ablation": ablation,
         "ffn_block": ffn,
         "fp8_variant": fp8,
+        "outlier_decomposition": decomp,
     }
     print(json.dumps(out), flush=True)
 

@@ -509,7 +509,8 @@ def pack_outlier_weights(W: torch.Tensor, out: Optional[torch.Tensor] = None) ->
 
 
 def outlier_columns(X: torch.Tensor, alpha: float = 6.0, pre: int = PRE_LAYERNORM, gamma=None,
-                    beta=None, eps: float = 1e-5):
+                    beta=None, eps: float = 1e-5,
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
     """Outlier set of the batch -> (slot int32 [K], cols int32 [K + 1]):
     cols[0] = |O|, cols[1:1+|O|] ascending; slot[j] = position of j in O or -1."""
     _need(X, "X", (torch.float32, torch.float16))
@@ -517,15 +518,21 @@ def outlier_columns(X: torch.Tensor, alpha: float = 6.0, pre: int = PRE_LAYERNOR
     for name, t in (("gamma", gamma), ("beta", beta)):
         if t is not None:
             _need(t, name, (torch.float32,), (K,), X.device)
-    slot = torch.empty((K,), dtype=torch.int32, device=X.device)
-    cols = torch.empty((K + 1,), dtype=torch.int32, device=X.device)
+    if out is None:
+        slot = torch.empty((K,), dtype=torch.int32, device=X.device)
+        cols = torch.empty((K + 1,), dtype=torch.int32, device=X.device)
+    else:
+        slot, cols = out
+    _need(slot, "slot", (torch.int32,), (K,), X.device)
+    _need(cols, "cols", (torch.int32,), (K + 1,), X.device)
     _call("zq_outlier_columns", _ptr(X), _fdtype(X), M, K, pre, _ptr(gamma), _ptr(beta), eps,
           alpha, _ptr(slot), _ptr(cols), _stream(X))
     return slot, cols
 
 
 def ln_quant_decomp(X: torch.Tensor, slot: torch.Tensor, pre: int = PRE_LAYERNORM, gamma=None,
-                    beta=None, eps: float = 1e-5):
+                    beta=None, eps: float = 1e-5,
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """Prologue of the INT8 part over the non-outlier columns ->
     (Xq int8 [M, K], s_x fp32 [M], XO fp16 [M, K]; XO[m, p] = y of the p-th outlier column)."""
     _need(X, "X", (torch.float32, torch.float16))
@@ -534,9 +541,15 @@ def ln_quant_decomp(X: torch.Tensor, slot: torch.Tensor, pre: int = PRE_LAYERNOR
     for name, t in (("gamma", gamma), ("beta", beta)):
         if t is not None:
             _need(t, name, (torch.float32,), (K,), X.device)
-    Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
-    s_x = torch.empty((M,), dtype=torch.float32, device=X.device)
-    XO = torch.empty((M, K), dtype=torch.float16, device=X.device)
+    if out is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+        s_x = torch.empty((M,), dtype=torch.float32, device=X.device)
+        XO = torch.empty((M, K), dtype=torch.float16, device=X.device)
+    else:
+        Xq, s_x, XO = out
+    _need(Xq, "Xq", (torch.int8,), (M, K), X.device)
+    _need(s_x, "s_x", (torch.float32,), (M,), X.device)
+    _need(XO, "XO", (torch.float16,), (M, K), X.device)
     _call("zq_ln_quant_decomp", _ptr(X), _fdtype(X), M, K, pre, _ptr(gamma), _ptr(beta), eps,
           _ptr(slot), _ptr(Xq), _ptr(s_x), _ptr(XO), _stream(X))
     return Xq, s_x, XO
@@ -544,7 +557,8 @@ def ln_quant_decomp(X: torch.Tensor, slot: torch.Tensor, pre: int = PRE_LAYERNOR
 
 def w8a8_gemm_decomp(Xq: torch.Tensor, x_scales: torch.Tensor, Wq: torch.Tensor,
                      w_scales: torch.Tensor, group_rows: int, cols: torch.Tensor, XO: torch.Tensor,
-                     W16t: torch.Tensor, bias=None, act: int = ACT_NONE):
+                     W16t: torch.Tensor, bias=None, act: int = ACT_NONE,
+                     out: Optional[torch.Tensor] = None):
     """INT8 GEMM + dequant + FP16 outlier product (+bias, GeLU) -> fp16 [M, N]."""
     _need(Xq, "Xq", (torch.int8,))
     M, K = Xq.shape
@@ -557,7 +571,8 @@ def w8a8_gemm_decomp(Xq: torch.Tensor, x_scales: torch.Tensor, Wq: torch.Tensor,
     _need(W16t, "W16t", (torch.float16,), (K, N), Xq.device)
     if bias is not None:
         _need(bias, "bias", (torch.float32,), (N,), Xq.device)
-    Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device) if out is None else out
+    _need(Y, "out", (torch.float16,), (M, N), Xq.device)
     _call("zq_w8a8_gemm_decomp", _ptr(Xq), _ptr(x_scales), _ptr(Wq), _ptr(w_scales), group_rows,
           _ptr(cols), _ptr(XO), _ptr(W16t), _ptr(bias), act, M, N, K, _ptr(Y), _stream(Xq))
     return Y

@@ -560,7 +560,10 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
         sx[m] = scale;
 }
 
-template <typename T, int WPT, int TPB, bool OUT_F16 = false, bool FP8 = false, int DEC = 0>
+// MAXN: the most 16-byte pieces per lane this shape is launched with (cases
+// above it are not instantiated; a row needing more is an invalid launch).
+template <typename T, int WPT, int TPB, bool OUT_F16 = false, bool FP8 = false, int DEC = 0,
+          int MAXN = 16>
 hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
                       const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
                       _Float16 *Y16 = nullptr, uint32_t *zero_rows = nullptr, float alpha = 0.0f,
@@ -571,6 +574,7 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
     const dim3 grid((unsigned)((M + TPB - 1) / TPB));
     const dim3 block(kWave * WPT * TPB);
 #define ZQ_LNQ_CASE(n)                                                                          \
+    if constexpr (n <= MAXN)                                                                    \
     if (per <= n) {                                                                             \
         hipLaunchKernelGGL((k_ln_quant<T, n, WPT, TPB, OUT_F16, FP8, DEC>), grid, block, 0,     \
                            stream, X, (int)M, (int)K, pre, gamma, beta, eps, Xq, sx, Y16,       \
@@ -588,6 +592,28 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
     ZQ_LNQ_CASE(16)
 #undef ZQ_LNQ_CASE
     return hipErrorInvalidValue;
+}
+
+// Waves per token by row length.  Rows up to 2048 elements take one wave
+// (four tokens per block).  Up to 8192 they take four waves (one token per
+// block): each lane then holds at most four 16-byte pieces of the row, few
+// enough registers for six to eight waves per SIMD, so the loads of some
+// tokens overlap the arithmetic of others (one wave per token, holding up to
+// 16 pieces, left room for two or three).  Longer rows take 16 waves.
+template <typename T, bool OUT_F16, bool FP8, int DEC>
+hipError_t launch_rows(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
+                       const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
+                       _Float16 *Y16, uint32_t *zero_rows, float alpha = 0.0f,
+                       int32_t *slot = nullptr, _Float16 *XO = nullptr)
+{
+    if (K <= 2048)
+        return launch_cfg<T, 1, 4, OUT_F16, FP8, DEC, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx,
+                                                         stream, Y16, zero_rows, alpha, slot, XO);
+    if (K <= 8192)
+        return launch_cfg<T, 4, 1, OUT_F16, FP8, DEC, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx,
+                                                         stream, Y16, zero_rows, alpha, slot, XO);
+    return launch_cfg<T, 16, 1, OUT_F16, FP8, DEC, 16>(X, M, K, pre, gamma, beta, eps, Xq, sx,
+                                                       stream, Y16, zero_rows, alpha, slot, XO);
 }
 
 template <typename T>
@@ -620,19 +646,11 @@ hipError_t launch_typed(const T *X, int64_t M, int64_t K, int pre, const float *
 #undef ZQ_ROWSEG
         return hipGetLastError();
     }
-    // Rows up to 64 lanes x 16 chunks x 8 = 8192 elements: one wave per token,
-    // four tokens per block.
     if (fp8)
-        return K <= 8192 ? launch_cfg<T, 1, 4, false, true>(X, M, K, pre, gamma, beta, eps, Xq, sx,
-                                                            stream, nullptr, zero_rows)
-                         : launch_cfg<T, 16, 1, false, true>(X, M, K, pre, gamma, beta, eps, Xq,
-                                                             sx, stream, nullptr, zero_rows);
-    if (K <= 8192)
-        return launch_cfg<T, 1, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream, nullptr,
-                                   zero_rows);
-    // Otherwise 16 waves per token.
-    return launch_cfg<T, 16, 1>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream, nullptr,
-                                zero_rows);
+        return launch_rows<T, false, true, 0>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream,
+                                              nullptr, zero_rows);
+    return launch_rows<T, false, false, 0>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream, nullptr,
+                                           zero_rows);
 }
 
 }  // namespace
@@ -641,18 +659,12 @@ hipError_t launch_ln_to_f16(const void *X, bool x_f16, int64_t M, int64_t K, int
                             const float *gamma, const float *beta, float eps, _Float16 *Y16,
                             hipStream_t stream)
 {
-    if (x_f16) {
-        const _Float16 *x = static_cast<const _Float16 *>(X);
-        return K <= 8192 ? launch_cfg<_Float16, 1, 4, true>(x, M, K, pre, gamma, beta, eps, nullptr,
-                                                           nullptr, stream, Y16)
-                         : launch_cfg<_Float16, 16, 1, true>(x, M, K, pre, gamma, beta, eps,
-                                                            nullptr, nullptr, stream, Y16);
-    }
-    const float *x = static_cast<const float *>(X);
-    return K <= 8192 ? launch_cfg<float, 1, 4, true>(x, M, K, pre, gamma, beta, eps, nullptr,
-                                                    nullptr, stream, Y16)
-                     : launch_cfg<float, 16, 1, true>(x, M, K, pre, gamma, beta, eps, nullptr,
-                                                     nullptr, stream, Y16);
+    if (x_f16)
+        return launch_rows<_Float16, true, false, 0>(static_cast<const _Float16 *>(X), M, K, pre,
+                                                     gamma, beta, eps, nullptr, nullptr, stream,
+                                                     Y16, nullptr);
+    return launch_rows<float, true, false, 0>(static_cast<const float *>(X), M, K, pre, gamma, beta,
+                                              eps, nullptr, nullptr, stream, Y16, nullptr);
 }
 
 namespace {
@@ -661,11 +673,8 @@ hipError_t launch_decomp_typed(const T *X, int64_t M, int64_t K, int pre, const 
                                const float *beta, float eps, float alpha, int32_t *slot,
                                int8_t *Xq, float *sx, _Float16 *XO, hipStream_t stream)
 {
-    if (K <= 8192)
-        return launch_cfg<T, 1, 4, false, false, DEC>(X, M, K, pre, gamma, beta, eps, Xq, sx,
-                                                      stream, nullptr, nullptr, alpha, slot, XO);
-    return launch_cfg<T, 16, 1, false, false, DEC>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream,
-                                                   nullptr, nullptr, alpha, slot, XO);
+    return launch_rows<T, false, false, DEC>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream,
+                                             nullptr, nullptr, alpha, slot, XO);
 }
 }  // namespace
 

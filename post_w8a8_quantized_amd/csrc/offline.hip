@@ -152,8 +152,8 @@ hipError_t quantize_typed(const T *W, const float *smooth, int64_t N, int64_t K,
 // ---- SmoothQuant statistics ----
 
 // Per-token LayerNorm statistics (gamma = 1, beta = 0): mean and 1/sqrt(var + eps),
-// fp32, two passes, one wave per token, same arithmetic order as the prologue's
-// per-lane partial sums is not required here (the factor is compared to tolerance).
+// fp32, two passes, one wave per token.  The summation order need not match the
+// prologue's: the factors feed an offline fold, not a code decision.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_ln_stats(const T *__restrict__ X, int M, int K,
                                                        float eps, float *__restrict__ stats)
