@@ -205,10 +205,17 @@ def outlier_leg(torch, zq, w, make_inputs, args, dev):
         zq.w8a8_gemm_decomp(xq, sx, s["Wq_d"], sw_d, G1, cols, xo, s["Wt"], None, w.act,
                             out=s["Y"])
 
+    # The int8 GEMM alone on the same codes and weights (no fp16 part): what the
+    # fp16 outlier epilogue adds, separated from data-dependent clock effects.
+    def stage_gemm_int8(i):
+        s = sets[i % nsets]
+        _, _, xq, sx, _ = parts(s)
+        zq.w8a8_gemm_dequant(xq, sx, s["Wq_d"], sw_d, G1, None, w.act, out=s["Y"])
+
     res = {}
     for name, fn in (("smoothquant", smoothquant), ("decomposed", decomposed),
                      ("columns", stage_columns), ("prologue", stage_prologue),
-                     ("gemm", stage_gemm)):
+                     ("gemm", stage_gemm), ("gemm_int8", stage_gemm_int8)):
         for i in range(nsets):
             fn(i)
         g = graph_of(torch, fn, args.steps)
@@ -225,7 +232,9 @@ def outlier_leg(torch, zq, w, make_inputs, args, dev):
            "decomposed_TOPS": round(ops / (res["decomposed"] * 1e-3) / 1e12, 2),
            "decomposed_breakdown_us": {"outlier_columns": round(res["columns"] * 1e3, 3),
                                        "prologue": round(res["prologue"] * 1e3, 3),
-                                       "gemm_with_fp16_part": round(res["gemm"] * 1e3, 3)},
+                                       "gemm_with_fp16_part": round(res["gemm"] * 1e3, 3),
+                                       "same_gemm_without_fp16_part":
+                                           round(res["gemm_int8"] * 1e3, 3)},
            "alpha": alpha, "outlier_columns": n_out,
            "weights": {"smoothquant": f"group_rows={w.group_rows}",
                        "decomposed": "group_rows=1 (per output channel) + fp16 [K x N] copy"}}

@@ -154,6 +154,20 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
     __shared__ __attribute__((aligned(1024))) int8_t lds3[NSTAGE > 3 ? C::STAGE : 16];
     __shared__ __attribute__((aligned(16))) float col_scale[BN];
     __shared__ __attribute__((aligned(16))) float col_bias[BN];
+    // ODEC: the outlier count and the first kOutCols outlier columns, fetched
+    // at the start so that they have arrived by the epilogue.
+    constexpr int kOutCols = 64;
+    __shared__ int out_cols[ODEC ? kOutCols + 1 : 1];
+    // ODEC, interior tiles with at most kPanel outlier columns (and N % 8 == 0,
+    // for 16-byte aligned weight rows): the tile's
+    // outlier operands are copied HBM -> LDS by DMA during the main loop:
+    // the weight panel [kPanel x BN] fp16 (row p = W16t[O_p, n0 .. n0 + BN)) and
+    // the activation panel [BM x kPanel] fp16 (row m = XO[m0 + m, 0 .. kPanel)).
+    // kPanel = 32 columns (16 for the 128x128 tile, whose two workgroups per CU
+    // leave less LDS).
+    constexpr int kPanel = BM * BN <= 128 * 128 ? 16 : 32;
+    __shared__ __attribute__((aligned(1024))) _Float16 panel_w[ODEC ? kPanel * BN : 8];
+    __shared__ __attribute__((aligned(1024))) _Float16 panel_x[ODEC ? BM * kPanel : 8];
 
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -169,6 +183,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
         const int n = min(n0 + tid, N - 1);
         col_scale[tid] = sw[n / G];
         col_bias[tid] = bias ? bias[n] : 0.0f;
+    }
+    if constexpr (ODEC) {
+        if (tid <= kOutCols && tid <= K)  // cols holds K + 1 entries
+            out_cols[tid] = dec.cols[tid];
     }
     float sxm[C::FM];
 #pragma unroll
@@ -287,6 +305,41 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
     // slab hands over: wait for slab kt+1, barrier (after which this slab's
     // buffer is free), refill it with slab kt+NSTAGE, read slab kt+1's first
     // fragments.
+    // The outlier panels go out with the first slab refill: by then the
+    // outlier list is in LDS (the first barrier has passed).  They are the
+    // youngest DMAs of that moment, so the slab waits that follow cover them
+    // too, and the final drain before the epilogue certainly does.  Lanes past
+    // the outlier count (or past K in the activation rows) fetch the zero block.
+    const int n_out = ODEC ? out_cols[0] : 0;
+    const bool use_panels = ODEC && n_out > 0 && n_out <= kPanel && n0 + BN <= N && (N & 7) == 0;
+    auto issue_panels = [&] {
+        if constexpr (ODEC) {
+            if (!use_panels)
+                return;
+            constexpr int WCH = BN / 8;                     // 16-byte pieces per weight-panel row
+            constexpr int NWD = kPanel * WCH / 64;          // wave-wide DMAs, weight panel
+            constexpr int NXD = BM * (kPanel / 8) / 64;     // wave-wide DMAs, activation panel
+            static_assert((kPanel * WCH) % 64 == 0 && (BM * (kPanel / 8)) % 64 == 0, "whole DMAs");
+            for (int j = wave; j < NWD; j += C::NW) {
+                const int idx = j * 64 + lane;
+                const int p = idx / WCH, c = idx % WCH;
+                const _Float16 *src = p < n_out ? dec.wt + (int64_t)out_cols[1 + p] * N + n0 + 8 * c
+                                                : reinterpret_cast<const _Float16 *>(g_zero16);
+                dma16(reinterpret_cast<const int8_t *>(src),
+                      reinterpret_cast<int8_t *>(panel_w) + j * 1024);
+            }
+            for (int j = wave; j < NXD; j += C::NW) {
+                const int idx = j * 64 + lane;
+                const int ml = idx / (kPanel / 8), c = idx % (kPanel / 8);
+                const _Float16 *src =
+                    8 * c < K ? dec.xo + (int64_t)min(m0 + ml, M - 1) * K + 8 * c
+                              : reinterpret_cast<const _Float16 *>(g_zero16);
+                dma16(reinterpret_cast<const int8_t *>(src),
+                      reinterpret_cast<int8_t *>(panel_x) + j * 1024);
+            }
+        }
+    };
+
     auto slab = [&](int kt, auto S) {
         constexpr int s = decltype(S)::value;
 #pragma unroll
@@ -301,6 +354,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                 wait_vmcnt<(NSTAGE - 2) * PER_SLAB>();
                 barrier();
                 issue(kt + NSTAGE, bufs[s]);
+                if constexpr (ODEC) {
+                    if (kt == 0)
+                        issue_panels();
+                }
                 load_frags(bufs[(s + 1) % NSTAGE], 0, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -383,51 +440,106 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                     acc[a][b][r] =
                         __float_as_int((float)acc[a][b][r] * (sxm[b] * col_scale[nl]));
                 }
-        const int P = __builtin_amdgcn_readfirstlane(dec.cols[0]);
-        for (int p0 = 0; p0 < P; p0 += 16) {
-            // Lane (frow, fhalf) holds outlier positions pb .. pb + 7.
-            const int pb = p0 + 8 * fhalf;
-            h8 xo[C::FM], wo[C::FN];
+        const int P = n_out;
+        if (use_panels) {
+            // Operands from the LDS panels (positions >= P are zero in the
+            // weight panel; activation positions >= P are dropped here).
 #pragma unroll
-            for (int b = 0; b < C::FM; b++) {
-                const int m = min(m0 + wm * C::TWM + b * 32 + frow, M - 1);
-                h8 v = {};
-                if (pb < P) {
-                    // pb + 8 <= K (K and pb are multiples of 8, pb < P <= K):
-                    // the load stays inside row m; positions >= P are dropped.
-                    const h8 raw = *reinterpret_cast<const h8 *>(dec.xo + (int64_t)m * K + pb);
+            for (int h = 0; h < kPanel / 16; h++) {
+                if (16 * h >= P)
+                    break;
+                const int pb = 16 * h + 8 * fhalf;
+                h8 xo[C::FM], wo[C::FN];
+#pragma unroll
+                for (int b = 0; b < C::FM; b++) {
+                    const int ml = wm * C::TWM + b * 32 + frow;
+                    const h8 raw = *reinterpret_cast<const h8 *>(panel_x + ml * kPanel + pb);
+                    h8 v;
 #pragma unroll
                     for (int i = 0; i < 8; i++)
                         v[i] = pb + i < P ? raw[i] : (_Float16)0.0f;
+                    xo[b] = v;
                 }
-                xo[b] = v;
+#pragma unroll
+                for (int a = 0; a < C::FN; a++) {
+                    const int nl = wn * C::TWN + a * 32 + frow;
+                    h8 v;
+#pragma unroll
+                    for (int i = 0; i < 8; i++)
+                        v[i] = panel_w[(pb + i) * BN + nl];
+                    wo[a] = v;
+                }
+#pragma unroll
+                for (int a = 0; a < C::FN; a++)
+#pragma unroll
+                    for (int b = 0; b < C::FM; b++) {
+                        v16f c;
+#pragma unroll
+                        for (int r = 0; r < 16; r++)
+                            c[r] = __int_as_float(acc[a][b][r]);
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(wo[a], xo[b], c, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 16; r++)
+                            acc[a][b][r] = __float_as_int(c[r]);
+                    }
             }
-            int oc[8];
+        }
+        // Otherwise straight from global memory, two 16-column chunks per
+        // round: every load of the round is issued before the first MFMA.
+        // Lane (frow, fhalf) holds positions pb .. pb + 7.
+        for (int p0 = 0; !use_panels && p0 < P; p0 += 32) {
+            h8 xo[2][C::FM], wo[2][C::FN];
 #pragma unroll
-            for (int i = 0; i < 8; i++)
-                oc[i] = pb + i < P ? dec.cols[1 + pb + i] : -1;
-#pragma unroll
-            for (int a = 0; a < C::FN; a++) {
-                const int n = min(n0 + wn * C::TWN + a * 32 + frow, N - 1);
-                h8 v;
-#pragma unroll
-                for (int i = 0; i < 8; i++)
-                    v[i] = oc[i] >= 0 ? dec.wt[(int64_t)oc[i] * N + n] : (_Float16)0.0f;
-                wo[a] = v;
-            }
-#pragma unroll
-            for (int a = 0; a < C::FN; a++)
+            for (int h = 0; h < 2; h++) {
+                const int pb = p0 + 16 * h + 8 * fhalf;
 #pragma unroll
                 for (int b = 0; b < C::FM; b++) {
-                    v16f c;
+                    const int m = min(m0 + wm * C::TWM + b * 32 + frow, M - 1);
+                    h8 v = {};
+                    if (pb < P) {
+                        // pb + 8 <= K (K and pb are multiples of 8, pb < P <= K):
+                        // the load stays inside row m; positions >= P are dropped.
+                        const h8 raw = *reinterpret_cast<const h8 *>(dec.xo + (int64_t)m * K + pb);
 #pragma unroll
-                    for (int r = 0; r < 16; r++)
-                        c[r] = __int_as_float(acc[a][b][r]);
-                    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(wo[a], xo[b], c, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 16; r++)
-                        acc[a][b][r] = __float_as_int(c[r]);
+                        for (int i = 0; i < 8; i++)
+                            v[i] = pb + i < P ? raw[i] : (_Float16)0.0f;
+                    }
+                    xo[h][b] = v;
                 }
+                int oc[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const int p = pb + i;
+                    oc[i] = p >= P ? -1 : p < kOutCols ? out_cols[1 + p] : dec.cols[1 + p];
+                }
+#pragma unroll
+                for (int a = 0; a < C::FN; a++) {
+                    const int n = min(n0 + wn * C::TWN + a * 32 + frow, N - 1);
+                    h8 v;
+#pragma unroll
+                    for (int i = 0; i < 8; i++)
+                        v[i] = oc[i] >= 0 ? dec.wt[(int64_t)oc[i] * N + n] : (_Float16)0.0f;
+                    wo[h][a] = v;
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                if (p0 + 16 * h >= P)
+                    break;
+#pragma unroll
+                for (int a = 0; a < C::FN; a++)
+#pragma unroll
+                    for (int b = 0; b < C::FM; b++) {
+                        v16f c;
+#pragma unroll
+                        for (int r = 0; r < 16; r++)
+                            c[r] = __int_as_float(acc[a][b][r]);
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(wo[h][a], xo[h][b], c, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 16; r++)
+                            acc[a][b][r] = __float_as_int(c[r]);
+                    }
+            }
         }
     }
     // With row_amax, the tile also folds max |fp16 output| of each of its rows
@@ -611,8 +723,10 @@ hipError_t launch_gemm_tiled_decomp(const int8_t *Xq, const float *x_scales, con
 #define ZQ_CFGD(BM, BN, WM, WN, BK, NS)                                                          \
     launch_cfg<BM, BN, WM, WN, BK, NS, false, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, \
                                                     N, K, Y, false, stream, nullptr, &dec)
+    // The 256x256 tile's slabs leave no LDS for the outlier panels: its
+    // problems take 256x192.
     switch (pick_tile(M, N)) {
-    case 6: return ZQ_CFGD(256, 256, 2, 4, 128, 2);
+    case 6:
     case 7: return ZQ_CFGD(256, 192, 4, 2, 128, 2);
     default: return ZQ_CFGD(128, 128, 2, 2, 64, 4);
     }

@@ -140,6 +140,8 @@ GEMM_CASES = [
     (77, 1000, 256, 1, ref.ACT_NONE, False, 0.0, 1.0, ALPHA, 13),       # P = 0
     (96, 128, 256, 1, ref.ACT_GELU, True, 0.02, 40.0, -1.0, 14),        # P = K
     (1024, 1536, 1024, 1, ref.ACT_NONE, True, 0.01, 60.0, ALPHA, 15),   # the large tiles
+    # 256x192 tiles with P = 20 (operands staged in LDS) and a ragged last N tile
+    (4096, 2848, 256, 1, ref.ACT_GELU, True, 0.08, 40.0, ALPHA, 16),
 ]
 
 
