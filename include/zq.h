@@ -7,7 +7,8 @@
  *         Quantization for Large-Scale Transformers" (reading notes): group-wise
  *         weight quantization; token-wise activation quantization; the
  *         kernel-fusion flowcharts ("LN/GeLU + Quantize" then "GeMM + DeQuantize").
- *   [T36] "探秘Transformer系列之（36）--- 大模型量化方案": 1.1.2 absmax quantization
+ *   [T36] "探秘Transformer系列之（36）--- 大模型量化方案": 1.1 LLM.int8() mixed-precision
+ *         decomposition (outlier columns in FP16); 1.1.2 absmax quantization
  *         and vector-wise (outer-product) denormalisation; 1.2.2 token-wise
  *         activation quantization fused with the preceding LayerNorm, INT32
  *         accumulation scaled by both scales before the FP16 write, group-wise

@@ -12,6 +12,7 @@
  *          group-wise weight quantization; token-wise activation quantization;
  *          the kernel-fusion flowcharts (LN/GeLU + Quantize, GeMM + DeQuantize).
  *   [T36]  "探秘Transformer系列之（36）--- 大模型量化方案":
+ *          1.1 LLM.int8() "方案" and "混合精度分解" (outlier columns in FP16),
  *          1.1.2 "8位数据类型和量化" (absmax quantization to [-127,127]),
  *          1.1.2 "逐向量量化" (outer-product denormalisation of an int GEMM),
  *          1.2.2 "用于激活的按token量化" (dynamic per-token scales; scaling the
