@@ -30,44 +30,67 @@ __global__ __launch_bounds__(256) void k_fill_i32(int32_t *__restrict__ p, int64
 }
 
 constexpr int kCompactThreads = 1024;
+constexpr int kColsPerThread = 32;
 
-// One workgroup.  Thread t owns columns [t * per, (t + 1) * per): it counts
-// its marks, an exclusive scan over the threads (in LDS) gives its first
-// position, and it rewrites its own columns.  No column is read by one
-// thread and written by another, so the rewrite needs no further barrier.
+// One workgroup, in batches of kCompactThreads * kColsPerThread columns.
+// Thread t owns the 32 consecutive columns at batch + 32 t: it reads their
+// marks with eight 16-byte loads issued together, counts them, an inclusive
+// scan over the threads (in LDS) gives its first position, and it rewrites
+// its own columns.  No column is read by one thread and written by another.
 __global__ __launch_bounds__(kCompactThreads) void k_outlier_compact(int32_t *__restrict__ slot,
                                                                      int K,
                                                                      int32_t *__restrict__ cols)
 {
     __shared__ int scan[kCompactThreads];
     const int t = threadIdx.x;
-    const int per = (K + kCompactThreads - 1) / kCompactThreads;
-    const int j0 = min(t * per, K);
-    const int j1 = min(j0 + per, K);
-    int cnt = 0;
-    for (int j = j0; j < j1; j++)
-        cnt += slot[j] != 0;
-    scan[t] = cnt;
-    __syncthreads();
-    // Hillis-Steele inclusive scan.
-    for (int d = 1; d < kCompactThreads; d <<= 1) {
-        const int add = t >= d ? scan[t - d] : 0;
+    int base = 0;
+    for (int b0 = 0; b0 < K; b0 += kCompactThreads * kColsPerThread) {
+        const int j0 = b0 + t * kColsPerThread;
+        int4 v[kColsPerThread / 4];
+        // K % 16 == 0, so each group of four columns is wholly inside or past K.
+#pragma unroll
+        for (int q = 0; q < kColsPerThread / 4; q++)
+            v[q] = j0 + 4 * q < K ? *reinterpret_cast<const int4 *>(slot + j0 + 4 * q)
+                                  : make_int4(0, 0, 0, 0);
+        int cnt = 0;
+#pragma unroll
+        for (int q = 0; q < kColsPerThread / 4; q++)
+            cnt += (v[q].x != 0) + (v[q].y != 0) + (v[q].z != 0) + (v[q].w != 0);
+        scan[t] = cnt;
         __syncthreads();
-        scan[t] += add;
-        __syncthreads();
-    }
-    int p = scan[t] - cnt;
-    for (int j = j0; j < j1; j++) {
-        if (slot[j] != 0) {
-            slot[j] = p;
-            cols[1 + p] = j;
-            p++;
-        } else {
-            slot[j] = -1;
+        // Hillis-Steele inclusive scan.
+        for (int d = 1; d < kCompactThreads; d <<= 1) {
+            const int add = t >= d ? scan[t - d] : 0;
+            __syncthreads();
+            scan[t] += add;
+            __syncthreads();
         }
+        int p = base + scan[t] - cnt;
+        const int batch_total = scan[kCompactThreads - 1];
+#pragma unroll
+        for (int q = 0; q < kColsPerThread / 4; q++) {
+            const int j = j0 + 4 * q;
+            if (j >= K)
+                break;
+            const int in[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+            int out[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                if (in[e] != 0) {
+                    out[e] = p;
+                    cols[1 + p] = j + e;
+                    p++;
+                } else {
+                    out[e] = -1;
+                }
+            }
+            *reinterpret_cast<int4 *>(slot + j) = make_int4(out[0], out[1], out[2], out[3]);
+        }
+        base += batch_total;
+        __syncthreads();  // scan[] is reused by the next batch
     }
-    if (t == kCompactThreads - 1)
-        cols[0] = scan[t];
+    if (t == 0)
+        cols[0] = base;
 }
 
 // W [N x K] (fp32 or fp16) -> W16t [K x N] fp16 (round to nearest even), through

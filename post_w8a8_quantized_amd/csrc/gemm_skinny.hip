@@ -57,11 +57,18 @@ __device__ __forceinline__ void wait_vmcnt()
 // F8: the operands are OCP E4M3 codes and the product is
 // v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales), accumulating in fp32;
 // OUT_I32 then writes the raw fp32 accumulators.
-template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED, bool OUT_I32, bool F8 = false>
+//
+// ODEC (fp16 output): the mixed-precision decomposition's fp16 part joins the
+// epilogue, sum_p XO[m, p] W16t[O_p, n] by fp32 FMAs per output (a handful of
+// outlier columns against a K-long weight stream).  The outlier count and the
+// first kOutCols columns are fetched into LDS at the start, so the epilogue's
+// loads depend on nothing in flight.
+template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED, bool OUT_I32, bool F8 = false,
+          bool ODEC = false>
 __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int act, int M, int N,
-    int K, void *__restrict__ Y, uint32_t *__restrict__ row_amax)
+    int K, void *__restrict__ Y, uint32_t *__restrict__ row_amax, OutlierOperands dec)
 {
     constexpr int WR = 16 * RG;            // weight rows per workgroup
     constexpr int XR = 16 * MT;            // token rows (padded to 16s)
@@ -91,6 +98,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     __shared__ __attribute__((aligned(1024))) int8_t buf6[NS > 6 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) int8_t buf7[NS > 7 ? STAGE : 16];
     int8_t *const bufs[8] = {buf0, buf1, buf2, buf3, buf4, buf5, buf6, buf7};
+    constexpr int kOutCols = 64;
+    __shared__ int out_cols[ODEC ? kOutCols + 1 : 1];
+    if constexpr (ODEC) {
+        if (threadIdx.x <= kOutCols && threadIdx.x <= K)  // cols holds K + 1 entries
+            out_cols[threadIdx.x] = dec.cols[threadIdx.x];
+    }
 
     // Wave index as a scalar: the DMA split, k blocks and row groups below
     // are uniform per wave.
@@ -273,11 +286,38 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
                 *reinterpret_cast<Acc *>(static_cast<int32_t *>(Y) + (int64_t)m * N + nn) = sum;
             } else {
                 const float sxm = sx[m];
+                float outl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (ODEC) {
+                    // Eight outlier positions per step: one 16-byte load of XO
+                    // (p0 + 8 <= K: p0 < P <= K, both multiples of 8), then
+                    // four weights of each column (8 bytes: N % 4 == 0, nn % 4 == 0).
+                    const int P = out_cols[0];
+                    for (int p0 = 0; p0 < P; p0 += 8) {
+                        const h8 xv = *reinterpret_cast<const h8 *>(dec.xo + (int64_t)m * K + p0);
+#pragma unroll
+                        for (int j = 0; j < 8; j++) {
+                            const int p = p0 + j;
+                            if (p < P) {
+                                const int col = p < kOutCols ? out_cols[1 + p] : dec.cols[1 + p];
+                                const h4 wv =
+                                    *reinterpret_cast<const h4 *>(dec.wt + (int64_t)col * N + nn);
+#pragma unroll
+                                for (int i = 0; i < 4; i++)
+                                    outl[i] = fmaf((float)xv[j], (float)wv[i], outl[i]);
+                            }
+                        }
+                    }
+                }
                 h4 o;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     // The tiled kernel's expression, so both give the same bits.
-                    float v = fmaf((float)sum[i], sxm * sw[(nn + i) / G], bias ? bias[nn + i] : 0.0f);
+                    float v;
+                    if constexpr (ODEC)
+                        v = fmaf((float)sum[i], sxm * sw[(nn + i) / G], outl[i]) +
+                            (bias ? bias[nn + i] : 0.0f);
+                    else
+                        v = fmaf((float)sum[i], sxm * sw[(nn + i) / G], bias ? bias[nn + i] : 0.0f);
                     if (act == 1)
                         v = gelu_fast(v);
                     o[i] = (_Float16)v;
@@ -294,19 +334,28 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     }
 }
 
-template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED = false, bool F8 = false>
+template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED = false, bool F8 = false,
+          bool ODEC = false>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
-                      void *Y, bool out_i32, hipStream_t stream, uint32_t *row_amax = nullptr)
+                      void *Y, bool out_i32, hipStream_t stream, uint32_t *row_amax = nullptr,
+                      const OutlierOperands *dec = nullptr)
 {
     const dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)));
     const dim3 block(kThreads);
-    if (out_i32)
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, true, F8>), grid, block, 0, stream, Xq,
-                           sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y, row_amax);
+    const OutlierOperands od = dec ? *dec : OutlierOperands{nullptr, nullptr, nullptr};
+    if constexpr (ODEC)
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, false, F8, true>), grid,
+                           block, 0, stream, Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N,
+                           (int)K, Y, row_amax, od);
+    else if (out_i32)
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, true, F8>), grid, block, 0,
+                           stream, Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y,
+                           row_amax, od);
     else
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, false, F8>), grid, block, 0, stream,
-                           Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y, row_amax);
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, false, F8>), grid, block, 0,
+                           stream, Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y,
+                           row_amax, od);
     return hipGetLastError();
 }
 
@@ -404,6 +453,20 @@ hipError_t launch_gemm_skinny_fp8(const int8_t *Xq, const float *x_scales, const
         return M <= 16 ? ZQ_SK8(1, true) : ZQ_SK8(2, true);
     return M <= 16 ? ZQ_SK8(1, false) : ZQ_SK8(2, false);
 #undef ZQ_SK8
+}
+
+hipError_t launch_gemm_skinny_decomp(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                     const float *w_scales, int64_t G, const float *bias, int act,
+                                     int64_t M, int64_t N, int64_t K, const int32_t *cols,
+                                     const _Float16 *XO, const _Float16 *W16t, void *Y,
+                                     hipStream_t stream)
+{
+    const OutlierOperands dec{cols, XO, W16t};
+    if (M <= 16)
+        return launch_cfg<1, 2, 512, 4, true, false, false, true>(
+            Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y, false, stream, nullptr, &dec);
+    return launch_cfg<2, 2, 512, 4, true, false, false, true>(
+        Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y, false, stream, nullptr, &dec);
 }
 
 int64_t packed_weights_bytes(int64_t N, int64_t K)

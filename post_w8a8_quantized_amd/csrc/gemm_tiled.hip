@@ -69,15 +69,6 @@ __device__ __forceinline__ void dma16(const int8_t *src, int8_t *lds_base)
                                      (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
-// The outlier part of the mixed-precision decomposition: cols[0] = P, cols[1 + p]
-// = the p-th outlier column; xo [M x K] fp16 holds token m's value of column
-// cols[1 + p] at xo[m * K + p]; wt [K x N] fp16 is W transposed.
-struct OutlierOperands {
-    const int32_t *cols;
-    const _Float16 *xo;
-    const _Float16 *wt;
-};
-
 template <int BM, int BN, int WM, int WN, int BK, int NSTAGE>
 struct Cfg {
     static constexpr int NW = WM * WN;                // waves per workgroup

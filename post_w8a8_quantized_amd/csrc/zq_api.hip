@@ -611,6 +611,22 @@ ZQ_API zq_status zq_smoothquant_factors(const void *X, zq_dtype x_dtype, int64_t
 
 // ---- Mixed-precision decomposition (outlier columns in fp16) ----
 
+namespace {
+// Few tokens: the weight-streaming kernel; otherwise the tiled one.
+zq_status gemm_decomp_dispatch(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                               const float *w_scales, int64_t G, const float *bias, zq_act act,
+                               int64_t M, int64_t N, int64_t K, const int32_t *cols,
+                               const _Float16 *XO, const _Float16 *W16t, void *Y,
+                               hipStream_t stream)
+{
+    if (M <= kSkinnyMaxM)
+        return map_hip(zq::launch_gemm_skinny_decomp(Xq, x_scales, Wq, w_scales, G, bias, (int)act,
+                                                     M, N, K, cols, XO, W16t, Y, stream));
+    return map_hip(zq::launch_gemm_tiled_decomp(Xq, x_scales, Wq, w_scales, G, bias, (int)act, M,
+                                                N, K, cols, XO, W16t, Y, stream));
+}
+}  // namespace
+
 ZQ_API zq_status zq_pack_outlier_weights(const void *W, zq_dtype w_dtype, int64_t N, int64_t K,
                                          void *W16t, hipStream_t stream)
 {
@@ -682,9 +698,9 @@ ZQ_API zq_status zq_w8a8_gemm_decomp(const int8_t *Xq, const float *x_scales, co
     if (!aligned16(XO) || !aligned16(W16t))
         return ZQ_ERR_ALIGN;
     clear_stale_error();
-    return map_hip(zq::launch_gemm_tiled_decomp(
-        Xq, x_scales, Wq, w_scales, group_rows, bias, (int)act, M, N, K, cols,
-        static_cast<const _Float16 *>(XO), static_cast<const _Float16 *>(W16t), Y, stream));
+    return gemm_decomp_dispatch(Xq, x_scales, Wq, w_scales, group_rows, bias, act, M, N, K, cols,
+                                static_cast<const _Float16 *>(XO),
+                                static_cast<const _Float16 *>(W16t), Y, stream);
 }
 
 // Workspace of zq_linear_w8a8_decomp: slot int32 [K] | cols int32 [K + 1] |
@@ -747,7 +763,6 @@ ZQ_API zq_status zq_linear_w8a8_decomp(const void *X, zq_dtype x_dtype, zq_pre p
                                             Xq, x_scales, XO, stream));
     if (st != ZQ_OK)
         return st;
-    return map_hip(zq::launch_gemm_tiled_decomp(Xq, x_scales, Wq, w_scales, group_rows, bias,
-                                                (int)act, M, N, K, cols, XO,
-                                                static_cast<const _Float16 *>(W16t), Y, stream));
+    return gemm_decomp_dispatch(Xq, x_scales, Wq, w_scales, group_rows, bias, act, M, N, K, cols,
+                                XO, static_cast<const _Float16 *>(W16t), Y, stream);
 }

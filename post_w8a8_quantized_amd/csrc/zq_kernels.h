@@ -8,6 +8,16 @@
 
 namespace zq {
 
+// The fp16 part of the mixed-precision decomposition, as the GEMM epilogues
+// read it: cols[0] = P, cols[1 + p] = the p-th outlier column; xo [M x K]
+// fp16 holds token m's value of column cols[1 + p] at xo[m * K + p]; wt
+// [K x N] fp16 is W transposed.
+struct OutlierOperands {
+    const int32_t *cols;
+    const _Float16 *xo;
+    const _Float16 *wt;
+};
+
 // Prologue: LN / GeLU / none in fp32, then per-token absmax quantization
 // (int8 codes, or with fp8 OCP E4M3 codes and power-of-two scales).
 // zero_rows (optional, M entries) is cleared on the way (a per-token absmax
@@ -81,6 +91,13 @@ hipError_t launch_ln_quant_decomp(const void *X, bool x_f16, int64_t M, int64_t 
                                   const float *gamma, const float *beta, float eps,
                                   const int32_t *slot, int8_t *Xq, float *x_scales, _Float16 *XO,
                                   hipStream_t stream);
+// Weight-streaming GEMM (M <= 32, row-major weights) whose epilogue adds the
+// fp16 outlier product (fp16 output).
+hipError_t launch_gemm_skinny_decomp(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
+                                     const float *w_scales, int64_t G, const float *bias, int act,
+                                     int64_t M, int64_t N, int64_t K, const int32_t *cols,
+                                     const _Float16 *XO, const _Float16 *W16t, void *Y,
+                                     hipStream_t stream);
 // Tiled GEMM whose epilogue adds the fp16 outlier product (fp16 output).
 hipError_t launch_gemm_tiled_decomp(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                                     const float *w_scales, int64_t G, const float *bias, int act,

@@ -142,6 +142,10 @@ GEMM_CASES = [
     (1024, 1536, 1024, 1, ref.ACT_NONE, True, 0.01, 60.0, ALPHA, 15),   # the large tiles
     # 256x192 tiles with P = 20 (operands staged in LDS) and a ragged last N tile
     (4096, 2848, 256, 1, ref.ACT_GELU, True, 0.08, 40.0, ALPHA, 16),
+    # few tokens: the weight-streaming kernel, ragged last workgroup, P ~ 20
+    (16, 1000, 2048, 1, ref.ACT_NONE, True, 0.01, 60.0, ALPHA, 17),
+    # M = 32 with more than 64 outlier columns (list read from global memory)
+    (32, 512, 4096, 8, ref.ACT_GELU, True, 0.02, 60.0, ALPHA, 18),
 ]
 
 
@@ -226,3 +230,24 @@ def test_linear_decomp_outlier_workload_full_size(zq):
     got = zq.linear_w8a8_decomp(Xd, Wq, s_w, G, Wt, ALPHA, w.pre, dev(inp.gamma), dev(inp.beta),
                                 w.eps)
     assert_y(host(got)[rows], want)
+
+
+def test_linear_decomp_decode_size(zq):
+    """The decode shape (X fp16 [16 x 28672] through the GeLU prologue, W
+    [8192 x 28672], G = 128) with 0.1% of the channels x10: the
+    weight-streaming kernel with the fp16 part, all 16 tokens against the oracle."""
+    w = workload(16, 28672, 8192, 128, "f16", ref.PRE_GELU, ref.ACT_NONE, False, 0.001, 10.0, 19)
+    say("decomp decode size", w.M, w.K, w.N)
+    inp = make_inputs(w)
+    check_not_borderline(ref.preop(inp.X, w.pre), ALPHA)
+    Wq_r, s_w_r = ref.quantize_groups(inp.W, w.group_rows)
+    want, q_ref, s_ref, cols = ref.linear_decomp(inp.X, w.pre, None, None, 1e-5, ALPHA, Wq_r,
+                                                 s_w_r, w.group_rows, inp.W, None, w.act)
+    assert cols.size > 0
+    Wd = dev(inp.W)
+    Wq, s_w = zq.quantize_weights_grouped(Wd, w.group_rows)
+    assert np.array_equal(host(Wq), Wq_r) and np.array_equal(host(s_w), s_w_r)
+    Wt = zq.pack_outlier_weights(Wd)
+    del Wd
+    got = zq.linear_w8a8_decomp(dev(inp.X), Wq, s_w, w.group_rows, Wt, ALPHA, w.pre)
+    assert_y(host(got), want)

@@ -55,3 +55,53 @@ def test_graph_replays_match_eager(M):
         got = Y.cpu().numpy().view(np.uint16)
         assert np.array_equal(got, eager), f"replay {r} differs"
         del junk
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_graph_replays_match_eager_decomposition(M):
+    """The decomposed layer (outlier search, prologue, GEMM with the fp16 part)
+    under capture: its workspace starts from different garbage on every replay
+    (the search clears its own marks with a kernel, not a memset)."""
+    import post_w8a8_quantized_amd as zq
+    say("graph replay decomposition", M)
+    rng = np.random.default_rng(M + 1)
+    K, N, G = 768, 512, 1
+    Xh = rng.standard_normal((M, K)).astype(np.float32)
+    Xh[:, [5, 300, 301, 700]] *= 40.0
+    X = torch.from_numpy(Xh.astype(np.float16)).cuda()
+    W = torch.from_numpy((0.02 * rng.standard_normal((N, K))).astype(np.float32)).cuda()
+    Wq, s_w = zq.quantize_weights_grouped(W, G)
+    Wt = zq.pack_outlier_weights(W)
+    bias = torch.from_numpy((0.01 * rng.standard_normal(N)).astype(np.float32)).cuda()
+    ws = torch.empty(zq.linear_decomp_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+
+    def call():
+        zq.linear_w8a8_decomp(X, Wq, s_w, G, Wt, 6.0, zq.PRE_LAYERNORM, None, None, 1e-5, bias,
+                              zq.ACT_GELU, workspace=ws, out=Y)
+
+    call()
+    torch.cuda.synchronize()
+    eager = Y.cpu().numpy().view(np.uint16).copy()
+    P = int(ws[(K * 4 + 255) // 256 * 256:][:4].view(torch.int32).item())
+    assert P >= 4
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(4):
+        Y.fill_(0)
+        ws.fill_(255 if r % 2 else 1)
+        junk = torch.randn(1 << 20, device="cuda").sum()   # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = Y.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, eager), f"replay {r} differs"
+        del junk
