@@ -588,14 +588,18 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                 if (CHECK && m >= M)
                     continue;
                 _Float16 *dst = Yh + (int64_t)m * N + n;
+                // Non-temporal stores: nothing in this kernel reads Y again, and
+                // the whole tile's output leaves at once at the end of the
+                // tile (measured: BERT FFN-up GEMM 25.1 -> 22.3 us, GPT QKV
+                // 128.8 -> 122.7 us, outlier 308 -> 296 us).
                 if (rows16 && (!CHECK || n + 8 <= N)) {
-                    *reinterpret_cast<h8 *>(dst) = v;
+                    __builtin_nontemporal_store(v, reinterpret_cast<h8 *>(dst));
                 } else {
                     // N is a multiple of 4: each half is wholly inside or outside Y.
                     if (!CHECK || n < N)
-                        *reinterpret_cast<h4 *>(dst) = v.lo;
+                        __builtin_nontemporal_store(v.lo, reinterpret_cast<h4 *>(dst));
                     if (!CHECK || n + 4 < N)
-                        *reinterpret_cast<h4 *>(dst + 4) = v.hi;
+                        __builtin_nontemporal_store(v.hi, reinterpret_cast<h4 *>(dst + 4));
                 }
             }
         }

@@ -27,11 +27,19 @@ namespace {
 template <typename T>
 struct Chunk;
 
+// load_nt: the same with the non-temporal hint, for data read exactly once.
 template <>
 struct Chunk<_Float16> {
     static __device__ __forceinline__ void load(const _Float16 *p, float (&v)[8])
     {
         const h8 h = *reinterpret_cast<const h8 *>(p);
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            v[i] = (float)h[i];
+    }
+    static __device__ __forceinline__ void load_nt(const _Float16 *p, float (&v)[8])
+    {
+        const h8 h = __builtin_nontemporal_load(reinterpret_cast<const h8 *>(p));
 #pragma unroll
         for (int i = 0; i < 8; i++)
             v[i] = (float)h[i];
@@ -46,6 +54,13 @@ struct Chunk<float> {
         const float4 b = *reinterpret_cast<const float4 *>(p + 4);
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    static __device__ __forceinline__ void load_nt(const float *p, float (&v)[8])
+    {
+        const v4f a = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p));
+        const v4f b = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p + 4));
+        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+        v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
     }
 };
 
@@ -140,13 +155,19 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
         return v;
     };
 
+    // The row is read once, with the non-temporal hint (measured: 4096x768 7.15 ->
+    // 6.53 us, 2048x4096 12.0 -> 11.0 us), except by the outlier-marking pass,
+    // whose X the decomposition's second pass reads again right after.
     float y[NCH][8];
     const T *xrow = X + m * (int64_t)K;
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
         const int c = t + TT * i;
         if (live && c < nchunks) {
-            Chunk<T>::load(xrow + (int64_t)c * 8, y[i]);
+            if constexpr (DEC == 1)
+                Chunk<T>::load(xrow + (int64_t)c * 8, y[i]);
+            else
+                Chunk<T>::load_nt(xrow + (int64_t)c * 8, y[i]);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; e++)
