@@ -341,6 +341,11 @@ def main():
     time_graph(torch, g_warm)
     ms_ev, ms_wall = time_graph(torch, g_steps)
     ms_step = ms_ev / args.steps
+    # Spread: further replays of the same K-step graph (outside the timed region).
+    reps = np.array([ms_step] + [time_graph(torch, g_steps)[0] / args.steps for _ in range(9)])
+    p10, p50, p90 = np.percentile(reps * 1e3, [10, 50, 90])
+    spread = {"replays": int(reps.size), "p10_us": round(float(p10), 3),
+              "p50_us": round(float(p50), 3), "p90_us": round(float(p90), 3)}
 
     # ---- per-kernel averages over graphs of the same launches (HIP events)
     g_pro = graph_of(torch, prologue, args.steps)
@@ -526,7 +531,8 @@ def main():
         "breakdown_us": {"layer_step": round(ms_step * 1e3, 3), "prologue": round(pro_ms * 1e3, 3),
                          "gemm": round(gemm_ms * 1e3, 3),
                          "prologue_GBps": round(bytes_pro / (pro_ms * 1e-3) / 1e9, 1),
-                         "timed_region_wall_ms": round(ms_wall, 3)},
+                         "timed_region_wall_ms": round(ms_wall, 3),
+                         "layer_step_spread": spread},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ablation": ablation,
