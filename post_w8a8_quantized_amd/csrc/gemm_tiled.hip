@@ -204,6 +204,15 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
         src_w[j] = Wq + (int64_t)min(n0 + row, N - 1) * K + 16 * c;
         kc_w[j] = 16 * c;
     }
+    // One DMA of a slab: j < LX are the X rows, the rest the W rows.
+    auto issue_one = [&](int slab, int8_t *bx, int j) {
+        const int k0 = slab * BK;
+        if (j < C::LX)
+            dma16(k0 + kc_x[j] < K ? src_x[j] + k0 : g_zero16, bx + (wave + C::NW * j) * 1024);
+        else
+            dma16(k0 + kc_w[j - C::LX] < K ? src_w[j - C::LX] + k0 : g_zero16,
+                  bx + BM * BK + (wave + C::NW * (j - C::LX)) * 1024);
+    };
     // Lanes whose 16-byte chunk lies past K fetch zeros instead (branch-free select).
     auto issue = [&](int slab, int8_t *bx) {
         const int k0 = slab * BK;
@@ -344,24 +353,37 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
             } else {
                 wait_vmcnt<(NSTAGE - 2) * PER_SLAB>();
                 barrier();
-                issue(kt + NSTAGE, bufs[s]);
-                if constexpr (ODEC) {
-                    if (kt == 0)
-                        issue_panels();
-                }
                 load_frags(bufs[(s + 1) % NSTAGE], 0, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
+            // In the last k-step the slab's refill DMAs go out one after each
+            // MFMA, so the memory queue drains while the matrix pipe is fed.
 #pragma unroll
             for (int a = 0; a < C::FN; a++)
 #pragma unroll
-                for (int b = 0; b < C::FM; b++)
+                for (int b = 0; b < C::FM; b++) {
                     if constexpr (F8)
                         acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                             fw[ks & 1][a], fx[ks & 1][b], acc[a][b], 0, 0, 0, 127, 0, 127);
                     else
                         acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                             fw[ks & 1][a], fx[ks & 1][b], acc[a][b], 0, 0, 0);
+                    const int i = a * C::FM + b;
+                    if (ks + 1 == KS && i < PER_SLAB) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue_one(kt + NSTAGE, bufs[s], i);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            if (ks + 1 == KS) {
+#pragma unroll
+                for (int j = C::FN * C::FM; j < PER_SLAB; j++)
+                    issue_one(kt + NSTAGE, bufs[s], j);
+                if constexpr (ODEC) {
+                    if (kt == 0)
+                        issue_panels();
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
