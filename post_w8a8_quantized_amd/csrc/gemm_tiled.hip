@@ -273,6 +273,26 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
         }
     };
 
+    // One fragment: idx < FM are the X fragments, the rest the W fragments.
+    auto load_frag_one = [&](const int8_t *stage, int ks, int idx, Frag (&fx)[C::FM],
+                             Frag (&fw)[C::FN]) {
+        const int8_t *row = idx < C::FM ? stage + xbase + idx * 32 * BK
+                                        : stage + wbase + (idx - C::FM) * 32 * BK;
+        Frag f;
+        if constexpr (F8) {
+            const int c0 = 4 * ks + 2 * fhalf;
+            const v4i lo = *reinterpret_cast<const v4i *>(row + ((c0 ^ sw_l) << 4));
+            const v4i hi = *reinterpret_cast<const v4i *>(row + (((c0 + 1) ^ sw_l) << 4));
+            f = Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+            f = *reinterpret_cast<const v4i *>(row + (((2 * ks + fhalf) ^ sw_l) << 4));
+        }
+        if (idx < C::FM)
+            fx[idx] = f;
+        else
+            fw[idx - C::FM] = f;
+    };
+
     int8_t *const bufs[4] = {lds0, lds1, lds2, lds3};
     // The slab count is padded to a multiple of NSTAGE: padding slabs lie past
     // K, every lane of their DMAs fetches the zero block, and their MFMAs add
@@ -340,24 +360,38 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
         }
     };
 
+    // The 256x256 tile with 2x4 waves and 128-byte slabs has no registers to spare
+    // for the spread schedule (it would spill): it issues its refill DMAs and then
+    // its fragment reads in bursts before the MFMAs.
+    constexpr bool kSpread = !(BM == 256 && BN == 256 && WN == 4 && BK == 128);
     auto slab = [&](int kt, auto S) {
         constexpr int s = decltype(S)::value;
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
-            if (ks + 1 < KS) {
-                // The reads feeding this k-step were issued a k-step ago and have
-                // returned; waiting for them here, before the next reads go out,
-                // lets the MFMAs below start without an LDS wait.
+            const bool last = ks + 1 == KS;
+            // Fragments for the next k-step (this slab's, or the next slab's first).
+            const int8_t *nstage = last ? bufs[(s + 1) % NSTAGE] : bufs[s];
+            const int nks = last ? 0 : ks + 1;
+            if (!last) {
+                // The reads feeding this k-step were issued a k-step ago.
                 __builtin_amdgcn_s_waitcnt(0xc07f);
-                load_frags(bufs[s], ks + 1, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
             } else {
                 wait_vmcnt<(NSTAGE - 2) * PER_SLAB>();
                 barrier();
-                load_frags(bufs[(s + 1) % NSTAGE], 0, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
+            }
+            if constexpr (!kSpread) {
+                if (last) {
+                    issue(kt + NSTAGE, bufs[s]);
+                    if constexpr (ODEC) {
+                        if (kt == 0)
+                            issue_panels();
+                    }
+                }
+                load_frags(nstage, nks, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            // In the last k-step the slab's refill DMAs go out one after each
-            // MFMA, so the memory queue drains while the matrix pipe is fed.
+            // Each MFMA is followed by one read of the next k-step's fragments and,
+            // in the last k-step, one refill DMA, so neither queue fills in a burst.
 #pragma unroll
             for (int a = 0; a < C::FN; a++)
 #pragma unroll
@@ -369,13 +403,19 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                         acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                             fw[ks & 1][a], fx[ks & 1][b], acc[a][b], 0, 0, 0);
                     const int i = a * C::FM + b;
-                    if (ks + 1 == KS && i < PER_SLAB) {
-                        __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (kSpread && i < C::FM + C::FN)
+                        load_frag_one(nstage, nks, i, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
+                    if (kSpread && last && i < PER_SLAB)
                         issue_one(kt + NSTAGE, bufs[s], i);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            if (ks + 1 == KS) {
+            if constexpr (kSpread) {
+#pragma unroll
+                for (int i = C::FN * C::FM; i < C::FM + C::FN; i++)
+                    load_frag_one(nstage, nks, i, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
+            }
+            if (kSpread && last) {
 #pragma unroll
                 for (int j = C::FN * C::FM; j < PER_SLAB; j++)
                     issue_one(kt + NSTAGE, bufs[s], j);
