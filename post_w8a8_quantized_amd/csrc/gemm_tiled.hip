@@ -13,11 +13,11 @@
 //  - v_mfma_i32_32x32x32_i8 (32 cycles per SIMD, the full int8 rate; the
 //    16x16x64 form issues at half that rate on gfx950).  W is the A operand
 //    and X the B operand, so each lane's 16 accumulators hold 4 runs of 4
-//    consecutive output columns of one token: the epilogue writes 8-byte
-//    fp16 groups straight from registers.
-//  - Four waves, one per SIMD, each owning a (BM/2) x (BN/2) output block
-//    (128 x 128 at the largest tile): one 16-byte LDS read per lane feeds up
-//    to four MFMAs, 0.5 KB of LDS traffic per MFMA.
+//    consecutive output columns of one token.
+//  - The prefill tiles (256x192 and 256x256) run eight waves, two per SIMD,
+//    each owning a 64x96 (or 128x64) output block: five or six 16-byte LDS
+//    reads per lane feed six or eight MFMAs per k-step.  128x128 tiles with
+//    four waves cover small problems.
 //  - k slabs of BK bytes move HBM -> LDS with global_load_lds_dwordx4 (no
 //    VGPR staging, no ds_write): lane l of a wave-wide load lands at
 //    LDS[base + 16 l], so the bank swizzle is applied by choosing which
@@ -26,13 +26,22 @@
 //  - LDS rows are BK bytes; chunk c of row r sits at position c ^ f(r)
 //    (f = (r/4)%4 for 64-byte rows, (r/2)%8 for 128-byte rows), which keeps
 //    the MFMA operand reads (32 rows, one chunk) free of bank conflicts.
-//  - MFMA fragments are double-buffered: the reads for k-step s+1 are issued
-//    before the MFMAs of k-step s.
+//  - MFMA fragments are double-buffered, and the schedule is spread out: each
+//    MFMA of a k-step is followed by one read of the next k-step's fragments
+//    and, at the slab boundary, by one refill DMA, so neither the LDS nor the
+//    memory queue takes a burst while the matrix pipe waits.
 //  - Per-column weight scales and biases of the tile are staged once in LDS;
-//    per-row activation scales sit in registers.
+//    per-row activation scales sit in registers.  The fp16 epilogue stages
+//    each wave's rows through LDS and writes whole-row 16-byte pieces with
+//    non-temporal stores.
 //  - Workgroup b runs on XCD b % 8.  Tiles are ordered in groups of 8
 //    M-tiles (N next) and each XCD takes a contiguous run, so the ~32 tiles
 //    an XCD runs at once share 8 X panels and 4 W panels in its L2.
+//  - Modes: int32 accumulators out (test mode), the FP8 variant (OCP E4M3
+//    operands on v_mfma_scale_f32_32x32x64_f8f6f4), a per-row |Y| maximum
+//    folded with atomics (for a downstream quantizer), and the
+//    mixed-precision decomposition's fp16 outlier part in the epilogue.
+
 #include "zq_device.h"
 #include "zq_kernels.h"
 

@@ -7,11 +7,14 @@
 // LayerNorm removes a round trip through HBM) and 1.1.2 (absmax to [-127, 127]).
 //
 // The kernel is HBM-bound: per token it reads K * sizeof(x) bytes and writes
-// K + 4.  A token row is read once with 16-byte loads (8 fp16 or 2 x 4 fp32
-// per chunk; consecutive lanes take consecutive chunks), the fused op's
-// result y stays in registers, the reductions (sum, sum of squares about the
-// mean, absmax) run on DPP without touching LDS (and through LDS only across
-// the waves of one token), and codes go out as 8-byte groups.
+// K + 4.  A token row is read once with non-temporal 16-byte loads (8 fp16 or
+// 2 x 4 fp32 per chunk; consecutive lanes take consecutive chunks) by one,
+// four or sixteen waves depending on its length (launch_rows), the fused
+// op's result y stays in registers, the reductions (sum, sum of squares
+// about the mean, absmax) run on DPP without touching LDS (and through LDS
+// only across the waves of one token), and codes go out as 8-byte groups.
+// The same kernel provides the fp16-output op of the unfused order, the FP8
+// codes, and the two passes of the mixed-precision decomposition.
 //
 // A few tokens with long rows (the decode shape) are spread over many
 // workgroups per row instead (see k_rowseg_quant).
