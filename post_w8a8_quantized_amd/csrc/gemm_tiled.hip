@@ -722,12 +722,14 @@ struct Shape {
 //  2: 256x192, 2x2 waves, 64 B x4     3: 128x128, 2x2 waves, 64 B x4
 //  4: 256x128, 2x2 waves, 64 B x4     5: 256x256, 2x4 waves, 64 B x4
 //  6: 256x256, 2x4 waves, 128 B x2    7: 256x192, 4x2 waves, 128 B x2
-constexpr int kNumShapes = 8;
+//  8: 256x256, 4x2 waves, 128 B x2
+constexpr int kNumShapes = 9;
 constexpr Shape kShapes[kNumShapes] = {{256, 256}, {256, 256}, {256, 192}, {128, 128},
-                                       {256, 128}, {256, 256}, {256, 256}, {256, 192}};
+                                       {256, 128}, {256, 256}, {256, 256}, {256, 192},
+                                       {256, 256}};
 
 // Bigger tiles move fewer bytes from L2 per MFMA; the choice trades that
-// against how evenly the tiles fill 256 CUs.  ZQ_GEMM_TILE=0..7 forces one.
+// against how evenly the tiles fill 256 CUs.  ZQ_GEMM_TILE=0..8 forces one.
 int pick_tile(int64_t M, int64_t N)
 {
     static const int forced = [] {
@@ -737,10 +739,13 @@ int pick_tile(int64_t M, int64_t N)
     if (forced >= 0 && forced < kNumShapes)
         return forced;
     const double cus = 256.0;
-    // Measured on MI355X: the two-waves-per-SIMD 256x192 and 256x256 tiles are
-    // the fastest on every prefill shape tried; 128x128 covers small problems.
-    const int cand[3] = {7, 6, 3};
-    const double weight[3] = {1.0, 1.0, 0.7};
+    // Measured on MI355X (spread schedule): 256x192 and 256x256 with 4x2 waves are
+    // the fastest tiles; 256x256 does ~10% more work per unit of time when both
+    // fill their rounds equally (outlier shape 274 vs 284 us), 128x128 ~25% less
+    // (it covers small problems).  Score = weight x the fraction of the rounds'
+    // CU slots that tiles fill.
+    const int cand[3] = {7, 8, 3};
+    const double weight[3] = {1.0, 1.1, 0.7};
     int best = 3;
     double best_score = -1.0;
     for (int i = 0; i < 3; i++) {
@@ -774,6 +779,7 @@ hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8
     case 5: return ZQ_CFG(256, 256, 2, 4, 64, 4);
     case 6: return ZQ_CFG(256, 256, 2, 4, 128, 2);
     case 7: return ZQ_CFG(256, 192, 4, 2, 128, 2);
+    case 8: return ZQ_CFG(256, 256, 4, 2, 128, 2);
     default: return ZQ_CFG(128, 128, 2, 2, 64, 4);
     }
 #undef ZQ_CFG
@@ -789,11 +795,12 @@ hipError_t launch_gemm_tiled_decomp(const int8_t *Xq, const float *x_scales, con
 #define ZQ_CFGD(BM, BN, WM, WN, BK, NS)                                                          \
     launch_cfg<BM, BN, WM, WN, BK, NS, false, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, \
                                                     N, K, Y, false, stream, nullptr, &dec)
-    // The 256x256 tile's slabs leave no LDS for the outlier panels: its
+    // The 256x256 tiles' slabs leave no LDS for the outlier panels: their
     // problems take 256x192.
     switch (pick_tile(M, N)) {
     case 6:
-    case 7: return ZQ_CFGD(256, 192, 4, 2, 128, 2);
+    case 7:
+    case 8: return ZQ_CFGD(256, 192, 4, 2, 128, 2);
     default: return ZQ_CFGD(128, 128, 2, 2, 64, 4);
     }
 #undef ZQ_CFGD
@@ -812,7 +819,7 @@ hipError_t launch_gemm_tiled_fp8(const int8_t *Xq, const float *x_scales, const 
     launch_cfg<BM, BN, WM, WN, 128, 2, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K,   \
                                              Y, out_raw, stream, nullptr)
     const int t = pick_tile(M, N);
-    if (t == 6 || t == 7)
+    if (t == 6 || t == 7 || t == 8)
         return ZQ_CFG8(256, 192, 4, 2);
     return ZQ_CFG8(128, 128, 2, 2);
 #undef ZQ_CFG8

@@ -45,6 +45,7 @@ TILED_SHAPES = [
     (33, 132, 48),       # one partial tile, K < one slab
     (1000, 516, 784),
     (4096, 256, 128),
+    (4096, 8180, 64),    # 256x256 tiles with 4x2 waves, ragged last column tile
 ]
 
 
