@@ -11,7 +11,9 @@
 //    at the decode shape).  Slabs of BKB bytes of those rows (and of the
 //    <= 32 token rows of X) move HBM -> LDS with global_load_lds_dwordx4;
 //    every wave-wide DMA reads 1 KB of ONE row, i.e. fully contiguous,
-//    streaming memory, which is what HBM rewards.  Two slabs are in flight.
+//    streaming memory, which is what HBM rewards.  NS slabs are in flight
+//    (four 512-byte slabs at the shapes used); the weights are read with
+//    the non-temporal policy, since each byte is used once.
 //  - In LDS, 16-byte chunk c of row r sits at slot c ^ (r % 16) (the DMA
 //    lane fetching a slot picks the matching chunk), so the MFMA operand
 //    reads -- 16 rows, one chunk each -- hit 16 different bank groups.
@@ -21,8 +23,6 @@
 //    are added through LDS in a fixed order (deterministic, no atomics).
 #include "zq_device.h"
 #include "zq_kernels.h"
-
-#include <stdlib.h>
 
 #include <algorithm>
 
@@ -63,7 +63,7 @@ __device__ __forceinline__ void wait_vmcnt()
 // outlier columns against a K-long weight stream).  The outlier count and the
 // first kOutCols columns are fetched into LDS at the start, so the epilogue's
 // loads depend on nothing in flight.
-template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED, bool OUT_I32, bool F8 = false,
+template <int MT, int RG, int BKB, int NS, bool PACKED, bool OUT_I32, bool F8 = false,
           bool ODEC = false>
 __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
                 p = slab < ns ? src_w[j] + (int64_t)slab * (WR * BKB) : zero16;
             else
                 p = k0 + kc_w[j] < K ? src_w[j] + k0 : zero16;
-            dma16<NTW ? 2 : 0>(p, buf + 1024 * (wave + 4 * j));
+            dma16<2>(p, buf + 1024 * (wave + 4 * j));  // streamed once: non-temporal
         }
 #pragma unroll
         for (int j = 0; j < LX; j++)
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     }
 }
 
-template <int MT, int RG, int BKB, int NS, bool NTW, bool PACKED = false, bool F8 = false,
+template <int MT, int RG, int BKB, int NS, bool PACKED = false, bool F8 = false,
           bool ODEC = false>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
@@ -345,15 +345,15 @@ hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const
     const dim3 block(kThreads);
     const OutlierOperands od = dec ? *dec : OutlierOperands{nullptr, nullptr, nullptr};
     if constexpr (ODEC)
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, false, F8, true>), grid,
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, PACKED, false, F8, true>), grid,
                            block, 0, stream, Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N,
                            (int)K, Y, row_amax, od);
     else if (out_i32)
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, true, F8>), grid, block, 0,
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, PACKED, true, F8>), grid, block, 0,
                            stream, Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y,
                            row_amax, od);
     else
-        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, NTW, PACKED, false, F8>), grid, block, 0,
+        hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, PACKED, false, F8>), grid, block, 0,
                            stream, Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y,
                            row_amax, od);
     return hipGetLastError();
@@ -382,16 +382,6 @@ __global__ __launch_bounds__(256) void k_pack_weights(const int8_t *__restrict__
     }
 }
 
-// ZQ_SKINNY_CFG=0..8 forces one configuration (measurement aid).
-int skinny_cfg()
-{
-    static const int forced = [] {
-        const char *e = getenv("ZQ_SKINNY_CFG");
-        return e ? atoi(e) : -1;
-    }();
-    return forced;
-}
-
 }  // namespace
 
 hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
@@ -399,33 +389,15 @@ hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int
                               int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
                               hipStream_t stream, uint32_t *row_amax)
 {
-#define ZQ_SK(MT, RG, BKB, NS, NT)                                                               \
-    launch_cfg<MT, RG, BKB, NS, NT>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,        \
-                                    out_i32, stream, row_amax)
-    // 32 weight rows per workgroup (two row groups) fills 256 CUs at N = 8192.
-    // Configurations: slab bytes per row x pipeline depth, nt = weight stream
-    // loaded with the non-temporal policy.
-    const int cfg = skinny_cfg();
-    if (M <= 16) {
-        switch (cfg) {
-        case 0: return ZQ_SK(1, 2, 1024, 2, false);
-        case 1: return ZQ_SK(1, 2, 1024, 3, false);
-        case 2: return ZQ_SK(1, 2, 512, 4, false);
-        case 3: return ZQ_SK(1, 2, 1024, 3, true);
-        case 5: return ZQ_SK(1, 2, 512, 6, true);
-        case 6: return ZQ_SK(1, 2, 256, 8, true);
-        case 7: return ZQ_SK(1, 2, 512, 5, true);
-        case 8: return ZQ_SK(1, 2, 256, 6, true);
-        default: return ZQ_SK(1, 2, 512, 4, true);
-        }
-    }
-    switch (cfg) {
-    case 0: return ZQ_SK(2, 2, 1024, 2, false);
-    case 1: return ZQ_SK(2, 2, 512, 4, false);
-    case 3: return ZQ_SK(2, 2, 1024, 2, true);
-    case 5: return ZQ_SK(2, 2, 256, 8, true);
-    default: return ZQ_SK(2, 2, 512, 4, true);
-    }
+#define ZQ_SK(MT, RG, BKB, NS)                                                                   \
+    launch_cfg<MT, RG, BKB, NS>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y, out_i32,   \
+                                stream, row_amax)
+    // 32 weight rows per workgroup (two row groups) fills 256 CUs at N = 8192;
+    // 512-byte row pieces four slabs deep (measured against 256- and 1024-byte
+    // pieces two to eight deep, and against cached weight loads).
+    if (M <= 16)
+        return ZQ_SK(1, 2, 512, 4);
+    return ZQ_SK(2, 2, 512, 4);
 #undef ZQ_SK
 }
 
@@ -435,9 +407,9 @@ hipError_t launch_gemm_skinny_packed(const int8_t *Xq, const float *x_scales, co
                                      hipStream_t stream)
 {
     if (M <= 16)
-        return launch_cfg<1, 2, kPackBytes, 4, true, true>(Xq, x_scales, Wp, w_scales, G, bias, act,
+        return launch_cfg<1, 2, kPackBytes, 4, true>(Xq, x_scales, Wp, w_scales, G, bias, act,
                                                            M, N, K, Y, out_i32, stream);
-    return launch_cfg<2, 2, kPackBytes, 4, true, true>(Xq, x_scales, Wp, w_scales, G, bias, act, M,
+    return launch_cfg<2, 2, kPackBytes, 4, true>(Xq, x_scales, Wp, w_scales, G, bias, act, M,
                                                        N, K, Y, out_i32, stream);
 }
 
@@ -447,8 +419,8 @@ hipError_t launch_gemm_skinny_fp8(const int8_t *Xq, const float *x_scales, const
                                   bool packed, hipStream_t stream)
 {
 #define ZQ_SK8(MT, P)                                                                             \
-    launch_cfg<MT, 2, kPackBytes, 4, true, P, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M,   \
-                                                     N, K, Y, out_raw, stream)
+    launch_cfg<MT, 2, kPackBytes, 4, P, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, \
+                                               Y, out_raw, stream)
     if (packed)
         return M <= 16 ? ZQ_SK8(1, true) : ZQ_SK8(2, true);
     return M <= 16 ? ZQ_SK8(1, false) : ZQ_SK8(2, false);
@@ -463,9 +435,9 @@ hipError_t launch_gemm_skinny_decomp(const int8_t *Xq, const float *x_scales, co
 {
     const OutlierOperands dec{cols, XO, W16t};
     if (M <= 16)
-        return launch_cfg<1, 2, 512, 4, true, false, false, true>(
+        return launch_cfg<1, 2, 512, 4, false, false, true>(
             Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y, false, stream, nullptr, &dec);
-    return launch_cfg<2, 2, 512, 4, true, false, false, true>(
+    return launch_cfg<2, 2, 512, 4, false, false, true>(
         Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y, false, stream, nullptr, &dec);
 }
 

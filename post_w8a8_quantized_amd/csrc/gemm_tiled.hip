@@ -115,14 +115,9 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     tn = r / gm;
 }
 
-// Waves per SIMD the register budget is planned for: the two-waves-per-SIMD
-// layouts and the small tile (two workgroups per CU) get 256 registers, the
-// large one-wave-per-SIMD tiles 512.
-template <int BM, int BN, int WM, int WN>
-constexpr int waves_per_simd()
-{
-    return (WM * WN == 8 || BM * BN < 256 * 128) ? 2 : 1;
-}
+// Every configuration runs two waves per SIMD (eight-wave workgroups, or two
+// four-wave workgroups of the small tile per CU): 256 registers per wave.
+constexpr int kWavesPerSimd = 2;
 
 // F8: the operands are OCP E4M3 codes and the product is
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) accumulating in fp32;
@@ -137,8 +132,7 @@ constexpr int waves_per_simd()
 template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool OUT_I32, int ACT, bool F8,
           bool ODEC = false>
 __global__ __launch_bounds__(WM *WN * 64)
-__attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
-                                   waves_per_simd<BM, BN, WM, WN>()))) void k_gemm_tiled(
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_tiled(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int M, int N, int K,
     void *__restrict__ Y, int tiles_m, int tiles_n, uint32_t *__restrict__ row_amax,
@@ -369,10 +363,6 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
         }
     };
 
-    // The 256x256 tile with 2x4 waves and 128-byte slabs has no registers to spare
-    // for the spread schedule (it would spill): it issues its refill DMAs and then
-    // its fragment reads in bursts before the MFMAs.
-    constexpr bool kSpread = !(BM == 256 && BN == 256 && WN == 4 && BK == 128);
     auto slab = [&](int kt, auto S) {
         constexpr int s = decltype(S)::value;
 #pragma unroll
@@ -387,16 +377,6 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
             } else {
                 wait_vmcnt<(NSTAGE - 2) * PER_SLAB>();
                 barrier();
-            }
-            if constexpr (!kSpread) {
-                if (last) {
-                    issue(kt + NSTAGE, bufs[s]);
-                    if constexpr (ODEC) {
-                        if (kt == 0)
-                            issue_panels();
-                    }
-                }
-                load_frags(nstage, nks, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
             // Each MFMA is followed by one read of the next k-step's fragments and,
@@ -413,18 +393,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM, BN, WM, WN>(),
                             fw[ks & 1][a], fx[ks & 1][b], acc[a][b], 0, 0, 0);
                     const int i = a * C::FM + b;
                     __builtin_amdgcn_sched_barrier(0);
-                    if (kSpread && i < C::FM + C::FN)
+                    if (i < C::FM + C::FN)
                         load_frag_one(nstage, nks, i, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
-                    if (kSpread && last && i < PER_SLAB)
+                    if (last && i < PER_SLAB)
                         issue_one(kt + NSTAGE, bufs[s], i);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            if constexpr (kSpread) {
 #pragma unroll
-                for (int i = C::FN * C::FM; i < C::FM + C::FN; i++)
-                    load_frag_one(nstage, nks, i, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
-            }
-            if (kSpread && last) {
+            for (int i = C::FN * C::FM; i < C::FM + C::FN; i++)
+                load_frag_one(nstage, nks, i, fx[(ks + 1) & 1], fw[(ks + 1) & 1]);
+            if (last) {
 #pragma unroll
                 for (int j = C::FN * C::FM; j < PER_SLAB; j++)
                     issue_one(kt + NSTAGE, bufs[s], j);
@@ -718,18 +696,14 @@ struct Shape {
     int bm, bn;
 };
 // Tile configurations (waves: WM x WN; slab: BK bytes, NSTAGE deep):
-//  0: 256x256, 2x2 waves, 64 B x4     1: 256x256, 2x2 waves, 128 B x2
-//  2: 256x192, 2x2 waves, 64 B x4     3: 128x128, 2x2 waves, 64 B x4
-//  4: 256x128, 2x2 waves, 64 B x4     5: 256x256, 2x4 waves, 64 B x4
-//  6: 256x256, 2x4 waves, 128 B x2    7: 256x192, 4x2 waves, 128 B x2
-//  8: 256x256, 4x2 waves, 128 B x2
-constexpr int kNumShapes = 9;
-constexpr Shape kShapes[kNumShapes] = {{256, 256}, {256, 256}, {256, 192}, {128, 128},
-                                       {256, 128}, {256, 256}, {256, 256}, {256, 192},
-                                       {256, 256}};
+//  0: 256x192, 4x2 waves, 128 B x2    1: 256x256, 4x2 waves, 128 B x2
+//  2: 128x128, 2x2 waves, 64 B x4
+constexpr int kNumShapes = 3;
+constexpr Shape kShapes[kNumShapes] = {{256, 192}, {256, 256}, {128, 128}};
 
 // Bigger tiles move fewer bytes from L2 per MFMA; the choice trades that
-// against how evenly the tiles fill 256 CUs.  ZQ_GEMM_TILE=0..8 forces one.
+// against how evenly the tiles fill 256 CUs.  ZQ_GEMM_TILE=0..2 forces one
+// (a measurement aid).
 int pick_tile(int64_t M, int64_t N)
 {
     static const int forced = [] {
@@ -739,23 +713,21 @@ int pick_tile(int64_t M, int64_t N)
     if (forced >= 0 && forced < kNumShapes)
         return forced;
     const double cus = 256.0;
-    // Measured on MI355X (spread schedule): 256x192 and 256x256 with 4x2 waves are
-    // the fastest tiles; 256x256 does ~10% more work per unit of time when both
-    // fill their rounds equally (outlier shape 274 vs 284 us), 128x128 ~25% less
-    // (it covers small problems).  Score = weight x the fraction of the rounds'
-    // CU slots that tiles fill.
-    const int cand[3] = {7, 8, 3};
-    const double weight[3] = {1.0, 1.1, 0.7};
-    int best = 3;
+    // Measured on MI355X: 256x256 does ~10% more work per unit of time than
+    // 256x192 when both fill their rounds equally (outlier shape 274 vs 284 us),
+    // 128x128 ~25% less (it covers small problems).  Score = weight x the
+    // fraction of the rounds' CU slots that tiles fill.
+    const double weight[kNumShapes] = {1.0, 1.1, 0.7};
+    int best = 2;
     double best_score = -1.0;
-    for (int i = 0; i < 3; i++) {
-        const Shape s = kShapes[cand[i]];
+    for (int i = 0; i < kNumShapes; i++) {
+        const Shape s = kShapes[i];
         const double tiles = (double)((M + s.bm - 1) / s.bm) * (double)((N + s.bn - 1) / s.bn);
         const double rounds = ceil(tiles / cus);
         const double score = weight[i] * tiles / (rounds * cus);
         if (score > best_score + 1e-9) {
             best_score = score;
-            best = cand[i];
+            best = i;
         }
     }
     return best;
@@ -772,14 +744,8 @@ hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8
     launch_cfg<BM, BN, WM, WN, BK, NS>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,      \
                                        out_i32, stream, row_amax)
     switch (pick_tile(M, N)) {
-    case 0: return ZQ_CFG(256, 256, 2, 2, 64, 4);
-    case 1: return ZQ_CFG(256, 256, 2, 2, 128, 2);
-    case 2: return ZQ_CFG(256, 192, 2, 2, 64, 4);
-    case 4: return ZQ_CFG(256, 128, 2, 2, 64, 4);
-    case 5: return ZQ_CFG(256, 256, 2, 4, 64, 4);
-    case 6: return ZQ_CFG(256, 256, 2, 4, 128, 2);
-    case 7: return ZQ_CFG(256, 192, 4, 2, 128, 2);
-    case 8: return ZQ_CFG(256, 256, 4, 2, 128, 2);
+    case 0: return ZQ_CFG(256, 192, 4, 2, 128, 2);
+    case 1: return ZQ_CFG(256, 256, 4, 2, 128, 2);
     default: return ZQ_CFG(128, 128, 2, 2, 64, 4);
     }
 #undef ZQ_CFG
@@ -797,12 +763,9 @@ hipError_t launch_gemm_tiled_decomp(const int8_t *Xq, const float *x_scales, con
                                                     N, K, Y, false, stream, nullptr, &dec)
     // The 256x256 tiles' slabs leave no LDS for the outlier panels: their
     // problems take 256x192.
-    switch (pick_tile(M, N)) {
-    case 6:
-    case 7:
-    case 8: return ZQ_CFGD(256, 192, 4, 2, 128, 2);
-    default: return ZQ_CFGD(128, 128, 2, 2, 64, 4);
-    }
+    if (pick_tile(M, N) != 2)
+        return ZQ_CFGD(256, 192, 4, 2, 128, 2);
+    return ZQ_CFGD(128, 128, 2, 2, 64, 4);
 #undef ZQ_CFGD
 }
 
@@ -818,8 +781,7 @@ hipError_t launch_gemm_tiled_fp8(const int8_t *Xq, const float *x_scales, const 
 #define ZQ_CFG8(BM, BN, WM, WN)                                                                   \
     launch_cfg<BM, BN, WM, WN, 128, 2, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K,   \
                                              Y, out_raw, stream, nullptr)
-    const int t = pick_tile(M, N);
-    if (t == 6 || t == 7 || t == 8)
+    if (pick_tile(M, N) != 2)
         return ZQ_CFG8(256, 192, 4, 2);
     return ZQ_CFG8(128, 128, 2, 2);
 #undef ZQ_CFG8
