@@ -58,7 +58,7 @@ def parse():
                          "mixed-precision decomposition)")
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip the chained FFN block timing (bert_ffn_up)")
-    ap.add_argument("--cpu-seconds", type=float, default=5.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat full oracle passes until this much wall time has passed")
     ap.add_argument("--calib-copy-mb", type=float, default=0.0,
                     help="only run a plain device copy of this size (counter calibration)")
@@ -514,7 +514,7 @@ def main():
         cpu = {"value": round((bytes_layer / per / 1e9) if decode else (ops / per / 1e12), 4),
                "unit": unit, "cores": cores, "kind": "oracle",
                "sample": f"all {M} tokens of the workload (prologue + int GEMM + epilogue), "
-                         f"{passes} passes, {per:.3f} s each"}
+                         f"{passes} passes, {per:.3f} s each, {el:.1f} s wall on {cores} threads"}
 
     out = {
         "metric": METRIC,
