@@ -58,6 +58,8 @@ def parse():
                          "mixed-precision decomposition)")
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip the chained FFN block timing (bert_ffn_up)")
+    ap.add_argument("--no-copy-reference", action="store_true",
+                    help="skip the 1 GiB device-copy bandwidth reference")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat full oracle passes until this much wall time has passed")
     ap.add_argument("--calib-copy-mb", type=float, default=0.0,
@@ -493,6 +495,27 @@ def main():
     if not args.no_decomp:
         decomp = outlier_leg(torch, zq, WORKLOADS["outlier_smooth"], make_inputs, args, dev)
 
+    # ---- achievable HBM bandwidth for context: a 1 GiB device-to-device copy
+    # (torch's copy kernel; read + write bytes over the HIP-event time of 5 copies)
+    hbm_ref = None
+    if not args.no_copy_reference:
+        torch.cuda.synchronize()
+        nb = 1 << 30
+        ca = torch.ones(nb, dtype=torch.uint8, device=dev)
+        cb = torch.empty_like(ca)
+        cb.copy_(ca)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            cb.copy_(ca)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_copy = e0.elapsed_time(e1) / 5
+        hbm_ref = {"copy_GBps": round(2 * nb / (ms_copy * 1e-3) / 1e9, 1),
+                   "bytes_moved": 2 * nb, "what": "1 GiB device copy (read + write), context only"}
+        del ca, cb
+
     # ---- CPU oracle on the host cores (a reported baseline, not the target)
     cpu = None
     if not args.no_cpu_baseline:
@@ -502,19 +525,33 @@ def main():
         g_h = gamma.cpu().numpy() if w.pre == 1 else None
         b_h = beta.cpu().numpy() if w.pre == 1 else None
         rows = np.arange(M, dtype=np.int64)
-        passes, t0 = 0, time.perf_counter()
-        while True:
-            ref.linear_rows(inp.X, w.pre, g_h, b_h, w.eps, Wq_h, sw_h, G, inp.bias, w.act, rows)
-            passes += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
+
+        def oracle_passes(seconds):
+            passes, t0 = 0, time.perf_counter()
+            while True:
+                ref.linear_rows(inp.X, w.pre, g_h, b_h, w.eps, Wq_h, sw_h, G, inp.bias, w.act,
+                                rows)
+                passes += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    return passes, el
+
+        def rate(per):
+            return round((bytes_layer / per / 1e9) if decode else (ops / per / 1e12), 4)
+
+        cores = ref.max_threads()
+        passes, el = oracle_passes(args.cpu_seconds)
         per = el / passes
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        cpu = {"value": round((bytes_layer / per / 1e9) if decode else (ops / per / 1e12), 4),
-               "unit": unit, "cores": cores, "kind": "oracle",
+        cpu = {"value": rate(per), "unit": unit, "cores": cores, "kind": "oracle",
                "sample": f"all {M} tokens of the workload (prologue + int GEMM + epilogue), "
                          f"{passes} passes, {per:.3f} s each, {el:.1f} s wall on {cores} threads"}
+        if decode:
+            # the few-token shapes also on one core (at least one pass, about 3 s)
+            ref.set_threads(1)
+            passes1, el1 = oracle_passes(3.0)
+            ref.set_threads(cores)
+            cpu["one_thread"] = {"value": rate(el1 / passes1), "unit": unit,
+                                 "sample": f"{passes1} passes, {el1 / passes1:.3f} s each"}
 
     out = {
         "metric": METRIC,
@@ -542,6 +579,7 @@ def main():
                          "layer_step_spread": spread},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "hbm_copy_reference": hbm_ref,
         "ablation": ablation,
         "ffn_block": ffn,
         "fp8_variant": fp8,

@@ -28,6 +28,8 @@ _i = ctypes.c_int
 _f = ctypes.c_float
 
 _SIGS = {
+    "zqref_set_threads": (None, [_i]),
+    "zqref_max_threads": (_i, []),
     "zqref_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
     "zqref_f64_to_f16": (ctypes.c_uint16, [ctypes.c_double]),
     "zqref_preop": (_i, [_p, _i, _i64, _i64, _i, _p, _p, _f, _p]),
@@ -95,6 +97,15 @@ def using_library(path: str):
         yield
     finally:
         _lib = saved
+
+
+def set_threads(n: int) -> None:
+    """Thread count of the oracle's parallel loops (timing only; results do not depend on it)."""
+    lib().zqref_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().zqref_max_threads())
 
 
 def _ptr(a: Optional[np.ndarray]):

@@ -42,6 +42,7 @@
  * scale) are taken in fp32, the precision of the stored scale.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -55,6 +56,18 @@
 #define PRE_GELU 2
 #define ACT_NONE 0
 #define ACT_GELU 1
+
+/* Thread count of the OpenMP loops below (for timing the oracle on one core
+ * or on all of them; results do not depend on it). */
+void zqref_set_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : 1);
+}
+
+int zqref_max_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* ---- IEEE binary16 <-> binary32/64, written from the format definition ---- */
 
