@@ -414,7 +414,10 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(g_ach, 1), "peak": PEAK_INT8_TOPS,
                     "unit": "TOP/s", "frac": round(g_ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
                     "kernel": gemm_kernel, "avg_launch_us": round(gemm_ms * 1e3, 3),
-                    "algorithmic_ops_per_launch": ops}
+                    "algorithmic_ops_per_launch": ops, "algorithmic_bytes_per_launch": bytes_gemm}
+    # counted HBM bytes over the bytes the kernel must move (re-reads, partial lines)
+    roofline["traffic_over_algorithmic"] = (round(traffic / bytes_gemm, 3) if traffic
+                                            else None)
 
     # ---- chained FFN block (BERT FFN-up shape): FFN-up then FFN-down (W2 [K x N] drawn
     # like W), as one zq_ffn_w8a8 call against two zq_linear_w8a8 calls
