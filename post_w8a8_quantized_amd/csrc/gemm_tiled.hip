@@ -585,8 +585,9 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
     // With row_amax, the tile also folds max |fp16 output| of each of its rows
     // into row_amax[m] (float bits; an atomic max after the two lanes that
     // hold a row have combined theirs), for a per-token quantizer downstream.
-    auto epilogue = [&](auto checked) {
+    auto epilogue = [&](auto checked, auto fold_amax) {
         constexpr bool CHECK = decltype(checked)::value;
+        constexpr bool AMAX = decltype(fold_amax)::value;  // row_amax given
 #pragma unroll
         for (int b = 0; b < C::FM; b++) {
             float rmax = 0.0f;
@@ -612,7 +613,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
                             v = gelu_fast(v);
                         o[i] = (_Float16)v;
                     }
-                    if (!CHECK || n0 + nl < N) {
+                    if (AMAX && (!CHECK || n0 + nl < N)) {
 #pragma unroll
                         for (int i = 0; i < 4; i++)
                             rmax = fmaxf(rmax, fabsf((float)o[i]));
@@ -620,7 +621,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
                     *reinterpret_cast<h4 *>(stage_out + frow * RS + 2 * nw) = o;
                 }
             }
-            if (row_amax) {
+            if constexpr (AMAX) {
                 rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
                 const int m = m0 + wm * C::TWM + b * 32 + frow;
                 if (fhalf == 0 && (!CHECK || m < M))
@@ -653,10 +654,18 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
             }
         }
     };
-    if (m0 + BM <= M && n0 + BN <= N)
-        epilogue(std::false_type{});
-    else
-        epilogue(std::true_type{});
+    const bool interior = m0 + BM <= M && n0 + BN <= N;
+    if (row_amax) {
+        if (interior)
+            epilogue(std::false_type{}, std::true_type{});
+        else
+            epilogue(std::true_type{}, std::true_type{});
+    } else {
+        if (interior)
+            epilogue(std::false_type{}, std::false_type{});
+        else
+            epilogue(std::true_type{}, std::false_type{});
+    }
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool F8 = false, bool ODEC = false>
