@@ -40,6 +40,15 @@ MUTANTS = {
     "outlier_weight_transposed": ("zqref_f64_to_f16((double)W[n * K + j])", "zqref_f64_to_f16((double)W[j * N + n])"),
     "outlier_act_unrounded": ("double a = (double)zqref_f16_to_f32(zqref_f64_to_f16((double)Y[m * K + j]));",
                               "double a = (double)Y[m * K + j];"),
+    # FP8 (E4M3) variant
+    "e4m3_truncates": ("double q = nearbyint(ldexp(a, 3 - e));", "double q = floor(ldexp(a, 3 - e));"),
+    "e4m3_subnormals_flushed": ("const double q = nearbyint(ldexp(a, 9));", "const double q = 0.0;"),
+    "e4m3_no_nan_code": ("    if (e == 15 && f == 7)\n        return NAN;", "    (void)0;"),
+    "e4m3_exponent_bias_8": ("ldexp((double)(8 + f), e - 10)", "ldexp((double)(8 + f), e - 11)"),
+    "e4m3_saturates_early": ("if (a >= 448.0)", "if (a >= 240.0)"),
+    "fp8_scale_for_240": ("    while (448.0 * ldexp(1.0, e) < (double)a)\n        e++;\n    while (448.0 * ldexp(1.0, e - 1) >= (double)a)",
+                          "    while (240.0 * ldexp(1.0, e) < (double)a)\n        e++;\n    while (240.0 * ldexp(1.0, e - 1) >= (double)a)"),
+    "fp8_gemm_transposed_w": ("lut[Wq[n * K + k]]", "lut[Wq[k * N + n]]"),
     "smooth_inverted": ("(float)sqrt(a / w)", "(float)sqrt(w / a)"),
     "fold_weight_divides": ("(double)W[n * K + j] * (double)s[j]", "(double)W[n * K + j] / (double)s[j]"),
     "group_absmax_first_row": ("s_w[g] = absmax_quantize(W + g * G * K, G * K, Wq + g * G * K);",
