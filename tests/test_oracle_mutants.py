@@ -40,6 +40,15 @@ MUTANTS = {
     "outlier_weight_transposed": ("zqref_f64_to_f16((double)W[n * K + j])", "zqref_f64_to_f16((double)W[j * N + n])"),
     "outlier_act_unrounded": ("double a = (double)zqref_f16_to_f32(zqref_f64_to_f16((double)Y[m * K + j]));",
                               "double a = (double)Y[m * K + j];"),
+    "ln_mean_not_subtracted": ("Y[row + k] = (float)((load_x(X, x_is_f16, row + k) - mu) * r * g + b);",
+                               "Y[row + k] = (float)(load_x(X, x_is_f16, row + k) * r * g + b);"),
+    "gelu_before_bias": ("(double)acc[m * N + n];\n            if (bias)\n                v += (double)bias[n];\n"
+                         "            if (act == ACT_GELU)\n                v = gelu64(v);",
+                         "(double)acc[m * N + n];\n            if (act == ACT_GELU)\n                v = gelu64(v);\n"
+                         "            if (bias)\n                v += (double)bias[n];"),
+    "gamma_fold_multiplies": ("gamma_out[j] = (float)(g / (double)s[j]);", "gamma_out[j] = (float)(g * (double)s[j]);"),
+    "f16_decode_exponent": ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)"),
+    "f16_decode_subnormal": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     # FP8 (E4M3) variant
     "e4m3_truncates": ("double q = nearbyint(ldexp(a, 3 - e));", "double q = floor(ldexp(a, 3 - e));"),
     "e4m3_subnormals_flushed": ("const double q = nearbyint(ldexp(a, 9));", "const double q = 0.0;"),
