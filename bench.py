@@ -248,7 +248,7 @@ def outlier_leg(torch, zq, w, make_inputs, args, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
 

@@ -59,7 +59,7 @@ typedef enum zq_status {
     ZQ_ERR_DTYPE = 4,       /* a dtype / op enum is not one this argument accepts */
     ZQ_ERR_WORKSPACE = 5,   /* the workspace is NULL or smaller than required */
     ZQ_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
-    ZQ_ERR_UNSUPPORTED = 7  /* a valid request this build does not implement */
+    ZQ_ERR_UNSUPPORTED = 7  /* a valid request the library does not implement */
 } zq_status;
 
 typedef enum zq_dtype {
