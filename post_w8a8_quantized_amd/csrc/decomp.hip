@@ -4,8 +4,9 @@
 // stay in fp16 on both sides, the rest go through the int8 GEMM).
 //
 // The set O is a property of the whole batch, so it is found in its own pass
-// (k_ln_quant with DEC = 1 marks slot[col] = 1) between a clear and a
-// one-workgroup compaction that turns the marks into
+// (k_ln_quant with DEC = 1 marks slot[col] = 1 after a clear; for few tokens
+// without a LayerNorm, k_mark_cols writes every mark, 1 or 0, itself) and a
+// one-workgroup compaction turns the marks into
 //   cols[0] = |O|, cols[1 + p] = the p-th outlier column (ascending),
 //   slot[j] = p for an outlier column j, -1 otherwise.
 // Both arrays are O(K) and stay in L2 for the passes that read them.
@@ -30,64 +31,75 @@ __global__ __launch_bounds__(256) void k_fill_i32(int32_t *__restrict__ p, int64
 }
 
 constexpr int kCompactThreads = 1024;
-constexpr int kColsPerThread = 32;
+constexpr int kTileCols = 4 * kCompactThreads;  // one 16-byte piece of marks per thread
+constexpr int kTilesLoaded = 8;                 // tiles whose marks are loaded together
 
-// One workgroup, in batches of kCompactThreads * kColsPerThread columns.
-// Thread t owns the 32 consecutive columns at batch + 32 t: it reads their
-// marks with eight 16-byte loads issued together, counts them, an inclusive
-// scan over the threads (in LDS) gives its first position, and it rewrites
-// its own columns.  No column is read by one thread and written by another.
+// One workgroup.  The marks go in tiles of 4096 columns: thread t owns
+// columns 4 t .. 4 t + 3 of a tile, so every load and store instruction is one
+// contiguous 1 KB run per wave.  kTilesLoaded tiles are loaded together; then,
+// tile by tile, an inclusive scan of the per-thread counts over the threads
+// (by shuffles within each wave, then over the wave totals in LDS) gives each
+// thread the position of its first outlier column, and it rewrites its own
+// four columns.  No column is read by one thread and written by another.
 __global__ __launch_bounds__(kCompactThreads) void k_outlier_compact(int32_t *__restrict__ slot,
                                                                      int K,
                                                                      int32_t *__restrict__ cols)
 {
-    __shared__ int scan[kCompactThreads];
+    constexpr int kWaves = kCompactThreads / kWave;
+    __shared__ int wsum[kWaves];
     const int t = threadIdx.x;
+    const int lane = t % kWave, wave = t / kWave;
     int base = 0;
-    for (int b0 = 0; b0 < K; b0 += kCompactThreads * kColsPerThread) {
-        const int j0 = b0 + t * kColsPerThread;
-        int4 v[kColsPerThread / 4];
+    for (int t0 = 0; t0 < K; t0 += kTileCols * kTilesLoaded) {
         // K % 16 == 0, so each group of four columns is wholly inside or past K.
+        int4 v[kTilesLoaded];
 #pragma unroll
-        for (int q = 0; q < kColsPerThread / 4; q++)
-            v[q] = j0 + 4 * q < K ? *reinterpret_cast<const int4 *>(slot + j0 + 4 * q)
-                                  : make_int4(0, 0, 0, 0);
-        int cnt = 0;
-#pragma unroll
-        for (int q = 0; q < kColsPerThread / 4; q++)
-            cnt += (v[q].x != 0) + (v[q].y != 0) + (v[q].z != 0) + (v[q].w != 0);
-        scan[t] = cnt;
-        __syncthreads();
-        // Hillis-Steele inclusive scan.
-        for (int d = 1; d < kCompactThreads; d <<= 1) {
-            const int add = t >= d ? scan[t - d] : 0;
-            __syncthreads();
-            scan[t] += add;
-            __syncthreads();
+        for (int i = 0; i < kTilesLoaded; i++) {
+            const int j = t0 + i * kTileCols + 4 * t;
+            v[i] = j < K ? *reinterpret_cast<const int4 *>(slot + j) : make_int4(0, 0, 0, 0);
         }
-        int p = base + scan[t] - cnt;
-        const int batch_total = scan[kCompactThreads - 1];
 #pragma unroll
-        for (int q = 0; q < kColsPerThread / 4; q++) {
-            const int j = j0 + 4 * q;
-            if (j >= K)
+        for (int i = 0; i < kTilesLoaded; i++) {
+            if (t0 + i * kTileCols >= K)  // the same for every thread: no barrier is skipped alone
                 break;
-            const int in[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-            int out[4];
+            const int cnt = (v[i].x != 0) + (v[i].y != 0) + (v[i].z != 0) + (v[i].w != 0);
+            int incl = cnt;
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                if (in[e] != 0) {
-                    out[e] = p;
-                    cols[1 + p] = j + e;
-                    p++;
-                } else {
-                    out[e] = -1;
-                }
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int up = __shfl_up(incl, d);
+                if (lane >= d)
+                    incl += up;
             }
-            *reinterpret_cast<int4 *>(slot + j) = make_int4(out[0], out[1], out[2], out[3]);
+            if (lane == kWave - 1)
+                wsum[wave] = incl;
+            __syncthreads();
+            int before = 0, tile_total = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) {
+                const int x = wsum[w];
+                before += w < wave ? x : 0;
+                tile_total += x;
+            }
+            const int j = t0 + i * kTileCols + 4 * t;
+            if (j < K) {
+                int p = base + before + incl - cnt;
+                const int in[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+                int out[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    if (in[e] != 0) {
+                        out[e] = p;
+                        cols[1 + p] = j + e;
+                        p++;
+                    } else {
+                        out[e] = -1;
+                    }
+                }
+                *reinterpret_cast<int4 *>(slot + j) = make_int4(out[0], out[1], out[2], out[3]);
+            }
+            base += tile_total;
+            __syncthreads();  // wsum[] is reused by the next tile
         }
-        base += batch_total;
-        __syncthreads();  // scan[] is reused by the next batch
     }
     if (t == 0)
         cols[0] = base;
@@ -126,11 +138,14 @@ hipError_t launch_outlier_columns(const void *X, bool x_f16, int64_t M, int64_t 
                                   const float *gamma, const float *beta, float eps, float alpha,
                                   int32_t *slot, int32_t *cols, hipStream_t stream)
 {
-    const int64_t blocks = std::min<int64_t>((K + 255) / 256, 1024);
-    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)blocks), dim3(256), 0, stream, slot, K, 0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
+    hipError_t e;
+    if (!outlier_detect_writes_all(M, K, pre)) {
+        const int64_t blocks = std::min<int64_t>((K + 255) / 256, 1024);
+        hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)blocks), dim3(256), 0, stream, slot, K, 0);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     if (M > 0) {
         e = launch_outlier_detect(X, x_f16, M, K, pre, gamma, beta, eps, alpha, slot, stream);
         if (e != hipSuccess)

@@ -584,6 +584,249 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
         sx[m] = scale;
 }
 
+// ---- The mixed-precision decomposition's two passes for few tokens ----
+//
+// Outlier marks without a LayerNorm (y of an element depends on that element
+// alone): workgroup c decides columns [128 c, 128 c + 128) over every token
+// and writes slot[col] = 1 or 0 for each, so the marks need no clearing first
+// and the erf GeLU of a few long rows is spread over many CUs.  Thread (r, q)
+// takes 8-column chunk q of the workgroup's columns for tokens r, r + 16, ...;
+// the 16 partial masks meet in LDS.  Same test as the one-pass kernel's
+// marking mode: |y| > alpha.
+constexpr int kMarkChunks = 16;  // 8-column chunks per workgroup
+constexpr int kMarkRows = kSegThreads / kMarkChunks;
+
+template <typename T, int PRE>
+__global__ __launch_bounds__(kSegThreads) void k_mark_cols(const T *__restrict__ X, int M, int K,
+                                                           float alpha,
+                                                           int32_t *__restrict__ slot)
+{
+    __shared__ uint32_t part[kSegThreads];
+    const int q = threadIdx.x % kMarkChunks;
+    const int r = threadIdx.x / kMarkChunks;
+    const int c = blockIdx.x * kMarkChunks + q;
+    const int nch = K / 8;
+    uint32_t mask = 0;  // bit e: column 8 c + e
+    if (c < nch) {
+        for (int m = r; m < M; m += kMarkRows) {
+            float v[8];
+            Chunk<T>::load(X + (int64_t)m * K + (int64_t)c * 8, v);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float y = PRE == 2 ? gelu_erf(v[e]) : v[e];
+                if (fabsf(y) > alpha)
+                    mask |= 1u << e;
+            }
+        }
+    }
+    part[threadIdx.x] = mask;
+    __syncthreads();
+    if (r == 0 && c < nch) {
+        uint32_t all = 0;
+#pragma unroll
+        for (int i = 0; i < kMarkRows; i++)
+            all |= part[i * kMarkChunks + q];
+        const int4 lo = make_int4(all & 1, (all >> 1) & 1, (all >> 2) & 1, (all >> 3) & 1);
+        const int4 hi = make_int4((all >> 4) & 1, (all >> 5) & 1, (all >> 6) & 1, (all >> 7) & 1);
+        *reinterpret_cast<int4 *>(slot + (int64_t)c * 8) = lo;
+        *reinterpret_cast<int4 *>(slot + (int64_t)c * 8 + 4) = hi;
+    }
+}
+
+// The INT8 part's prologue for few tokens with long rows, laid out as
+// k_rowseg_quant: workgroup (seg, m) codes chunks [256 seg, 256 seg + 256) of
+// token m, after taking the row statistic over the whole row itself.  The
+// statistic is max |y| over the columns outside O (slot < 0), as in the
+// one-pass kernel's mode 2 (whose zeroed outlier values add nothing to it):
+// for LayerNorm a third pass over y with the mask; otherwise the masked max
+// and min of x (and, for GeLU, the masked L and R of k_rowseg_quant's rule),
+// so GeLU is evaluated on the workgroup's own chunk only.  An empty set
+// outside O gives 0.  Outlier values of the own chunk go to XO[m * K + p] as
+// fp16 and are then coded as 0.
+template <typename T, int PRE>
+__global__ __launch_bounds__(kSegThreads) void k_rowseg_decomp(
+    const T *__restrict__ X, int M, int K, int nseg, const float *__restrict__ gamma,
+    const float *__restrict__ beta, float eps, const int32_t *__restrict__ slot,
+    int8_t *__restrict__ Xq, float *__restrict__ sx, _Float16 *__restrict__ XO)
+{
+    __shared__ float red[kSegThreads / kWave];
+    const int j = blockIdx.x / 8;
+    const int seg = j % nseg;
+    const int64_t m = (int64_t)(j / nseg) * 8 + blockIdx.x % 8;
+    if (m >= M)
+        return;
+    const T *xrow = X + m * (int64_t)K;
+    const int nch = K / 8;
+    const int own = seg * kSegThreads + threadIdx.x;
+    const float inf = __builtin_inff();
+    auto load_slot = [&](int c, int (&sl)[8]) {
+        const int4 s0 = *reinterpret_cast<const int4 *>(slot + (int64_t)c * 8);
+        const int4 s1 = *reinterpret_cast<const int4 *>(slot + (int64_t)c * 8 + 4);
+        sl[0] = s0.x; sl[1] = s0.y; sl[2] = s0.z; sl[3] = s0.w;
+        sl[4] = s1.x; sl[5] = s1.y; sl[6] = s1.z; sl[7] = s1.w;
+    };
+    auto load_affine = [&](int c, float (&g)[8], float (&b)[8]) {
+        if (gamma) {
+            load8(gamma + c * 8, g);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) g[e] = 1.0f;
+        }
+        if (beta) {
+            load8(beta + c * 8, b);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) b[e] = 0.0f;
+        }
+    };
+
+    float mine[8];
+    int osl[8];
+    if (own < nch) {
+        Chunk<T>::load(xrow + (int64_t)own * 8, mine);
+        load_slot(own, osl);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            mine[e] = 0.0f;
+            osl[e] = -1;
+        }
+    }
+
+    float a = 0.0f, mean = 0.0f, rstd = 0.0f;
+    if constexpr (PRE == 1) {
+        float s = 0.0f;
+#pragma unroll 4
+        for (int c = threadIdx.x; c < nch; c += kSegThreads) {
+            float v[8];
+            Chunk<T>::load(xrow + (int64_t)c * 8, v);
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                s += v[e];
+        }
+        mean = block_reduce<false>(s, red) / (float)K;
+        float ss = 0.0f;
+#pragma unroll 4
+        for (int c = threadIdx.x; c < nch; c += kSegThreads) {
+            float v[8];
+            Chunk<T>::load(xrow + (int64_t)c * 8, v);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float d = v[e] - mean;
+                ss += d * d;
+            }
+        }
+        rstd = 1.0f / sqrtf(block_reduce<false>(ss, red) / (float)K + eps);
+        float amax = 0.0f;
+#pragma unroll 2
+        for (int c = threadIdx.x; c < nch; c += kSegThreads) {
+            float v[8], g[8], b[8];
+            int sl[8];
+            Chunk<T>::load(xrow + (int64_t)c * 8, v);
+            load_slot(c, sl);
+            load_affine(c, g, b);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float ga = rstd * g[e];
+                const float y = fmaf(v[e], ga, fmaf(-mean, ga, b[e]));
+                if (sl[e] < 0)
+                    amax = fmaxf(amax, fabsf(y));
+            }
+        }
+        a = block_reduce<true>(amax, red);
+    } else {
+        // Masked max and min of x, kBatch chunks per thread loaded at a time.
+        constexpr int kBatch = 8;
+        float mx = -inf, mn = inf;
+        for (int base = threadIdx.x; base < nch; base += kSegThreads * kBatch) {
+            float v[kBatch][8];
+            int sl[kBatch][8];
+#pragma unroll
+            for (int i = 0; i < kBatch; i++) {
+                const int c = base + kSegThreads * i;
+                if (c < nch) {
+                    Chunk<T>::load(xrow + (int64_t)c * 8, v[i]);
+                    load_slot(c, sl[i]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kBatch; i++) {
+                if (base + kSegThreads * i < nch) {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        mx = fmaxf(mx, sl[i][e] < 0 ? v[i][e] : -inf);
+                        mn = fminf(mn, sl[i][e] < 0 ? v[i][e] : inf);
+                    }
+                }
+            }
+        }
+        const float xmax = block_reduce<true>(mx, red);
+        const float xmin = -block_reduce<true>(-mn, red);
+        if (xmax > -inf) {  // some column outside O
+            if constexpr (PRE == 0) {
+                a = fmaxf(xmax, -xmin);
+            } else {
+                a = fabsf(gelu_erf(xmax));
+                if (!(xmax >= kGeluPosBound)) {
+                    float lo = -inf, hi = inf;
+#pragma unroll 4
+                    for (int c = threadIdx.x; c < nch; c += kSegThreads) {
+                        float v[8];
+                        int sl[8];
+                        Chunk<T>::load(xrow + (int64_t)c * 8, v);
+                        load_slot(c, sl);
+#pragma unroll
+                        for (int e = 0; e < 8; e++) {
+                            lo = fmaxf(lo, sl[e] < 0 && v[e] <= kGeluArgMin ? v[e] : -inf);
+                            hi = fminf(hi, sl[e] < 0 && v[e] > kGeluArgMin ? v[e] : inf);
+                        }
+                    }
+                    const float L = block_reduce<true>(lo, red);
+                    const float R = -block_reduce<true>(-hi, red);
+                    if (L > -inf)
+                        a = fmaxf(a, fabsf(gelu_erf(L)));
+                    if (R < inf)
+                        a = fmaxf(a, fabsf(gelu_erf(R)));
+                }
+            }
+        }
+    }
+
+    const float scale = a / 127.0f;
+    const bool fast = rcp_quant_ok(scale);
+    const float rs = fast ? 1.0f / scale : 0.0f;
+    if (own < nch) {
+        float y[8];
+        if constexpr (PRE == 2) {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                y[e] = gelu_erf(mine[e]);
+        } else if constexpr (PRE == 1) {
+            float g[8], b[8];
+            load_affine(own, g, b);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float ga = rstd * g[e];
+                y[e] = fmaf(mine[e], ga, fmaf(-mean, ga, b[e]));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                y[e] = mine[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            if (osl[e] >= 0) {
+                XO[m * (int64_t)K + osl[e]] = (_Float16)y[e];
+                y[e] = 0.0f;
+            }
+        }
+        *reinterpret_cast<uint2 *>(Xq + m * K + (int64_t)own * 8) = quant8(y, scale, rs, fast);
+    }
+    if (seg == 0 && threadIdx.x == 0)
+        sx[m] = scale;
+}
+
 // MAXN: the most 16-byte pieces per lane this shape is launched with (cases
 // above it are not instantiated; a row needing more is an invalid launch).
 template <typename T, int WPT, int TPB, bool OUT_F16 = false, bool FP8 = false, int DEC = 0,
@@ -702,10 +945,34 @@ hipError_t launch_decomp_typed(const T *X, int64_t M, int64_t K, int pre, const 
 }
 }  // namespace
 
+bool outlier_detect_writes_all(int64_t M, int64_t K, int pre)
+{
+    return M >= 1 && M <= kRowSegMaxM && K >= kRowSegMinK && pre != 1;
+}
+
 hipError_t launch_outlier_detect(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                                  const float *gamma, const float *beta, float eps, float alpha,
                                  int32_t *slot, hipStream_t stream)
 {
+    if (outlier_detect_writes_all(M, K, pre)) {
+        const dim3 grid((unsigned)((K / 8 + kMarkChunks - 1) / kMarkChunks));
+#define ZQ_MARK(T, P)                                                                            \
+    hipLaunchKernelGGL((k_mark_cols<T, P>), grid, dim3(kSegThreads), 0, stream,                   \
+                       static_cast<const T *>(X), (int)M, (int)K, alpha, slot)
+        if (x_f16) {
+            if (pre == 2)
+                ZQ_MARK(_Float16, 2);
+            else
+                ZQ_MARK(_Float16, 0);
+        } else {
+            if (pre == 2)
+                ZQ_MARK(float, 2);
+            else
+                ZQ_MARK(float, 0);
+        }
+#undef ZQ_MARK
+        return hipGetLastError();
+    }
     if (x_f16)
         return launch_decomp_typed<_Float16, 1>(static_cast<const _Float16 *>(X), M, K, pre, gamma,
                                                 beta, eps, alpha, slot, nullptr, nullptr, nullptr,
@@ -719,6 +986,31 @@ hipError_t launch_ln_quant_decomp(const void *X, bool x_f16, int64_t M, int64_t 
                                   const int32_t *slot, int8_t *Xq, float *x_scales, _Float16 *XO,
                                   hipStream_t stream)
 {
+    if (M <= kRowSegMaxM && K >= kRowSegMinK) {
+        const int nseg = (int)((K + kSegElems - 1) / kSegElems);
+        const dim3 grid((unsigned)(8 * ((M + 7) / 8) * nseg));
+#define ZQ_RSD(T, P)                                                                             \
+    hipLaunchKernelGGL((k_rowseg_decomp<T, P>), grid, dim3(kSegThreads), 0, stream,               \
+                       static_cast<const T *>(X), (int)M, (int)K, nseg, gamma, beta, eps, slot,   \
+                       Xq, x_scales, XO)
+        if (x_f16) {
+            if (pre == 1)
+                ZQ_RSD(_Float16, 1);
+            else if (pre == 2)
+                ZQ_RSD(_Float16, 2);
+            else
+                ZQ_RSD(_Float16, 0);
+        } else {
+            if (pre == 1)
+                ZQ_RSD(float, 1);
+            else if (pre == 2)
+                ZQ_RSD(float, 2);
+            else
+                ZQ_RSD(float, 0);
+        }
+#undef ZQ_RSD
+        return hipGetLastError();
+    }
     int32_t *sl = const_cast<int32_t *>(slot);  // read only in this pass
     if (x_f16)
         return launch_decomp_typed<_Float16, 2>(static_cast<const _Float16 *>(X), M, K, pre, gamma,

@@ -81,7 +81,10 @@ hipError_t launch_gemm_skinny_fp8(const int8_t *Xq, const float *x_scales, const
 hipError_t launch_outlier_columns(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                                   const float *gamma, const float *beta, float eps, float alpha,
                                   int32_t *slot, int32_t *cols, hipStream_t stream);
-// The marking pass alone (slot must be cleared first).
+// The marking pass alone.  slot must be cleared first unless
+// outlier_detect_writes_all(M, K, pre), in which case the pass writes every
+// entry (1 or 0) itself.
+bool outlier_detect_writes_all(int64_t M, int64_t K, int pre);
 hipError_t launch_outlier_detect(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                                  const float *gamma, const float *beta, float eps, float alpha,
                                  int32_t *slot, hipStream_t stream);

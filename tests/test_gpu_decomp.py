@@ -75,6 +75,11 @@ PROLOGUE_CASES = [
     (20, 256, ref.PRE_NONE, "f32", 0.03, 8.0, 5),
     (16, 28672, ref.PRE_GELU, "f16", 0.001, 10.0, 6),          # the decode row length
     (129, 2048, ref.PRE_LAYERNORM, "f16", 0.0, 1.0, 7),        # no outlier channel
+    # few tokens with long rows: marks by column segment, INT8 part by row segment
+    (40, 10000, ref.PRE_NONE, "f32", 0.01, 20.0, 9),           # ragged segments, M > 16
+    (64, 4096, ref.PRE_GELU, "f32", 0.005, 10.0, 10),          # largest M, shortest K there
+    (5, 6160, ref.PRE_LAYERNORM, "f32", 0.01, 80.0, 11),
+    (1, 8192, ref.PRE_NONE, "f16", 0.002, 30.0, 12),
 ]
 
 
@@ -111,6 +116,52 @@ def test_outlier_set_extremes(zq, alpha, every):
     assert np.array_equal(ref.outlier_columns(ref.preop(X, ref.PRE_LAYERNORM), alpha), want)
     slot, cols = zq.outlier_columns(dev(X), alpha, ref.PRE_LAYERNORM)
     check_set(host(slot), host(cols), want)
+
+
+@pytest.mark.parametrize("pre", [ref.PRE_GELU, ref.PRE_NONE])
+@pytest.mark.parametrize("alpha,every", [(-1.0, True), (float("nan"), False)])
+def test_few_token_extremes(zq, pre, alpha, every):
+    """Few tokens with long rows: every column an outlier (nothing left for the
+    INT8 part: scale 0, codes 0) and none (the plain prologue's codes)."""
+    say("decomp few-token extremes", pre, alpha)
+    w = workload(16, 8192, 64, 64, "f16", pre, 0, False, 0.002, 10.0, 13)
+    X = make_inputs(w).X
+    Y = ref.preop(X, pre)
+    want = ref.outlier_columns(Y, alpha)
+    assert want.size == (8192 if every else 0)
+    Xd = dev(X)
+    slot, cols = zq.outlier_columns(Xd, alpha, pre)
+    check_set(host(slot), host(cols), want)
+    Xq, s_x, XO = zq.ln_quant_decomp(Xd, slot, pre)
+    q_ref, s_ref = ref.quantize_rows_excluding(Y, want)
+    assert_codes(host(Xq), q_ref)
+    assert_scales(host(s_x), s_ref)
+    if every:
+        assert not host(Xq).any() and not host(s_x).any()
+
+
+def test_few_token_gelu_negative_side(zq):
+    """GeLU rows whose columns outside O are all at most 0.3, so the INT8 part's
+    scale comes from the negative side (the L and R of the rule), while the
+    outlier columns hold large positive values."""
+    say("decomp few-token gelu negative side")
+    rng = np.random.default_rng(14)
+    M, K = 16, 8192
+    X = -np.abs(rng.standard_normal((M, K))).astype(np.float32) * 2.0
+    X[:, rng.choice(K, 12, replace=False)] = 10.0 + rng.random((M, 12)).astype(np.float32)
+    X = X.astype(np.float16)
+    Y = ref.preop(X, ref.PRE_GELU)
+    check_not_borderline(Y, ALPHA)
+    want = ref.outlier_columns(Y, ALPHA)
+    assert want.size == 12
+    Xd = dev(X)
+    slot, cols = zq.outlier_columns(Xd, ALPHA, ref.PRE_GELU)
+    check_set(host(slot), host(cols), want)
+    Xq, s_x, XO = zq.ln_quant_decomp(Xd, slot, ref.PRE_GELU)
+    q_ref, s_ref = ref.quantize_rows_excluding(Y, want)
+    assert_codes(host(Xq), q_ref)
+    assert_scales(host(s_x), s_ref)
+    assert np.all(host(s_x) < 0.2 / 127 + 1e-6)    # the negative side decided every scale
 
 
 @pytest.mark.parametrize("N,K,dt", [(200, 96, np.float32), (64, 5120, np.float16),
