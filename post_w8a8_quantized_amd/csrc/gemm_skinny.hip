@@ -100,10 +100,28 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     int8_t *const bufs[8] = {buf0, buf1, buf2, buf3, buf4, buf5, buf6, buf7};
     constexpr int kOutCols = 64;
     __shared__ int out_cols[ODEC ? kOutCols + 1 : 1];
+    // ODEC with at most kPanelP outlier columns and N % 8 == 0: the epilogue's
+    // operands, the fp16 weights of the outlier columns for this workgroup's
+    // WR output rows (pw[p][n - n0]) and the tokens' outlier values
+    // (px[m][p]), are loaded as one 16-byte piece per thread right after the
+    // first slab DMAs, held in registers through the main loop and stored to
+    // LDS at its final drain, so the epilogue waits for no memory.
+    constexpr int kPanelP = 32;
+    constexpr int kPW = kPanelP * (WR / 8);  // weight-panel pieces
+    constexpr int kPX = XR * (kPanelP / 8);  // activation-panel pieces
+    static_assert(!ODEC || kPW + kPX <= kThreads, "one piece per thread");
+    __shared__ __attribute__((aligned(16))) _Float16 pw[ODEC ? kPanelP * WR : 8];
+    __shared__ __attribute__((aligned(16))) _Float16 px[ODEC ? XR * kPanelP : 8];
+    int n_out = 0, pcol = 0;
     if constexpr (ODEC) {
         if (threadIdx.x <= kOutCols && threadIdx.x <= K)  // cols holds K + 1 entries
             out_cols[threadIdx.x] = dec.cols[threadIdx.x];
+        n_out = dec.cols[0];
+        const int p = threadIdx.x / (WR / 8);
+        if (threadIdx.x < kPW && p < K)
+            pcol = dec.cols[1 + p];
     }
+    const bool use_panel = ODEC && n_out <= kPanelP && (N & 7) == 0;
 
     // Wave index as a scalar: the DMA split, k blocks and row groups below
     // are uniform per wave.
@@ -228,6 +246,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
 #pragma unroll
     for (int j = 0; j < NS - 1; j++)
         issue(j, bufs[j]);
+    h8 piece = {};
+    if constexpr (ODEC) {
+        const int t = threadIdx.x;
+        if (use_panel && t < kPW) {
+            const int p = t / (WR / 8), c = t % (WR / 8);
+            if (p < n_out && n0 + 8 * c + 8 <= N)
+                piece = *reinterpret_cast<const h8 *>(dec.wt + (int64_t)pcol * N + n0 + 8 * c);
+        } else if (use_panel && t < kPW + kPX) {
+            // 8 c < n_out <= K, both multiples of 8 up to K: the piece stays inside row tok.
+            const int i = t - kPW;
+            const int tok = i / (kPanelP / 8), c = i % (kPanelP / 8);
+            if (tok < M && 8 * c < n_out)
+                piece = *reinterpret_cast<const h8 *>(dec.xo + (int64_t)tok * K + 8 * c);
+        }
+    }
     auto step = [&](int s, auto J) {
         constexpr int j = decltype(J)::value;
         wait_vmcnt<(NS - 2) * PER_WAVE>();
@@ -254,6 +287,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     // The last NS - 1 refills lie past K and fill buffers nobody reads; drain
     // them, and let every wave finish its reads, before buf0 is reused.
     wait_vmcnt<0>();
+    if constexpr (ODEC) {
+        const int t = threadIdx.x;
+        if (use_panel && t < kPW)
+            *reinterpret_cast<h8 *>(pw + (t / (WR / 8)) * WR + 8 * (t % (WR / 8))) = piece;
+        else if (use_panel && t < kPW + kPX)
+            *reinterpret_cast<h8 *>(px + ((t - kPW) / (kPanelP / 8)) * kPanelP +
+                                    8 * ((t - kPW) % (kPanelP / 8))) = piece;
+    }
     barrier();
 
     // Partial sums of the four waves go through buf0 (free now).
@@ -292,7 +333,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
                     // (p0 + 8 <= K: p0 < P <= K, both multiples of 8), then
                     // four weights of each column (8 bytes: N % 4 == 0, nn % 4 == 0).
                     const int P = out_cols[0];
-                    for (int p0 = 0; p0 < P; p0 += 8) {
+                    if (use_panel) {
+                        // The same sum, in the same order, from the LDS panels.
+                        const int ml = 16 * t + r16;
+                        const int nl = nn - n0;
+                        for (int p = 0; p < P; p++) {
+                            const float xv = (float)px[ml * kPanelP + p];
+                            const h4 wv = *reinterpret_cast<const h4 *>(pw + p * WR + nl);
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                outl[i] = fmaf(xv, (float)wv[i], outl[i]);
+                        }
+                    }
+                    for (int p0 = 0; !use_panel && p0 < P; p0 += 8) {
                         const h8 xv = *reinterpret_cast<const h8 *>(dec.xo + (int64_t)m * K + p0);
 #pragma unroll
                         for (int j = 0; j < 8; j++) {
