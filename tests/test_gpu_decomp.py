@@ -197,6 +197,9 @@ GEMM_CASES = [
     (16, 1000, 2048, 1, ref.ACT_NONE, True, 0.01, 60.0, ALPHA, 17),
     # M = 32 with more than 64 outlier columns (list read from global memory)
     (32, 512, 4096, 8, ref.ACT_GELU, True, 0.02, 60.0, ALPHA, 18),
+    # few tokens, P <= 32: operands staged in LDS for 32 tokens; N % 8 == 4 reads them directly
+    (32, 1024, 2048, 1, ref.ACT_GELU, True, 0.008, 60.0, ALPHA, 19),
+    (9, 1004, 1024, 4, ref.ACT_NONE, True, 0.01, 60.0, ALPHA, 20),
 ]
 
 
