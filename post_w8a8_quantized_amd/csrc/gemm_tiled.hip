@@ -500,14 +500,26 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
                         v[i] = pb + i < P ? raw[i] : (_Float16)0.0f;
                     xo[b] = v;
                 }
+                // The weight panel is [position][column]; the A operand wants 8
+                // consecutive positions of one column per lane.  ds_read_b64_tr_b16
+                // transposes 4 x 16 blocks: in each 16-lane group, lane j addresses
+                // row j / 4, columns 4 (j % 4) .. + 3 of the block, and lane i
+                // receives column i of the block's 4 rows (layout checked on the
+                // GPU).  Groups 0, 1 take columns 0-15, 16-31 of positions pb0 ..;
+                // groups 2, 3 the same 8 positions further on; two reads per lane
+                // give its 8 positions.
+                const int grp = lane >> 4, gl = lane & 15;
+                const int prow = 16 * h + 8 * (grp >> 1) + (gl >> 2);
+                const int pcolb = 16 * (grp & 1) + 4 * (gl & 3);
 #pragma unroll
                 for (int a = 0; a < C::FN; a++) {
-                    const int nl = wn * C::TWN + a * 32 + frow;
-                    h8 v;
-#pragma unroll
-                    for (int i = 0; i < 8; i++)
-                        v[i] = panel_w[(pb + i) * BN + nl];
-                    wo[a] = v;
+                    const _Float16 *src = panel_w + prow * BN + wn * C::TWN + a * 32 + pcolb;
+                    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(src));
+                    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(src + 4 * BN));
+                    wo[a] = __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4,
+                                                                           5, 6, 7));
                 }
 #pragma unroll
                 for (int a = 0; a < C::FN; a++)
