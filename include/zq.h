@@ -263,15 +263,16 @@ size_t zq_linear_unfused_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * i.e. zq_linear_w8a8 with LayerNorm and the GeLU epilogue, then
  * zq_linear_w8a8 without a pre-op on H ([ZQN] flowchart: LN+Quantize,
  * GeMM+DeQuantize, GeLU, Quantize, GeMM+DeQuantize; [T36] 1.2.2).  The
- * FFN-up GEMM's epilogue also folds max |H[m, :]| of each of its tiles into a
- * per-token buffer (atomic max), so H's per-token quantizer needs no
- * reduction pass; the result equals the two zq_linear_w8a8 calls bit for bit.
+ * FFN-up GEMM's epilogue also writes, for every token, max |H[m, :]| over each
+ * of its column groups (plain stores of partial maxima, no atomics), so H's
+ * quantizer combines a few partials per token instead of reducing H; the
+ * result equals the two zq_linear_w8a8 calls bit for bit.
  *
  *   X [M x K] (ZQ_F16 / ZQ_F32); gamma, beta [K] or NULL; W1q [F x K] int8 with
  *   w1_scales [F / group_rows1] and bias1 [F] or NULL; W2q [K x F] int8 with
  *   w2_scales [K / group_rows2] and bias2 [K] or NULL; Y [M x K] fp16.
  *   workspace  zq_ffn_workspace_bytes(M, K, F) bytes, 256-byte aligned,
- *              overwritten (H, codes and scales of both layers).
+ *              overwritten (H, the partial maxima, codes and scales of both layers).
  * Requires each layer to meet zq_linear_w8a8's rules.
  */
 zq_status zq_ffn_w8a8(const void *X, zq_dtype x_dtype, const float *gamma, const float *beta,

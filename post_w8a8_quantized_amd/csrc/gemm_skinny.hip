@@ -68,7 +68,7 @@ template <int MT, int RG, int BKB, int NS, bool PACKED, bool OUT_I32, bool F8 = 
 __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int act, int M, int N,
-    int K, void *__restrict__ Y, uint32_t *__restrict__ row_amax, OutlierOperands dec)
+    int K, void *__restrict__ Y, float *__restrict__ row_part, OutlierOperands dec)
 {
     constexpr int WR = 16 * RG;            // weight rows per workgroup
     constexpr int XR = 16 * MT;            // token rows (padded to 16s)
@@ -321,67 +321,77 @@ __global__ __launch_bounds__(kThreads) void k_gemm_skinny(
                 sum += part[((w * RG + g) * MT + t) * kWave + lane];
             const int m = 16 * t + r16;
             const int nn = n0 + 16 * g + 4 * kq;
-            if (m >= M || nn >= N)
-                continue;
-            if constexpr (OUT_I32) {
-                *reinterpret_cast<Acc *>(static_cast<int32_t *>(Y) + (int64_t)m * N + nn) = sum;
-            } else {
-                const float sxm = sx[m];
-                float outl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if constexpr (ODEC) {
-                    // Eight outlier positions per step: one 16-byte load of XO
-                    // (p0 + 8 <= K: p0 < P <= K, both multiples of 8), then
-                    // four weights of each column (8 bytes: N % 4 == 0, nn % 4 == 0).
-                    const int P = out_cols[0];
-                    if (use_panel) {
-                        // The same sum, in the same order, from the LDS panels.
-                        const int ml = 16 * t + r16;
-                        const int nl = nn - n0;
-                        for (int p = 0; p < P; p++) {
-                            const float xv = (float)px[ml * kPanelP + p];
-                            const h4 wv = *reinterpret_cast<const h4 *>(pw + p * WR + nl);
-#pragma unroll
-                            for (int i = 0; i < 4; i++)
-                                outl[i] = fmaf(xv, (float)wv[i], outl[i]);
-                        }
-                    }
-                    for (int p0 = 0; !use_panel && p0 < P; p0 += 8) {
-                        const h8 xv = *reinterpret_cast<const h8 *>(dec.xo + (int64_t)m * K + p0);
-#pragma unroll
-                        for (int j = 0; j < 8; j++) {
-                            const int p = p0 + j;
-                            if (p < P) {
-                                const int col = p < kOutCols ? out_cols[1 + p] : dec.cols[1 + p];
-                                const h4 wv =
-                                    *reinterpret_cast<const h4 *>(dec.wt + (int64_t)col * N + nn);
+            float r = 0.0f;  // max |fp16 output| of this lane's four outputs
+            if (m < M && nn < N) {
+                if constexpr (OUT_I32) {
+                    *reinterpret_cast<Acc *>(static_cast<int32_t *>(Y) + (int64_t)m * N + nn) = sum;
+                } else {
+                    const float sxm = sx[m];
+                    float outl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (ODEC) {
+                        // Eight outlier positions per step: one 16-byte load of XO
+                        // (p0 + 8 <= K: p0 < P <= K, both multiples of 8), then
+                        // four weights of each column (8 bytes: N % 4 == 0, nn % 4 == 0).
+                        const int P = out_cols[0];
+                        if (use_panel) {
+                            // The same sum, in the same order, from the LDS panels.
+                            const int ml = 16 * t + r16;
+                            const int nl = nn - n0;
+                            for (int p = 0; p < P; p++) {
+                                const float xv = (float)px[ml * kPanelP + p];
+                                const h4 wv = *reinterpret_cast<const h4 *>(pw + p * WR + nl);
 #pragma unroll
                                 for (int i = 0; i < 4; i++)
-                                    outl[i] = fmaf((float)xv[j], (float)wv[i], outl[i]);
+                                    outl[i] = fmaf(xv, (float)wv[i], outl[i]);
+                            }
+                        }
+                        for (int p0 = 0; !use_panel && p0 < P; p0 += 8) {
+                            const h8 xv =
+                                *reinterpret_cast<const h8 *>(dec.xo + (int64_t)m * K + p0);
+#pragma unroll
+                            for (int j = 0; j < 8; j++) {
+                                const int p = p0 + j;
+                                if (p < P) {
+                                    const int col =
+                                        p < kOutCols ? out_cols[1 + p] : dec.cols[1 + p];
+                                    const h4 wv = *reinterpret_cast<const h4 *>(
+                                        dec.wt + (int64_t)col * N + nn);
+#pragma unroll
+                                    for (int i = 0; i < 4; i++)
+                                        outl[i] = fmaf((float)xv[j], (float)wv[i], outl[i]);
+                                }
                             }
                         }
                     }
-                }
-                h4 o;
+                    h4 o;
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    // The tiled kernel's expression, so both give the same bits.
-                    float v;
-                    if constexpr (ODEC)
-                        v = fmaf((float)sum[i], sxm * sw[(nn + i) / G], outl[i]) +
-                            (bias ? bias[nn + i] : 0.0f);
-                    else
-                        v = fmaf((float)sum[i], sxm * sw[(nn + i) / G], bias ? bias[nn + i] : 0.0f);
-                    if (act == 1)
-                        v = gelu_fast(v);
-                    o[i] = (_Float16)v;
+                    for (int i = 0; i < 4; i++) {
+                        // The tiled kernel's expression, so both give the same bits.
+                        float v;
+                        if constexpr (ODEC)
+                            v = fmaf((float)sum[i], sxm * sw[(nn + i) / G], outl[i]) +
+                                (bias ? bias[nn + i] : 0.0f);
+                        else
+                            v = fmaf((float)sum[i], sxm * sw[(nn + i) / G],
+                                     bias ? bias[nn + i] : 0.0f);
+                        if (act == 1)
+                            v = gelu_fast(v);
+                        o[i] = (_Float16)v;
+                    }
+                    *reinterpret_cast<h4 *>(static_cast<_Float16 *>(Y) + (int64_t)m * N + nn) = o;
+                    if (row_part)
+                        r = fmaxf(fmaxf(fabsf((float)o[0]), fabsf((float)o[1])),
+                                  fmaxf(fabsf((float)o[2]), fabsf((float)o[3])));
                 }
-                *reinterpret_cast<h4 *>(static_cast<_Float16 *>(Y) + (int64_t)m * N + nn) = o;
-                if (row_amax) {
-                    // max |fp16 output| of the row, for a per-token quantizer downstream
-                    const float r = fmaxf(fmaxf(fabsf((float)o[0]), fabsf((float)o[1])),
-                                          fmaxf(fabsf((float)o[2]), fabsf((float)o[3])));
-                    atomic_max_nonneg(row_amax + m, r);
-                }
+            }
+            if (!OUT_I32 && row_part) {
+                // Partial max |fp16 output| of token m over this row group's 16
+                // outputs (the four column quads of lanes r16 + 16 kq combined),
+                // for a per-token quantizer downstream: a plain store per group.
+                r = fmaxf(r, __shfl_xor(r, 16));
+                r = fmaxf(r, __shfl_xor(r, 32));
+                if (kq == 0 && m < M)
+                    row_part[(int64_t)m * (gridDim.x * RG) + blockIdx.x * RG + g] = r;
             }
         }
     }
@@ -391,7 +401,7 @@ template <int MT, int RG, int BKB, int NS, bool PACKED = false, bool F8 = false,
           bool ODEC = false>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
-                      void *Y, bool out_i32, hipStream_t stream, uint32_t *row_amax = nullptr,
+                      void *Y, bool out_i32, hipStream_t stream, float *row_part = nullptr,
                       const OutlierOperands *dec = nullptr)
 {
     const dim3 grid((unsigned)((N + 16 * RG - 1) / (16 * RG)));
@@ -400,15 +410,15 @@ hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const
     if constexpr (ODEC)
         hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, PACKED, false, F8, true>), grid,
                            block, 0, stream, Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N,
-                           (int)K, Y, row_amax, od);
+                           (int)K, Y, row_part, od);
     else if (out_i32)
         hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, PACKED, true, F8>), grid, block, 0,
                            stream, Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y,
-                           row_amax, od);
+                           row_part, od);
     else
         hipLaunchKernelGGL((k_gemm_skinny<MT, RG, BKB, NS, PACKED, false, F8>), grid, block, 0,
                            stream, Xq, sx, Wq, sw, (int)G, bias, act, (int)M, (int)N, (int)K, Y,
-                           row_amax, od);
+                           row_part, od);
     return hipGetLastError();
 }
 
@@ -440,11 +450,11 @@ __global__ __launch_bounds__(256) void k_pack_weights(const int8_t *__restrict__
 hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                               const float *w_scales, int64_t G, const float *bias, int act,
                               int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
-                              hipStream_t stream, uint32_t *row_amax)
+                              hipStream_t stream, float *row_part)
 {
 #define ZQ_SK(MT, RG, BKB, NS)                                                                   \
     launch_cfg<MT, RG, BKB, NS>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y, out_i32,   \
-                                stream, row_amax)
+                                stream, row_part)
     // 32 weight rows per workgroup (two row groups) fills 256 CUs at N = 8192;
     // 512-byte row pieces four slabs deep (measured against 256- and 1024-byte
     // pieces two to eight deep, and against cached weight loads).
@@ -452,6 +462,11 @@ hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int
         return ZQ_SK(1, 2, 512, 4);
     return ZQ_SK(2, 2, 512, 4);
 #undef ZQ_SK
+}
+
+int64_t gemm_skinny_row_groups(int64_t N)
+{
+    return (N + 31) / 32 * 2;  // 32 output rows per workgroup, two row groups
 }
 
 hipError_t launch_gemm_skinny_packed(const int8_t *Xq, const float *x_scales, const int8_t *Wp,

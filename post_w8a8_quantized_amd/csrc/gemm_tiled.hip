@@ -135,8 +135,8 @@ __global__ __launch_bounds__(WM *WN * 64)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_tiled(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int M, int N, int K,
-    void *__restrict__ Y, int tiles_m, int tiles_n, uint32_t *__restrict__ row_amax,
-    OutlierOperands dec)
+    void *__restrict__ Y, int tiles_m, int tiles_n, float *__restrict__ row_part,
+    int part_groups, OutlierOperands dec)
 {
     using C = Cfg<BM, BN, WM, WN, BK, NSTAGE>;
     // One LDS object per slab buffer, referenced statically from an unrolled
@@ -594,12 +594,13 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
             }
         }
     }
-    // With row_amax, the tile also folds max |fp16 output| of each of its rows
-    // into row_amax[m] (float bits; an atomic max after the two lanes that
-    // hold a row have combined theirs), for a per-token quantizer downstream.
+    // With row_part, each wave also writes max |fp16 output| of each of its
+    // rows over its TWN columns to row_part[m * part_groups + tn * WN + wn]
+    // (after the two lanes that hold a row have combined theirs): partial
+    // maxima for a per-token quantizer downstream, plain stores, no atomics.
     auto epilogue = [&](auto checked, auto fold_amax) {
         constexpr bool CHECK = decltype(checked)::value;
-        constexpr bool AMAX = decltype(fold_amax)::value;  // row_amax given
+        constexpr bool AMAX = decltype(fold_amax)::value;  // row_part given
 #pragma unroll
         for (int b = 0; b < C::FM; b++) {
             float rmax = 0.0f;
@@ -637,7 +638,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
                 rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
                 const int m = m0 + wm * C::TWM + b * 32 + frow;
                 if (fhalf == 0 && (!CHECK || m < M))
-                    atomic_max_nonneg(row_amax + m, rmax);
+                    row_part[(int64_t)m * part_groups + tn * WN + wn] = rmax;
             }
 #pragma unroll
             for (int j = 0; j < 32 * CPR_OUT / 64; j++) {
@@ -667,7 +668,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
         }
     };
     const bool interior = m0 + BM <= M && n0 + BN <= N;
-    if (row_amax) {
+    if (row_part) {
         if (interior)
             epilogue(std::false_type{}, std::true_type{});
         else
@@ -683,7 +684,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
 template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool F8 = false, bool ODEC = false>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
-                      void *Y, bool out_i32, hipStream_t stream, uint32_t *row_amax,
+                      void *Y, bool out_i32, hipStream_t stream, float *row_part,
                       const OutlierOperands *dec = nullptr)
 {
     const int tiles_m = (int)((M + BM - 1) / BM);
@@ -694,7 +695,7 @@ hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const
 #define ZQ_GEMM_LAUNCH(I32, A, D)                                                                 \
     hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, BK, NSTAGE, I32, A, F8, D>), grid, block, 0,  \
                        stream, Xq, sx, Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y, tiles_m,  \
-                       tiles_n, row_amax, od)
+                       tiles_n, row_part, tiles_n * WN, od)
     if constexpr (ODEC) {
         static_assert(!F8, "the outlier epilogue follows the int8 GEMM");
         if (act == 1)
@@ -759,17 +760,26 @@ int pick_tile(int64_t M, int64_t N)
 hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                              const float *w_scales, int64_t G, const float *bias, int act,
                              int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
-                             hipStream_t stream, uint32_t *row_amax)
+                             hipStream_t stream, float *row_part)
 {
 #define ZQ_CFG(BM, BN, WM, WN, BK, NS)                                                           \
     launch_cfg<BM, BN, WM, WN, BK, NS>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,      \
-                                       out_i32, stream, row_amax)
+                                       out_i32, stream, row_part)
     switch (pick_tile(M, N)) {
     case 0: return ZQ_CFG(256, 192, 4, 2, 128, 2);
     case 1: return ZQ_CFG(256, 256, 4, 2, 128, 2);
     default: return ZQ_CFG(128, 128, 2, 2, 64, 4);
     }
 #undef ZQ_CFG
+}
+
+int64_t gemm_tiled_row_groups(int64_t M, int64_t N)
+{
+    switch (pick_tile(M, N)) {
+    case 0: return (N + 191) / 192 * 2;   // 256x192, two waves across
+    case 1: return (N + 255) / 256 * 2;   // 256x256, two waves across
+    default: return (N + 127) / 128 * 2;  // 128x128, two waves across
+    }
 }
 
 hipError_t launch_gemm_tiled_decomp(const int8_t *Xq, const float *x_scales, const int8_t *Wq,

@@ -124,7 +124,7 @@ template <typename T, int NCH, int WPT, int TPB, bool OUT_F16 = false, bool FP8 
 __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
     const T *__restrict__ X, int M, int K, int pre, const float *__restrict__ gamma,
     const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx,
-    _Float16 *__restrict__ Y16, uint32_t *__restrict__ zero_rows, float alpha,
+    _Float16 *__restrict__ Y16, float alpha,
     int32_t *__restrict__ slot, _Float16 *__restrict__ XO)
 {
     constexpr int TT = kWave * WPT;  // threads per token
@@ -135,8 +135,6 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
     const int64_t m = (int64_t)blockIdx.x * TPB + tok_in_blk;
     const bool live = m < M;
     const int nchunks = K / 8;
-    if (zero_rows && live && t == 0)
-        zero_rows[m] = 0u;
 
     __shared__ float red[TPB][WPT > 1 ? WPT : 1];
 
@@ -426,8 +424,7 @@ __device__ __forceinline__ float block_reduce(float v, float *red)
 template <typename T, int PRE, bool FP8>
 __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
     const T *__restrict__ X, int M, int K, int nseg, const float *__restrict__ gamma,
-    const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx,
-    uint32_t *__restrict__ zero_rows)
+    const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx)
 {
     __shared__ float red[kSegThreads / kWave];
     const int j = blockIdx.x / 8;
@@ -435,8 +432,6 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
     const int64_t m = (int64_t)(j / nseg) * 8 + blockIdx.x % 8;
     if (m >= M)
         return;
-    if (zero_rows && seg == 0 && threadIdx.x == 0)
-        zero_rows[m] = 0u;
     const T *xrow = X + m * (int64_t)K;
     const int nch = K / 8;
     const int own = seg * kSegThreads + threadIdx.x;  // this thread's chunk
@@ -833,7 +828,7 @@ template <typename T, int WPT, int TPB, bool OUT_F16 = false, bool FP8 = false, 
           int MAXN = 16>
 hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
                       const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
-                      _Float16 *Y16 = nullptr, uint32_t *zero_rows = nullptr, float alpha = 0.0f,
+                      _Float16 *Y16 = nullptr, float alpha = 0.0f,
                       int32_t *slot = nullptr, _Float16 *XO = nullptr)
 {
     const int64_t nchunks = K / 8;
@@ -845,7 +840,7 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
     if (per <= n) {                                                                             \
         hipLaunchKernelGGL((k_ln_quant<T, n, WPT, TPB, OUT_F16, FP8, DEC>), grid, block, 0,     \
                            stream, X, (int)M, (int)K, pre, gamma, beta, eps, Xq, sx, Y16,       \
-                           zero_rows, alpha, slot, XO);                                         \
+                           alpha, slot, XO);                                                    \
         return hipGetLastError();                                                               \
     }
     ZQ_LNQ_CASE(1)
@@ -870,23 +865,23 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
 template <typename T, bool OUT_F16, bool FP8, int DEC>
 hipError_t launch_rows(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
                        const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
-                       _Float16 *Y16, uint32_t *zero_rows, float alpha = 0.0f,
+                       _Float16 *Y16, float alpha = 0.0f,
                        int32_t *slot = nullptr, _Float16 *XO = nullptr)
 {
     if (K <= 2048)
         return launch_cfg<T, 1, 4, OUT_F16, FP8, DEC, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx,
-                                                         stream, Y16, zero_rows, alpha, slot, XO);
+                                                         stream, Y16, alpha, slot, XO);
     if (K <= 8192)
         return launch_cfg<T, 4, 1, OUT_F16, FP8, DEC, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx,
-                                                         stream, Y16, zero_rows, alpha, slot, XO);
+                                                         stream, Y16, alpha, slot, XO);
     return launch_cfg<T, 16, 1, OUT_F16, FP8, DEC, 16>(X, M, K, pre, gamma, beta, eps, Xq, sx,
-                                                       stream, Y16, zero_rows, alpha, slot, XO);
+                                                       stream, Y16, alpha, slot, XO);
 }
 
 template <typename T>
 hipError_t launch_typed(const T *X, int64_t M, int64_t K, int pre, const float *gamma,
                         const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream,
-                        uint32_t *zero_rows, bool fp8)
+                        bool fp8)
 {
     // Few tokens with long rows: spread each row over ceil(K / 2048) workgroups.
     if (M <= kRowSegMaxM && K >= kRowSegMinK) {
@@ -894,7 +889,7 @@ hipError_t launch_typed(const T *X, int64_t M, int64_t K, int pre, const float *
         const dim3 grid((unsigned)(8 * ((M + 7) / 8) * nseg));
 #define ZQ_ROWSEG(P, F)                                                                           \
     hipLaunchKernelGGL((k_rowseg_quant<T, P, F>), grid, dim3(kSegThreads), 0, stream, X, (int)M,  \
-                       (int)K, nseg, gamma, beta, eps, Xq, sx, zero_rows)
+                       (int)K, nseg, gamma, beta, eps, Xq, sx)
         if (fp8) {
             if (pre == 1)
                 ZQ_ROWSEG(1, true);
@@ -915,9 +910,9 @@ hipError_t launch_typed(const T *X, int64_t M, int64_t K, int pre, const float *
     }
     if (fp8)
         return launch_rows<T, false, true, 0>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream,
-                                              nullptr, zero_rows);
-    return launch_rows<T, false, false, 0>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream, nullptr,
-                                           zero_rows);
+                                              nullptr);
+    return launch_rows<T, false, false, 0>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream,
+                                           nullptr);
 }
 
 }  // namespace
@@ -929,9 +924,9 @@ hipError_t launch_ln_to_f16(const void *X, bool x_f16, int64_t M, int64_t K, int
     if (x_f16)
         return launch_rows<_Float16, true, false, 0>(static_cast<const _Float16 *>(X), M, K, pre,
                                                      gamma, beta, eps, nullptr, nullptr, stream,
-                                                     Y16, nullptr);
+                                                     Y16);
     return launch_rows<float, true, false, 0>(static_cast<const float *>(X), M, K, pre, gamma, beta,
-                                              eps, nullptr, nullptr, stream, Y16, nullptr);
+                                              eps, nullptr, nullptr, stream, Y16);
 }
 
 namespace {
@@ -941,7 +936,7 @@ hipError_t launch_decomp_typed(const T *X, int64_t M, int64_t K, int pre, const 
                                int8_t *Xq, float *sx, _Float16 *XO, hipStream_t stream)
 {
     return launch_rows<T, false, false, DEC>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream,
-                                             nullptr, nullptr, alpha, slot, XO);
+                                             nullptr, alpha, slot, XO);
 }
 }  // namespace
 
@@ -1021,48 +1016,62 @@ hipError_t launch_ln_quant_decomp(const void *X, bool x_f16, int64_t M, int64_t 
 
 hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                            const float *gamma, const float *beta, float eps, int8_t *Xq,
-                           float *x_scales, hipStream_t stream, uint32_t *zero_rows, bool fp8)
+                           float *x_scales, hipStream_t stream, bool fp8)
 {
     if (x_f16)
         return launch_typed(static_cast<const _Float16 *>(X), M, K, pre, gamma, beta, eps, Xq,
-                            x_scales, stream, zero_rows, fp8);
+                            x_scales, stream, fp8);
     return launch_typed(static_cast<const float *>(X), M, K, pre, gamma, beta, eps, Xq, x_scales,
-                        stream, zero_rows, fp8);
+                        stream, fp8);
 }
 
-// Codes of fp16 rows whose absmax is already known (row_amax holds the float
-// bits of max |y| per row, non-negative): s = fl32(a / 127) as the prologue
-// computes it, then the same quantizer.  One thread per 8-element chunk.
+// Codes of fp16 rows whose absmax comes from partial maxima: part[m * groups + j]
+// holds max |Y[m, n]| over column group j (written by the producing GEMM's
+// epilogue), so max_j part[m * groups + j] is the row's absmax exactly.  One
+// workgroup per row: the partials are combined first, then s = fl32(a / 127)
+// as the prologue computes it and the same quantizer.
 namespace {
-__global__ __launch_bounds__(256) void k_quant_known(const _Float16 *__restrict__ Y, int M, int K,
-                                                     const uint32_t *__restrict__ row_amax,
-                                                     int8_t *__restrict__ Xq,
-                                                     float *__restrict__ sx)
+constexpr int kQpThreads = 128;
+
+__global__ __launch_bounds__(kQpThreads) void k_quant_rows_part(
+    const _Float16 *__restrict__ Y, int K, const float *__restrict__ part, int groups,
+    int8_t *__restrict__ Xq, float *__restrict__ sx)
 {
-    const int cpr = K / 8;
-    const int64_t total = (int64_t)M * cpr;
-    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
-         c += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t m = c / cpr;
-        const float scale = __uint_as_float(row_amax[m]) / 127.0f;
-        const bool fast = rcp_quant_ok(scale);
-        const float rs = fast ? 1.0f / scale : 0.0f;
+    __shared__ float red[kQpThreads / kWave];
+    const int64_t m = blockIdx.x;
+    float a = 0.0f;
+    for (int j = threadIdx.x; j < groups; j += kQpThreads)
+        a = fmaxf(a, part[m * groups + j]);
+    a = wave_max(a);
+    if (threadIdx.x % kWave == 0)
+        red[threadIdx.x / kWave] = a;
+    __syncthreads();
+    a = red[0];
+#pragma unroll
+    for (int w = 1; w < kQpThreads / kWave; w++)
+        a = fmaxf(a, red[w]);
+    const float scale = a / 127.0f;
+    const bool fast = rcp_quant_ok(scale);
+    const float rs = fast ? 1.0f / scale : 0.0f;
+    const _Float16 *yrow = Y + m * (int64_t)K;
+    int8_t *qrow = Xq + m * (int64_t)K;
+    for (int c = threadIdx.x; c < K / 8; c += kQpThreads) {
         float y[8];
-        Chunk<_Float16>::load(Y + c * 8, y);
-        *reinterpret_cast<uint2 *>(Xq + c * 8) = quant8(y, scale, rs, fast);
-        if (c % cpr == 0)
-            sx[m] = scale;
+        Chunk<_Float16>::load(yrow + (int64_t)c * 8, y);
+        *reinterpret_cast<uint2 *>(qrow + (int64_t)c * 8) = quant8(y, scale, rs, fast);
     }
+    if (threadIdx.x == 0)
+        sx[m] = scale;
 }
 }  // namespace
 
-hipError_t launch_quant_known(const _Float16 *Y, int64_t M, int64_t K, const uint32_t *row_amax,
-                              int8_t *Xq, float *x_scales, hipStream_t stream)
+hipError_t launch_quant_rows_part(const _Float16 *Y, int64_t M, int64_t K, const float *part,
+                                  int64_t groups, int8_t *Xq, float *x_scales, hipStream_t stream)
 {
-    const int64_t total = M * (K / 8);
-    const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
-    hipLaunchKernelGGL(k_quant_known, dim3((unsigned)blocks), dim3(256), 0, stream, Y, (int)M,
-                       (int)K, row_amax, Xq, x_scales);
+    if (M < 1)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_quant_rows_part, dim3((unsigned)M), dim3(kQpThreads), 0, stream, Y,
+                       (int)K, part, (int)groups, Xq, x_scales);
     return hipGetLastError();
 }
 

@@ -349,8 +349,17 @@ ZQ_API zq_status zq_linear_w8a8_unfused(const void *X, zq_dtype x_dtype, zq_pre 
                                       stream));
 }
 
-// Workspace of zq_ffn_w8a8: codes1 [M*K] | scales1 [M] | H fp16 [M*F] | row absmax [M] |
-// codes2 [M*F] | scales2 [M], each part starting on a 256-byte boundary.
+namespace {
+// Column groups of H's partial row maxima: at most F / 16 + 2 for either GEMM.
+int64_t ffn_row_groups_max(int64_t F)
+{
+    return F / 16 + 2;
+}
+}  // namespace
+
+// Workspace of zq_ffn_w8a8: codes1 [M*K] | scales1 [M] | H fp16 [M*F] |
+// partial row maxima fp32 [M * (F/16 + 2)] | codes2 [M*F] | scales2 [M], each part
+// starting on a 256-byte boundary.
 ZQ_API size_t zq_ffn_workspace_bytes(int64_t M, int64_t K, int64_t F)
 {
     if (M < 1 || !k_ok(K) || !k_ok(F) || M > INT32_MAX || M * K > (int64_t)1 << 40 ||
@@ -358,7 +367,8 @@ ZQ_API size_t zq_ffn_workspace_bytes(int64_t M, int64_t K, int64_t F)
         return 0;
     const size_t m = (size_t)M;
     return round_up(m * K, 256) + round_up(4 * m, 256) + round_up(2 * m * F, 256) +
-           round_up(4 * m, 256) + round_up(m * F, 256) + round_up(4 * m, 256);
+           round_up(4 * m * (size_t)ffn_row_groups_max(F), 256) + round_up(m * F, 256) +
+           round_up(4 * m, 256);
 }
 
 ZQ_API zq_status zq_ffn_w8a8(const void *X, zq_dtype x_dtype, const float *gamma,
@@ -386,8 +396,8 @@ ZQ_API zq_status zq_ffn_w8a8(const void *X, zq_dtype x_dtype, const float *gamma
     off += round_up(4 * m, 256);
     _Float16 *H = reinterpret_cast<_Float16 *>(ws + off);
     off += round_up(2 * mf, 256);
-    uint32_t *amax = reinterpret_cast<uint32_t *>(ws + off);
-    off += round_up(4 * m, 256);
+    float *part = reinterpret_cast<float *>(ws + off);
+    off += round_up(4 * m * (size_t)(F > 0 ? ffn_row_groups_max(F) : 0), 256);
     int8_t *Xq2 = reinterpret_cast<int8_t *>(ws + off);
     off += round_up(mf, 256);
     float *sx2 = reinterpret_cast<float *>(ws + off);
@@ -405,22 +415,26 @@ ZQ_API zq_status zq_ffn_w8a8(const void *X, zq_dtype x_dtype, const float *gamma
     if (workspace_bytes < need)
         return ZQ_ERR_WORKSPACE;
     clear_stale_error();
-    // FFN-up: LN + quantize (clearing the row absmax buffer on the way) ...
+    // FFN-up: LN + quantize ...
     st = map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, ZQ_PRE_LAYERNORM, gamma, beta,
-                                     eps, Xq1, sx1, stream, amax));
+                                     eps, Xq1, sx1, stream));
     if (st != ZQ_OK)
         return st;
-    // ... GEMM + bias + GeLU, whose epilogue also folds max |H[m, :]| into amax ...
-    if (M <= kSkinnyMaxM)
+    // ... GEMM + bias + GeLU, whose epilogue also writes partial maxima of |H[m, :]| ...
+    const bool skinny = M <= kSkinnyMaxM;
+    const int64_t groups = skinny ? zq::gemm_skinny_row_groups(F) : zq::gemm_tiled_row_groups(M, F);
+    if (groups > ffn_row_groups_max(F))
+        return ZQ_ERR_UNSUPPORTED;  // not reached: every column group has at least 16 columns
+    if (skinny)
         st = map_hip(zq::launch_gemm_skinny(Xq1, sx1, W1q, w1_scales, group_rows1, bias1,
-                                            ZQ_ACT_GELU, M, F, K, H, false, stream, amax));
+                                            ZQ_ACT_GELU, M, F, K, H, false, stream, part));
     else
         st = map_hip(zq::launch_gemm_tiled(Xq1, sx1, W1q, w1_scales, group_rows1, bias1,
-                                           ZQ_ACT_GELU, M, F, K, H, false, stream, amax));
+                                           ZQ_ACT_GELU, M, F, K, H, false, stream, part));
     if (st != ZQ_OK)
         return st;
-    // FFN-down: quantize H with the absmax already known, then GEMM + bias.
-    st = map_hip(zq::launch_quant_known(H, M, F, amax, Xq2, sx2, stream));
+    // FFN-down: quantize H from the partial maxima, then GEMM + bias.
+    st = map_hip(zq::launch_quant_rows_part(H, M, F, part, groups, Xq2, sx2, stream));
     if (st != ZQ_OK)
         return st;
     return gemm_dispatch(Xq2, sx2, W2q, w2_scales, group_rows2, bias2, ZQ_ACT_NONE, M, K, F, Y,
@@ -462,7 +476,7 @@ ZQ_API zq_status zq_ln_quant_per_token_fp8(const void *X, zq_dtype x_dtype, int6
     return map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                        pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                        pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, Xq,
-                                       x_scales, stream, nullptr, true));
+                                       x_scales, stream, true));
 }
 
 namespace {
@@ -545,8 +559,7 @@ zq_status linear_fp8_impl(const void *X, zq_dtype x_dtype, zq_pre pre, const flo
     st = map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                      pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                      pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps,
-                                     reinterpret_cast<int8_t *>(Xq8), x_scales, stream, nullptr,
-                                     true));
+                                     reinterpret_cast<int8_t *>(Xq8), x_scales, stream, true));
     if (st != ZQ_OK)
         return st;
     return fp8_gemm(Xq8, x_scales, Wq8, w_scales, group_rows, bias, act, M, N, K, Y, ZQ_F16,

@@ -20,16 +20,15 @@ struct OutlierOperands {
 
 // Prologue: LN / GeLU / none in fp32, then per-token absmax quantization
 // (int8 codes, or with fp8 OCP E4M3 codes and power-of-two scales).
-// zero_rows (optional, M entries) is cleared on the way (a per-token absmax
-// buffer that a following GEMM epilogue fills with atomics).
 hipError_t launch_ln_quant(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
                            const float *gamma, const float *beta, float eps,
-                           int8_t *Xq, float *x_scales, hipStream_t stream,
-                           uint32_t *zero_rows = nullptr, bool fp8 = false);
+                           int8_t *Xq, float *x_scales, hipStream_t stream, bool fp8 = false);
 
-// Quantization of fp16 rows whose per-row absmax (float bits) is already known.
-hipError_t launch_quant_known(const _Float16 *Y, int64_t M, int64_t K, const uint32_t *row_amax,
-                              int8_t *Xq, float *x_scales, hipStream_t stream);
+// Quantization of fp16 rows whose absmax is the maximum of partial maxima
+// part[m * groups + j] (from a GEMM epilogue's row_part output).
+hipError_t launch_quant_rows_part(const _Float16 *Y, int64_t M, int64_t K, const float *part,
+                                  int64_t groups, int8_t *Xq, float *x_scales,
+                                  hipStream_t stream);
 
 // The op alone, its result stored as fp16 (the unfused order).
 hipError_t launch_ln_to_f16(const void *X, bool x_f16, int64_t M, int64_t K, int pre,
@@ -43,12 +42,14 @@ hipError_t launch_dequant(const int32_t *acc, const float *x_scales, const float
 
 // Tiled MFMA GEMM (prefill shapes) with the fused dequant epilogue.
 // out_i32 selects the raw-accumulator test mode.
-// row_amax (optional, fp16 output only): atomic max of |Y[m, :]| per row, as
-// float bits; the caller clears it first.
+// row_part (optional, fp16 output only): partial maxima of |Y[m, :]|,
+// row_part[m * gemm_tiled_row_groups(M, N) + j] over column group j; every
+// entry of a row m < M is written (plain stores, nothing to clear first).
 hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                              const float *w_scales, int64_t G, const float *bias, int act,
                              int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
-                             hipStream_t stream, uint32_t *row_amax = nullptr);
+                             hipStream_t stream, float *row_part = nullptr);
+int64_t gemm_tiled_row_groups(int64_t M, int64_t N);
 
 // The FP8 variant of the tiled GEMM: OCP E4M3 operands, fp32 accumulation,
 // same epilogue; out_raw writes the fp32 accumulators.
@@ -57,11 +58,13 @@ hipError_t launch_gemm_tiled_fp8(const int8_t *Xq, const float *x_scales, const 
                                  int64_t M, int64_t N, int64_t K, void *Y, bool out_raw,
                                  hipStream_t stream);
 
-// Weight-streaming MFMA GEMM for M <= 32 (decode shapes), same epilogue.
+// Weight-streaming MFMA GEMM for M <= 32 (decode shapes), same epilogue;
+// row_part as for the tiled GEMM, with gemm_skinny_row_groups(N) groups.
 hipError_t launch_gemm_skinny(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                               const float *w_scales, int64_t G, const float *bias, int act,
                               int64_t M, int64_t N, int64_t K, void *Y, bool out_i32,
-                              hipStream_t stream, uint32_t *row_amax = nullptr);
+                              hipStream_t stream, float *row_part = nullptr);
+int64_t gemm_skinny_row_groups(int64_t N);
 
 // The same kernel reading weights in the packed layout of launch_pack_weights.
 hipError_t launch_gemm_skinny_packed(const int8_t *Xq, const float *x_scales, const int8_t *Wp,

@@ -64,14 +64,16 @@ def test_ffn_block(zq, M, K, F, dt):
     Y2 = host(zq.linear_w8a8(H2, W2q, s2, G2, zq.PRE_NONE, None, None, 1e-5, b2d, zq.ACT_NONE))
     assert np.array_equal(Y.view(np.uint16), Y2.view(np.uint16))
 
-    # H and the folded row absmax in the workspace
+    # H in the workspace, and H's per-token scales, which come from the partial
+    # row maxima the FFN-up epilogue wrote: exactly fl32(max |H[m, :]| / 127)
     w = host(ws)
     off = r256(M * K) + r256(4 * M)
     H = w[off:off + 2 * M * F].view(np.float16).reshape(M, F)
     assert np.array_equal(H.view(np.uint16), host(H2).view(np.uint16))
-    off += r256(2 * M * F)
-    amax = w[off:off + 4 * M].view(np.float32)
-    assert np.array_equal(amax, np.max(np.abs(H.astype(np.float32)), axis=1))
+    off += r256(2 * M * F) + r256(4 * M * (F // 16 + 2)) + r256(M * F)
+    sx2 = w[off:off + 4 * M].view(np.float32)
+    amax = np.max(np.abs(H.astype(np.float32)), axis=1)
+    assert np.array_equal(sx2, (amax / np.float32(127.0)).astype(np.float32))
 
     # against the oracle's chain (its own H, codes and scales)
     W1q_h, s1_h, W2q_h, s2_h = host(W1q), host(s1), host(W2q), host(s2)
