@@ -38,8 +38,8 @@
 //    M-tiles (N next) and each XCD takes a contiguous run, so the ~32 tiles
 //    an XCD runs at once share 8 X panels and 4 W panels in its L2.
 //  - Modes: int32 accumulators out (test mode), the FP8 variant (OCP E4M3
-//    operands on v_mfma_scale_f32_32x32x64_f8f6f4), a per-row |Y| maximum
-//    folded with atomics (for a downstream quantizer), and the
+//    operands on v_mfma_scale_f32_32x32x64_f8f6f4), partial per-row |Y|
+//    maxima, one per wave (for a downstream quantizer), and the
 //    mixed-precision decomposition's fp16 outlier part in the epilogue.
 
 #include "zq_device.h"

@@ -1,7 +1,7 @@
 """The chained FFN block: bit-identical to two zq_linear_w8a8 calls (FFN-up with
 LayerNorm and the GeLU epilogue, then FFN-down without a pre-op on H), the
-per-token absmax the FFN-up epilogue folds equal to max |H| exactly, and the
-block against the oracle's chain."""
+scales of H (from the partial row maxima the FFN-up epilogue writes) equal to
+fl32(max |H| / 127) exactly, and the block against the oracle's chain."""
 from __future__ import annotations
 
 import numpy as np

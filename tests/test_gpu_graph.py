@@ -137,9 +137,9 @@ def _check_replays(call, Y, ws, fills=(0, 0, 0, 0)):
 
 @pytest.mark.parametrize("M", [16, 300])
 def test_graph_replays_match_eager_ffn(M):
-    """The chained FFN block: its FFN-up epilogue folds max |H| per token into a
-    workspace buffer with atomics, which the prologue kernel clears first, so
-    garbage left in the workspace between replays changes nothing."""
+    """The chained FFN block: its FFN-up epilogue writes every partial row
+    maximum that H's quantizer reads (plain stores), so garbage left in the
+    workspace between replays changes nothing."""
     import post_w8a8_quantized_amd as zq
     say("graph replay ffn", M)
     rng = np.random.default_rng(M + 2)
