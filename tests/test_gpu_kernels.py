@@ -122,6 +122,35 @@ def test_gemm_dequant_epilogue(zq, path, act, G):
     assert off.mean() <= 1e-3, off.mean()
 
 
+@pytest.mark.parametrize("path", ["tiled", "skinny"])
+def test_gemm_gelu_epilogue_far_range(zq, path):
+    """GeLU epilogue over pre-activations far outside the polynomial's fitted
+    range [-6.5, 6.5] (the bias carries them out to +-3e4): every output is
+    finite and within one fp16 ulp of fp16(exact GeLU), so GeLU(v) = v for
+    large v and -0 or 0 for large negative v."""
+    M = 24 if path == "skinny" else 200
+    N, K, G = 192, 64, 4
+    say("gelu far range", path)
+    rng = np.random.default_rng(7)
+    Xq = random_int8(rng, (M, K))
+    Wq = random_int8(rng, (N, K))
+    s_x = (np.exp(rng.standard_normal(M)) * 1e-3).astype(np.float32)
+    s_w = (np.exp(rng.standard_normal(N // G)) * 1e-4).astype(np.float32)
+    mag = 10.0 ** rng.uniform(-2.0, np.log10(3e4), N)
+    bias = (np.where(np.arange(N) % 2 == 0, 1.0, -1.0) * mag).astype(np.float32)
+    want = ref.epilogue(ref.gemm_i32(Xq, Wq), s_x, s_w, G, bias, ref.ACT_GELU)
+    p = zq.PATH_TILED if path == "tiled" else zq.PATH_SKINNY
+    got = host(zq.w8a8_gemm_dequant(dev(Xq), dev(s_x), dev(Wq), dev(s_w), G, dev(bias),
+                                    zq.ACT_GELU, path=p))
+    assert np.all(np.isfinite(got))
+    w64 = want.astype(np.float64)
+    ulp = np.spacing(np.abs(want).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(got.astype(np.float64) - w64) <= ulp)
+    big = np.abs(w64) >= 8.0
+    assert big.sum() > M * N // 6
+    assert np.array_equal(got[big], want[big])
+
+
 @pytest.mark.parametrize("M,N,K", TILED_SHAPES + [(520, 392, 256), (300, 204, 96)])
 def test_gemm_tiled_f16_tile_edges(zq, M, N, K):
     """fp16 output of the tiled kernel at tile multiples and at ragged M and N
