@@ -28,6 +28,11 @@
  *   - Matrices are row-major and dense: X [M x K], Xq [M x K], W / Wq [N x K]
  *     (output rows, input columns, so both GEMM operands are K-contiguous),
  *     Y [M x N].  M = tokens, K = input features, N = output features.
+ *   - Size caps beyond each call's own rules: M, N <= 2^31 - 1 and every
+ *     matrix a call reads or writes (M x K, N x K, M x N) has at most 2^40
+ *     elements (the unfused layer caps M x N at 2^38, the FFN block M x F
+ *     at 2^39, for their workspaces); larger sizes return ZQ_ERR_SHAPE, and
+ *     the workspace-size helpers return 0.
  *   - Arguments are validated on the host before anything is enqueued; on an
  *     error nothing is enqueued and a non-zero zq_status is returned.  A
  *     launch failure reported by the HIP runtime returns ZQ_ERR_HIP.  Faults

@@ -56,7 +56,8 @@ zq_status check_gemm(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
         return ZQ_ERR_NULL;
     if (M < 1 || N < 1 || !k_ok(K) || G < 1 || N % G != 0 || N % 4 != 0)
         return ZQ_ERR_SHAPE;
-    if (M > INT32_MAX || N > INT32_MAX || M * K > (int64_t)1 << 40 || N * K > (int64_t)1 << 40)
+    if (M > INT32_MAX || N > INT32_MAX || M * K > (int64_t)1 << 40 || N * K > (int64_t)1 << 40 ||
+        M * N > (int64_t)1 << 40)
         return ZQ_ERR_SHAPE;
     if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(Y))
         return ZQ_ERR_ALIGN;

@@ -67,6 +67,9 @@ def gemm(L, Xq=A, sx=A, Wq=A, sw=A, G=128, bias=None, act=0, M=16, N=256, K=256,
     (dict(M=0), SHAPE), (dict(N=0), SHAPE), (dict(K=0), SHAPE), (dict(K=24), SHAPE),
     (dict(K=131072 + 16), SHAPE), (dict(G=0), SHAPE), (dict(G=96), SHAPE),
     (dict(N=250, G=2), SHAPE), (dict(M=33, path=2), SHAPE),
+    (dict(M=1 << 31, K=16), SHAPE), (dict(N=1 << 31, K=16, G=1), SHAPE),
+    (dict(M=1 << 21, N=1 << 20, K=16, G=1), SHAPE),    # Y would exceed 2^40 elements
+    (dict(M=1 << 24, K=1 << 17), SHAPE),                # Xq would exceed 2^40 elements
     (dict(Xq=UNALIGNED), ALIGN), (dict(Wq=UNALIGNED), ALIGN), (dict(Y=UNALIGNED), ALIGN),
     (dict(ydt=0), DTYPE), (dict(ydt=2), DTYPE), (dict(act=2), DTYPE), (dict(path=3), DTYPE),
 ])
