@@ -111,6 +111,36 @@ def test_fp8_gemm_accumulators(zq, M, N, K):
     assert np.all(np.abs(acc.astype(np.float64) - want) <= bound)
 
 
+@pytest.mark.parametrize("M", [200, 16])
+def test_fp8_gemm_gelu_far_range(zq, M):
+    """The FP8 GEMMs' GeLU epilogue over pre-activations far outside the
+    polynomial's fitted range (the bias carries them out to +-3e4): outputs are
+    finite, GeLU(v) is v for large v (within one fp16 ulp: the FP8 accumulators
+    are not exact) and exactly 0 for large negative v."""
+    N, K, G = 192, 128, 4
+    say("fp8 gelu far range", M)
+    rng = np.random.default_rng(11 + M)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    q_ref, s_ref = ref.quantize_rows_fp8(X)
+    wq_ref, sw_ref = ref.quantize_groups_fp8(W, G)
+    mag = 10.0 ** rng.uniform(-2.0, np.log10(3e4), N)
+    bias = (np.where(np.arange(N) % 2 == 0, 1.0, -1.0) * mag).astype(np.float32)
+    Y = host(zq.fp8_gemm_dequant(dev(q_ref), dev(s_ref), dev(wq_ref), dev(sw_ref), G, dev(bias),
+                                 zq.ACT_GELU))
+    want = ref.epilogue_f64acc(ref.gemm_fp8(q_ref, wq_ref), s_ref, sw_ref, G, bias, zq.ACT_GELU)
+    assert np.all(np.isfinite(Y))
+    assert_y(Y, want)
+    w64, y64 = want.astype(np.float64), Y.astype(np.float64)
+    ulp = np.spacing(np.abs(want).astype(np.float16)).astype(np.float64)
+    big = w64 >= 8.0
+    assert big.sum() > M * N // 6
+    assert np.all(np.abs(y64[big] - w64[big]) <= ulp[big])
+    neg = np.broadcast_to(bias <= -10.0, Y.shape)
+    assert neg.sum() > M * N // 6
+    assert np.all(y64[neg] == 0.0)
+
+
 @pytest.mark.parametrize("M,N,K,G,act", [(200, 384, 768, 64, 1), (16, 256, 1024, 64, 0),
                                          (33, 132, 512, 4, 1)])
 def test_fp8_gemm_epilogue(zq, M, N, K, G, act):
