@@ -34,9 +34,10 @@
 //    per-row activation scales sit in registers.  The fp16 epilogue stages
 //    each wave's rows through LDS and writes whole-row 16-byte pieces with
 //    non-temporal stores.
-//  - Workgroup b runs on XCD b % 8.  Tiles are ordered in groups of 8
+//  - Workgroup b runs on XCD b % 8.  Tiles are ordered in groups of 4
 //    M-tiles (N next) and each XCD takes a contiguous run, so the ~32 tiles
-//    an XCD runs at once share 8 X panels and 4 W panels in its L2.
+//    an XCD runs at once share 4 X panels and 8 W panels in its L2 (on BERT
+//    FFN-up 1.5-2% faster than 8 X and 4 W panels, which fetch ~9% more).
 //  - Modes: int32 accumulators out (test mode), the FP8 variant (OCP E4M3
 //    operands on v_mfma_scale_f32_32x32x64_f8f6f4), partial per-row |Y|
 //    maxima, one per wave (for a downstream quantizer), and the
@@ -106,7 +107,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     int t = bid;
     if ((total & 7) == 0)
         t = (bid & 7) * (total >> 3) + (bid >> 3);
-    constexpr int GM = 8;
+    constexpr int GM = 4;
     const int per_group = GM * tiles_n;
     const int g = t / per_group;
     const int gm = min(GM, tiles_m - g * GM);
