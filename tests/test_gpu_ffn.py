@@ -42,6 +42,7 @@ def r256(v):
     (5, 768, 3072, np.float16),
     (200, 768, 3072, np.float16),   # tiled kernels, ragged M
     (300, 512, 1040, np.float16),   # ragged F tile
+    (40, 256, 4112, np.float16),    # H rows longer than the quantizer holds in registers
 ])
 def test_ffn_block(zq, M, K, F, dt):
     say("ffn", M, K, F, dt.__name__)
