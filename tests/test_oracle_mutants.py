@@ -60,6 +60,15 @@ MUTANTS = {
     "fp8_gemm_transposed_w": ("lut[Wq[n * K + k]]", "lut[Wq[k * N + n]]"),
     "smooth_inverted": ("(float)sqrt(a / w)", "(float)sqrt(w / a)"),
     "fold_weight_divides": ("(double)W[n * K + j] * (double)s[j]", "(double)W[n * K + j] / (double)s[j]"),
+    # row-subset and unquantized forms, FP8 weight groups
+    "linear_rows_gather_slip": ("memcpy(Xs + esz * (size_t)(r * K), (const char *)X + esz * (size_t)(rows[r] * K), esz * (size_t)K);\n    int rc = zqref_prologue(",
+                                "memcpy(Xs + esz * (size_t)(r * K), (const char *)X + esz * (size_t)(r * K), esz * (size_t)K);\n    int rc = zqref_prologue("),
+    "fp8_group_stride": ("s[g] = pow2_quantize(W + g * G * K, G * K, q + g * G * K);",
+                         "s[g] = pow2_quantize(W + g * K, G * K, q + g * G * K);"),
+    "float_layer_bias_dropped": ("                if (bias)\n                    v += (double)bias[n];\n                if (act == ACT_GELU)\n                    v = gelu64(v);\n                Y_out[r * N + n] = v;",
+                                 "                if (act == ACT_GELU)\n                    v = gelu64(v);\n                Y_out[r * N + n] = v;"),
+    "float_layer_transposed_w": ("v += (double)Y[r * K + k] * (double)W[n * K + k];",
+                                 "v += (double)Y[r * K + k] * (double)W[k * N + n];"),
     "group_absmax_first_row": ("s_w[g] = absmax_quantize(W + g * G * K, G * K, Wq + g * G * K);",
                                "{ s_w[g] = absmax_quantize(W + g * G * K, K, Wq + g * G * K);\n"
                                "        for (int64_t i = K; i < G * K; i++) {\n"

@@ -618,6 +618,104 @@ def pin_decomp_rows_subset():
     assert np.array_equal(Yr.view(np.uint16), Yd[rows].view(np.uint16))
 
 
+
+# --------------------------------------------------------------------------
+# The row-subset and unquantized forms used as references for the full-size
+# workloads ("探秘Transformer系列之（36）" 1.2.2: every token is quantized with
+# its own scale, so a token's output depends on that token's row alone)
+# --------------------------------------------------------------------------
+
+def pin_linear_rows_is_subset_of_linear():
+    """linear_rows(rows) equals the listed rows of linear() bit for bit, for
+    fp16 and fp32 X, LayerNorm (with an affine) and GeLU, rows listed out of
+    order and with a repeat."""
+    rng = np.random.default_rng(60)
+    M, K, N, G = 11, 48, 12, 4
+    rows = np.array([7, 0, 10, 3, 7, 5])
+    for x_dtype in (np.float16, np.float32):
+        X = (rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))).astype(x_dtype)
+        W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+        bias = (0.01 * rng.standard_normal(N)).astype(np.float32)
+        gamma = (1 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+        beta = (0.1 * rng.standard_normal(K)).astype(np.float32)
+        Wq, s_w = ref.quantize_groups(W, G)
+        for pre, act, g, b in ((ref.PRE_LAYERNORM, ref.ACT_NONE, gamma, beta),
+                               (ref.PRE_GELU, ref.ACT_GELU, None, None),
+                               (ref.PRE_NONE, ref.ACT_GELU, None, None)):
+            Y, q, s = ref.linear(X, pre, g, b, 1e-5, Wq, s_w, G, bias, act)
+            Yr, qr, sr = ref.linear_rows(X, pre, g, b, 1e-5, Wq, s_w, G, bias, act, rows)
+            assert np.array_equal(qr, q[rows]) and np.array_equal(sr, s[rows]), (x_dtype, pre)
+            assert np.array_equal(Yr.view(np.uint16), Y[rows].view(np.uint16)), (x_dtype, pre)
+
+
+def pin_linear_float_rows_is_plain_matmul():
+    """The unquantized layer equals preop(X)[rows] W^T + b (+ erf GeLU)
+    written with numpy's float64 matmul and scipy's erf, to 1e-12 of the sum
+    of the terms' magnitudes."""
+    from scipy.special import erf
+    rng = np.random.default_rng(61)
+    M, K, N = 9, 64, 10
+    X = (rng.standard_normal((M, K)) * 3).astype(np.float16)
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    bias = (0.5 * rng.standard_normal(N)).astype(np.float32)
+    rows = np.array([8, 2, 4])
+    for pre, act in ((ref.PRE_LAYERNORM, ref.ACT_NONE), (ref.PRE_GELU, ref.ACT_GELU)):
+        got = ref.linear_float_rows(X, pre, None, None, 1e-5, W, bias, act, rows)
+        y = ref.preop(X, pre)[rows].astype(np.float64)
+        v = y @ W.astype(np.float64).T + bias.astype(np.float64)
+        mag = np.abs(y) @ np.abs(W.astype(np.float64)).T + np.abs(bias)
+        if act == ref.ACT_GELU:
+            v = 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+        assert np.all(np.abs(got - v) <= 1e-12 * mag), pre
+    # without a bias the output changes by exactly the bias
+    nob = ref.linear_float_rows(X, ref.PRE_LAYERNORM, None, None, 1e-5, W, None, ref.ACT_NONE, rows)
+    wib = ref.linear_float_rows(X, ref.PRE_LAYERNORM, None, None, 1e-5, W, bias, ref.ACT_NONE, rows)
+    np.testing.assert_allclose(wib - nob, np.broadcast_to(bias.astype(np.float64), nob.shape),
+                               rtol=0, atol=1e-12)
+
+
+def pin_fp8_group_special_cases():
+    """FP8 group codes: G = N is one power-of-two scale over the whole tensor
+    (the per-row quantizer applied to the flattened tensor), G = 1 is the
+    per-row quantizer on each row, and an intermediate G takes each block of
+    G consecutive rows on its own ("探秘Transformer系列之（36）" 1.3 granularity)."""
+    rng = np.random.default_rng(62)
+    N, K = 12, 40
+    W = (0.02 * rng.standard_normal((N, K)) * np.exp(2 * rng.standard_normal((N, 1)))).astype(np.float32)
+    q, s = ref.quantize_groups_fp8(W, N)
+    qt, st = ref.quantize_rows_fp8(W.reshape(1, N * K))
+    assert np.array_equal(q.ravel(), qt.ravel()) and s[0] == st[0]
+    q, s = ref.quantize_groups_fp8(W, 1)
+    qr, sr = ref.quantize_rows_fp8(W)
+    assert np.array_equal(q, qr) and np.array_equal(s, sr)
+    q, s = ref.quantize_groups_fp8(W, 4)
+    for g in range(3):
+        qg, sg = ref.quantize_rows_fp8(W[4 * g:4 * g + 4].reshape(1, 4 * K))
+        assert np.array_equal(q[4 * g:4 * g + 4].ravel(), qg.ravel()) and s[g] == sg[0], g
+
+
+def pin_smoothquant_identity_fp32():
+    """The SmoothQuant identity (X diag(s)^-1)(diag(s) W) = X W holds to 1e-5
+    relative (max norm) with both products taken in fp32 ("SmoothQuant技术解析"
+    2.2), on the oracle's fp32 factors and folded weights."""
+    rng = np.random.default_rng(63)
+    M, K, N = 64, 256, 96
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    X[:, [3, 100, 201]] *= np.float32(100.0)
+    X = X.astype(np.float16)
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    s = ref.smooth_factors(X, W)
+    Xt = ref.preop(X, ref.PRE_LAYERNORM)
+    Xh = (Xt / s).astype(np.float32)
+    Wh = ref.fold_weights(W, s)
+    Y0 = np.matmul(Xt, W.T, dtype=np.float32)
+    Y1 = np.matmul(Xh, Wh.T, dtype=np.float32)
+    assert Y0.dtype == np.float32 and Y1.dtype == np.float32
+    assert np.max(np.abs(Y1 - Y0)) <= 1e-5 * np.max(np.abs(Y0))
+    # a wrong fold (W divided instead of multiplied) is far outside it
+    bad = np.matmul(Xh, (W / s).astype(np.float32).T, dtype=np.float32)
+    assert np.max(np.abs(bad - Y0)) > 1e-2 * np.max(np.abs(Y0))
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
