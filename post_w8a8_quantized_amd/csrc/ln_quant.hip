@@ -176,14 +176,21 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
         }
     }
 
-    if (pre == 1) {  // LayerNorm: mean, then biased variance about the mean
+    if (pre == 1) {
+        // LayerNorm: the mean, taken about the row's first element x0 (so a
+        // row of equal values gets its value back exactly and y = beta), then
+        // the biased variance about the mean.
+        const float x0 = live ? (float)xrow[0] : 0.0f;
         float s = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NCH; i++)
+        for (int i = 0; i < NCH; i++) {
+            if (t + TT * i < nchunks) {
 #pragma unroll
-            for (int e = 0; e < 8; e++)
-                s += y[i][e];
-        const float mean = token_reduce(s, false) / (float)K;
+                for (int e = 0; e < 8; e++)
+                    s += y[i][e] - x0;
+            }
+        }
+        const float mean = x0 + token_reduce(s, false) / (float)K;
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < NCH; i++) {
@@ -195,7 +202,9 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
                 }
             }
         }
-        const float rstd = 1.0f / sqrtf(token_reduce(ss, false) / (float)K + eps);
+        // 1 / sqrt(var + eps) once per token in fp64, rounded once to fp32.
+        const float rstd =
+            (float)(1.0 / sqrt((double)(token_reduce(ss, false) / (float)K) + (double)eps));
 #pragma unroll
         for (int i = 0; i < NCH; i++) {
             const int c = t + TT * i;
@@ -214,10 +223,8 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
                     for (int e = 0; e < 8; e++) b[e] = 0.0f;
                 }
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const float a = rstd * g[e];          // y = (x - mean) * rstd * g + b
-                    y[i][e] = fmaf(y[i][e], a, fmaf(-mean, a, b[e]));
-                }
+                for (int e = 0; e < 8; e++)               // y = (x - mean) * rstd * g + b
+                    y[i][e] = fmaf(y[i][e] - mean, rstd * g[e], b[e]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; e++)
@@ -448,6 +455,8 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
 
     float a, mean = 0.0f, rstd = 0.0f;
     if constexpr (PRE == 1) {
+        // Mean about the row's first element (exact for a row of equal values).
+        const float x0 = (float)xrow[0];
         float s = 0.0f;
 #pragma unroll 4
         for (int c = threadIdx.x; c < nch; c += kSegThreads) {
@@ -455,9 +464,9 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
             Chunk<T>::load(xrow + (int64_t)c * 8, v);
 #pragma unroll
             for (int e = 0; e < 8; e++)
-                s += v[e];
+                s += v[e] - x0;
         }
-        mean = block_reduce<false>(s, red) / (float)K;
+        mean = x0 + block_reduce<false>(s, red) / (float)K;
         float ss = 0.0f;
 #pragma unroll 4
         for (int c = threadIdx.x; c < nch; c += kSegThreads) {
@@ -469,7 +478,7 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
                 ss += d * d;
             }
         }
-        rstd = 1.0f / sqrtf(block_reduce<false>(ss, red) / (float)K + eps);
+        rstd = (float)(1.0 / sqrt((double)(block_reduce<false>(ss, red) / (float)K) + (double)eps));
         float amax = 0.0f;
 #pragma unroll 2
         for (int c = threadIdx.x; c < nch; c += kSegThreads) {
@@ -488,10 +497,8 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
                 for (int e = 0; e < 8; e++) b[e] = 0.0f;
             }
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const float ga = rstd * g[e];
-                amax = fmaxf(amax, fabsf(fmaf(v[e], ga, fmaf(-mean, ga, b[e]))));
-            }
+            for (int e = 0; e < 8; e++)
+                amax = fmaxf(amax, fabsf(fmaf(v[e] - mean, rstd * g[e], b[e])));
         }
         a = block_reduce<true>(amax, red);
     } else {
@@ -563,10 +570,8 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_quant(
                 for (int e = 0; e < 8; e++) b[e] = 0.0f;
             }
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const float ga = rstd * g[e];
-                y[e] = fmaf(mine[e], ga, fmaf(-mean, ga, b[e]));
-            }
+            for (int e = 0; e < 8; e++)
+                y[e] = fmaf(mine[e] - mean, rstd * g[e], b[e]);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; e++)
@@ -690,6 +695,8 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_decomp(
 
     float a = 0.0f, mean = 0.0f, rstd = 0.0f;
     if constexpr (PRE == 1) {
+        // Mean about the row's first element (exact for a row of equal values).
+        const float x0 = (float)xrow[0];
         float s = 0.0f;
 #pragma unroll 4
         for (int c = threadIdx.x; c < nch; c += kSegThreads) {
@@ -697,9 +704,9 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_decomp(
             Chunk<T>::load(xrow + (int64_t)c * 8, v);
 #pragma unroll
             for (int e = 0; e < 8; e++)
-                s += v[e];
+                s += v[e] - x0;
         }
-        mean = block_reduce<false>(s, red) / (float)K;
+        mean = x0 + block_reduce<false>(s, red) / (float)K;
         float ss = 0.0f;
 #pragma unroll 4
         for (int c = threadIdx.x; c < nch; c += kSegThreads) {
@@ -711,7 +718,7 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_decomp(
                 ss += d * d;
             }
         }
-        rstd = 1.0f / sqrtf(block_reduce<false>(ss, red) / (float)K + eps);
+        rstd = (float)(1.0 / sqrt((double)(block_reduce<false>(ss, red) / (float)K) + (double)eps));
         float amax = 0.0f;
 #pragma unroll 2
         for (int c = threadIdx.x; c < nch; c += kSegThreads) {
@@ -722,8 +729,7 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_decomp(
             load_affine(c, g, b);
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                const float ga = rstd * g[e];
-                const float y = fmaf(v[e], ga, fmaf(-mean, ga, b[e]));
+                const float y = fmaf(v[e] - mean, rstd * g[e], b[e]);
                 if (sl[e] < 0)
                     amax = fmaxf(amax, fabsf(y));
             }
@@ -800,10 +806,8 @@ __global__ __launch_bounds__(kSegThreads) void k_rowseg_decomp(
             float g[8], b[8];
             load_affine(own, g, b);
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const float ga = rstd * g[e];
-                y[e] = fmaf(mine[e], ga, fmaf(-mean, ga, b[e]));
-            }
+            for (int e = 0; e < 8; e++)
+                y[e] = fmaf(mine[e] - mean, rstd * g[e], b[e]);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; e++)

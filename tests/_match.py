@@ -1,12 +1,12 @@
 """Matching rules between the HIP path and the CPU oracle.
 
 - int32 accumulators, weight codes and weight scales: bit-exact.
-- Activation codes: |diff| <= 1 everywhere and |diff| == 1 on at most 1e-4 of
-  the elements (at least one element is allowed at small sizes: a single
-  near-tie flip is the case the rule permits).  LayerNorm reductions run in a
-  different order (fp32 on the GPU, fp64 in the oracle), so a value that
-  lands within rounding of a half-integer may round either way.
-- Per-token scales: within 8 fp32 ulps.
+- Activation codes: |diff| <= 1 everywhere and |diff| == 1 on at most
+  floor(1e-4 n) of the n elements (none at all below 10^4 elements).
+  LayerNorm reductions run in a different order (fp32 on the GPU, fp64 in
+  the oracle), so a value that lands within rounding of a half-integer may
+  round either way; nothing else may differ.
+- Per-token scales: within 4 fp32 ulps.
 - fp16 outputs: max |dY| <= 1e-2 * max |Y_ref| and normwise mean relative
   error sum |dY| / sum |Y_ref| <= 1e-3.
 """
@@ -31,17 +31,22 @@ def assert_codes(got: np.ndarray, want: np.ndarray, what: str = "codes", exact: 
         return 0
     assert d.max(initial=0) <= 1, f"{what}: max code difference {d.max()}"
     flips = int((d == 1).sum())
-    allowed = max(1, int(1e-4 * d.size))
+    allowed = int(1e-4 * d.size)
+    if flips:
+        say(f"{what}: {flips} +-1 flips of {d.size} ({allowed} allowed)")
     assert flips <= allowed, f"{what}: {flips} +-1 flips > {allowed} allowed of {d.size}"
     return flips
 
 
-def assert_scales(got: np.ndarray, want: np.ndarray, what: str = "scales", ulps: int = 8):
+def assert_scales(got: np.ndarray, want: np.ndarray, what: str = "scales", ulps: int = 4):
     got = np.asarray(got, dtype=np.float32)
     want = np.asarray(want, dtype=np.float32)
     tol = ulps * np.spacing(np.abs(want))
     d = np.abs(got.astype(np.float64) - want.astype(np.float64))
-    assert np.all(d <= tol), f"{what}: max diff {(d / np.maximum(np.spacing(np.abs(want)), 1e-45)).max():.1f} ulps"
+    worst = (d / np.maximum(np.spacing(np.abs(want)), 1e-45)).max(initial=0.0)
+    if worst > 1:
+        say(f"{what}: worst scale {worst:.1f} ulps")
+    assert np.all(d <= tol), f"{what}: max diff {worst:.1f} ulps"
 
 
 def y_errors(got: np.ndarray, want: np.ndarray):

@@ -73,14 +73,37 @@ def test_unfused_layer(zq, M, K, N, pre, dt, act, affine):
                                     act, workspace=ws))
     y16, q, s, acc = split_ws(ws, M, N, K)
 
-    # (1) the op's fp16 tensor: the oracle's op rounded to fp16, within one fp16 ulp
-    y_ref = ref.round_to_f16(ref.preop(X, pre, g, b, 1e-5)).astype(np.float16)
-    ulp = np.spacing(np.abs(y_ref)).astype(np.float64)
-    assert np.all(np.abs(y16.astype(np.float64) - y_ref.astype(np.float64)) <= ulp)
-    # (2) the quantizer on that tensor
+    # (1) the op's fp16 tensor: the oracle's op rounded to fp16.  The two sides'
+    # fp32 values differ by rounding order only: the GPU's y carries a few fp32
+    # roundings of its own inputs (x - mean, rstd * gamma, + beta), so its error
+    # is a few ulps of the element plus a few ulps of the row's largest |y| (an
+    # element near 0 after cancellation).  An element may therefore round to the
+    # other fp16 neighbour only where the oracle's value sits that close to the
+    # midpoint between the two (a near-tie: both roundings are correct).
+    y32 = ref.preop(X, pre, g, b, 1e-5)
+    y_ref = ref.round_to_f16(y32).astype(np.float16)
+    a, r = y16.astype(np.float64), y_ref.astype(np.float64)
+    off = a != r
+    if off.any():
+        step = np.maximum(np.spacing(np.abs(y16[off])), np.spacing(np.abs(y_ref[off])))
+        assert np.all(np.abs(a[off] - r[off]) <= step.astype(np.float64))
+        mid = (a[off] + r[off]) / 2
+        dist = np.abs(y32[off].astype(np.float64) - mid)
+        rowmax = np.broadcast_to(np.abs(y32).max(axis=1, keepdims=True), y32.shape)[off]
+        near = 8 * np.spacing(np.abs(y32[off])).astype(np.float64) + 2.0 ** -21 * rowmax
+        say(f"unfused fp16 tensor: {int(off.sum())} near-tie roundings of {off.size}, "
+            f"largest distance {np.max(dist / near):.3f} of the allowance")
+        assert np.all(dist <= near)
+    # (2) the quantizer on that tensor: the oracle's quantizer fed the GPU's own
+    # fp16 tensor gives the same codes and scales bit for bit; where the two
+    # tensors agree the whole unfused prologue agrees exactly
+    q_own, s_own = ref.quantize_rows(y16.astype(np.float32))
+    assert_codes(q, q_own, exact=True)
+    assert np.array_equal(s, s_own)
     q_ref, s_ref = ref.unfused_prologue(X, pre, g, b, 1e-5)
-    assert_codes(q, q_ref)
-    assert_scales(s, s_ref)
+    same = ~off.any(axis=1)
+    assert_codes(q[same], q_ref[same], exact=True)
+    assert np.array_equal(s[same], s_ref[same])
     # (3) exact accumulators of the GPU's own codes
     assert np.array_equal(acc, ref.gemm_i32(q, Wq))
     # (4) the dequantized output: the fused epilogue's bits for the same codes ...
