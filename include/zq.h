@@ -37,6 +37,10 @@
  *     error nothing is enqueued and a non-zero zq_status is returned.  A
  *     launch failure reported by the HIP runtime returns ZQ_ERR_HIP.  Faults
  *     during execution surface at the caller's next synchronisation.
+ *   - An error already pending on the calling thread when a call starts (left
+ *     by the caller's earlier HIP work, as hipPeekAtLastError shows it) makes
+ *     the call return ZQ_ERR_HIP before enqueueing anything; the error is left
+ *     pending for the caller to read, never cleared by the library.
  *   - Calls never abort and never throw.  The library keeps no mutable global
  *     state: calls are reentrant; calls on different streams that write the
  *     same buffers race, as any two kernels would.
@@ -154,7 +158,9 @@ zq_status zq_ln_quant_per_token(const void *X, zq_dtype x_dtype, int64_t M, int6
  *   the raw int32 accumulators and x_scales, w_scales, bias and act are
  *   ignored (they may be NULL).
  * Requires M, N >= 1, 1 <= K <= ZQ_MAX_K, K % 16 == 0, G >= 1, N % G == 0,
- * N % 4 == 0.
+ * N % 4 == 0 (outputs leave in whole 8-byte fp16 / 16-byte int32 pieces of
+ * four columns; with G a multiple of 4, as every group size the pages give
+ * is, N % G == 0 implies it).  Every call that runs this GEMM shares the rule.
  */
 zq_status zq_w8a8_gemm_dequant(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
                                const float *w_scales, int64_t group_rows, const float *bias,

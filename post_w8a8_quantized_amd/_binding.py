@@ -149,6 +149,21 @@ def _need(t: torch.Tensor, name: str, dtypes, shape=None, device=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _need_ws(ws: torch.Tensor, need: int, device):
+    """A caller-provided workspace: a contiguous GPU tensor on `device` holding
+    at least `need` bytes (the C ABI sees only a pointer and a byte count, so a
+    host tensor or a short buffer has to be caught here)."""
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if ws.device.type != "cuda" or ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    have = ws.numel() * ws.element_size()
+    if have < need:
+        raise ValueError(f"workspace holds {have} bytes, {need} needed")
+
+
 def _fdtype(t: torch.Tensor) -> int:
     return F16 if t.dtype == torch.float16 else F32
 
@@ -166,6 +181,8 @@ def quantize_weights_grouped(W: torch.Tensor, group_rows: int, smooth: Optional[
         s_w = torch.empty((max(N // group_rows, 1),), dtype=torch.float32, device=W.device)
     else:
         Wq, s_w = out
+        _need(Wq, "Wq", (torch.int8,), (N, K), W.device)
+        _need(s_w, "w_scales", (torch.float32,), (max(N // group_rows, 1),), W.device)
     _call("zq_quantize_weights_grouped", _ptr(W), _fdtype(W), _ptr(smooth), N, K, group_rows,
           _ptr(Wq), _ptr(s_w), _stream(W))
     return Wq, s_w
@@ -184,6 +201,8 @@ def ln_quant_per_token(X: torch.Tensor, pre: int = PRE_LAYERNORM, gamma=None, be
         s_x = torch.empty((M,), dtype=torch.float32, device=X.device)
     else:
         Xq, s_x = out
+        _need(Xq, "Xq", (torch.int8,), (M, K), X.device)
+        _need(s_x, "x_scales", (torch.float32,), (M,), X.device)
     _call("zq_ln_quant_per_token", _ptr(X), _fdtype(X), M, K, pre, _ptr(gamma), _ptr(beta), eps,
           _ptr(Xq), _ptr(s_x), _stream(X))
     return Xq, s_x
@@ -212,6 +231,7 @@ def w8a8_gemm_dequant(Xq: torch.Tensor, x_scales: Optional[torch.Tensor], Wq: to
     if bias is not None:
         _need(bias, "bias", (torch.float32,), (N,), Xq.device)
     Y = torch.empty((M, N), dtype=out_dtype, device=Xq.device) if out is None else out
+    _need(Y, "out", (out_dtype,), (M, N), Xq.device)
     _call("zq_w8a8_gemm_dequant_ex", _ptr(Xq), _ptr(x_scales), _ptr(Wq), _ptr(w_scales),
           group_rows, _ptr(bias), act, M, N, K, _ptr(Y), ydt, path, _stream(Xq))
     return Y
@@ -239,7 +259,9 @@ def linear_w8a8(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor, group
     need = linear_workspace_bytes(M, K)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    _need_ws(workspace, need, X.device)
     Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _need(Y, "out", (torch.float16,), (M, N), X.device)
     _call("zq_linear_w8a8", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps, _ptr(Wq),
           _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(workspace),
           workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
@@ -270,7 +292,9 @@ def linear_w8a8_unfused(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tenso
     need = linear_unfused_workspace_bytes(M, N, K)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    _need_ws(workspace, need, X.device)
     Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _need(Y, "out", (torch.float16,), (M, N), X.device)
     _call("zq_linear_w8a8_unfused", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps,
           _ptr(Wq), _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(workspace),
           workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
@@ -302,7 +326,9 @@ def ffn_w8a8(X: torch.Tensor, W1q: torch.Tensor, w1_scales: torch.Tensor, group_
     need = ffn_workspace_bytes(M, K, F)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    _need_ws(workspace, need, X.device)
     Y = torch.empty((M, K), dtype=torch.float16, device=X.device) if out is None else out
+    _need(Y, "out", (torch.float16,), (M, K), X.device)
     _call("zq_ffn_w8a8", _ptr(X), _fdtype(X), _ptr(gamma), _ptr(beta), eps, _ptr(W1q),
           _ptr(w1_scales), group_rows1, _ptr(bias1), _ptr(W2q), _ptr(w2_scales), group_rows2,
           _ptr(bias2), M, K, F, _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -390,7 +416,9 @@ def linear_w8a8_fp8(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor, g
     need = linear_workspace_bytes(M, K)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    _need_ws(workspace, need, X.device)
     Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _need(Y, "out", (torch.float16,), (M, N), X.device)
     _call("zq_linear_w8a8_fp8_packed" if packed else "zq_linear_w8a8_fp8", _ptr(X), _fdtype(X),
           pre, _ptr(gamma), _ptr(beta), eps, _ptr(Wq), _ptr(w_scales), group_rows, _ptr(bias),
           act, M, N, K, _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(Y),
@@ -443,6 +471,7 @@ def w8a8_gemm_dequant_packed(Xq: torch.Tensor, x_scales: Optional[torch.Tensor],
     if bias is not None:
         _need(bias, "bias", (torch.float32,), (N,), Xq.device)
     Y = torch.empty((M, N), dtype=out_dtype, device=Xq.device) if out is None else out
+    _need(Y, "out", (out_dtype,), (M, N), Xq.device)
     _call("zq_w8a8_gemm_dequant_packed", _ptr(Xq), _ptr(x_scales), _ptr(Wp), _ptr(w_scales),
           group_rows, _ptr(bias), act, M, N, K, _ptr(Y), ydt, _stream(Xq))
     return Y
@@ -465,7 +494,9 @@ def linear_w8a8_packed(X: torch.Tensor, Wp: torch.Tensor, w_scales: torch.Tensor
     need = linear_workspace_bytes(M, K)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    _need_ws(workspace, need, X.device)
     Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _need(Y, "out", (torch.float16,), (M, N), X.device)
     _call("zq_linear_w8a8_packed", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps,
           _ptr(Wp), _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(workspace),
           workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
@@ -602,7 +633,9 @@ def linear_w8a8_decomp(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor
     need = linear_decomp_workspace_bytes(M, K)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    _need_ws(workspace, need, X.device)
     Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _need(Y, "out", (torch.float16,), (M, N), X.device)
     _call("zq_linear_w8a8_decomp", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps, alpha,
           _ptr(Wq), _ptr(w_scales), group_rows, _ptr(W16t), _ptr(bias), act, M, N, K,
           _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))

@@ -30,11 +30,13 @@ zq_status map_hip(hipError_t e)
     return e == hipSuccess ? ZQ_OK : ZQ_ERR_HIP;
 }
 
-// Drop an error left by earlier, unrelated work so that it is not reported
-// as this call's launch failure.
-void clear_stale_error()
+// An error left pending on this thread by earlier HIP work belongs to the
+// caller: the call then returns ZQ_ERR_HIP before enqueueing anything and
+// leaves that error pending (peek, not get), so the caller still reads it,
+// and a launch failure this library reports is always its own.
+bool hip_error_pending()
 {
-    (void)hipGetLastError();
+    return hipPeekAtLastError() != hipSuccess;
 }
 
 bool k_ok(int64_t K)
@@ -131,7 +133,8 @@ ZQ_API zq_status zq_quantize_weights_grouped(const void *W, zq_dtype w_dtype, co
         return ZQ_ERR_SHAPE;
     if (!aligned16(W) || !aligned16(Wq))
         return ZQ_ERR_ALIGN;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return map_hip(zq::launch_quantize_weights(W, w_dtype == ZQ_F16, smooth, N, K, group_rows, Wq,
                                                w_scales, stream));
 }
@@ -143,7 +146,8 @@ ZQ_API zq_status zq_ln_quant_per_token(const void *X, zq_dtype x_dtype, int64_t 
     zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta, Xq, x_scales);
     if (st != ZQ_OK)
         return st;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                        pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                        pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, Xq,
@@ -164,7 +168,8 @@ ZQ_API zq_status zq_w8a8_gemm_dequant_ex(const int8_t *Xq, const float *x_scales
         return ZQ_ERR_DTYPE;
     if (path == ZQ_PATH_SKINNY && M > kSkinnyMaxM)
         return ZQ_ERR_SHAPE;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return gemm_dispatch(Xq, x_scales, Wq, w_scales, group_rows, bias, act, M, N, K, Y, y_dtype,
                          path, stream);
 }
@@ -215,7 +220,8 @@ zq_status linear_impl(const void *X, zq_dtype x_dtype, zq_pre pre, const float *
         return ZQ_ERR_SHAPE;
     if (workspace_bytes < need)
         return ZQ_ERR_WORKSPACE;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     st = map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                      pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                      pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, Xq, x_scales,
@@ -268,7 +274,8 @@ ZQ_API zq_status zq_pack_weights(const int8_t *Wq, int64_t N, int64_t K, int8_t 
         return ZQ_ERR_SHAPE;
     if (!aligned16(Wq) || !aligned16(Wp))
         return ZQ_ERR_ALIGN;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return map_hip(zq::launch_pack_weights(Wq, N, K, Wp, stream));
 }
 
@@ -284,7 +291,8 @@ ZQ_API zq_status zq_w8a8_gemm_dequant_packed(const int8_t *Xq, const float *x_sc
         return st;
     if (M > kSkinnyMaxM)
         return ZQ_ERR_SHAPE;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return map_hip(zq::launch_gemm_skinny_packed(Xq, x_scales, Wp, w_scales, group_rows, bias,
                                                  (int)act, M, N, K, Y, y_dtype == ZQ_I32,
                                                  stream));
@@ -332,7 +340,8 @@ ZQ_API zq_status zq_linear_w8a8_unfused(const void *X, zq_dtype x_dtype, zq_pre 
         return ZQ_ERR_SHAPE;
     if (workspace_bytes < need)
         return ZQ_ERR_WORKSPACE;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     st = map_hip(zq::launch_ln_to_f16(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                       pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                       pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, y16, stream));
@@ -415,7 +424,8 @@ ZQ_API zq_status zq_ffn_w8a8(const void *X, zq_dtype x_dtype, const float *gamma
         return ZQ_ERR_SHAPE;
     if (workspace_bytes < need)
         return ZQ_ERR_WORKSPACE;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     // FFN-up: LN + quantize ...
     st = map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, ZQ_PRE_LAYERNORM, gamma, beta,
                                      eps, Xq1, sx1, stream));
@@ -458,7 +468,8 @@ ZQ_API zq_status zq_quantize_weights_grouped_fp8(const void *W, zq_dtype w_dtype
         return ZQ_ERR_SHAPE;
     if (!aligned16(W) || !aligned16(Wq8))
         return ZQ_ERR_ALIGN;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return map_hip(zq::launch_quantize_weights(W, w_dtype == ZQ_F16, smooth, N, K, group_rows,
                                                reinterpret_cast<int8_t *>(Wq8), w_scales, stream,
                                                true));
@@ -473,7 +484,8 @@ ZQ_API zq_status zq_ln_quant_per_token_fp8(const void *X, zq_dtype x_dtype, int6
     zq_status st = check_prologue(X, x_dtype, M, K, pre, gamma, beta, Xq, x_scales);
     if (st != ZQ_OK)
         return st;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                        pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                        pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, Xq,
@@ -522,7 +534,8 @@ ZQ_API zq_status zq_fp8_gemm_dequant(const uint8_t *Xq8, const float *x_scales,
                                   y_dtype, bias);
     if (st != ZQ_OK)
         return st;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return fp8_gemm(Xq8, x_scales, Wq8, w_scales, group_rows, bias, act, M, N, K, Y, y_dtype,
                     false, stream);
 }
@@ -556,7 +569,8 @@ zq_status linear_fp8_impl(const void *X, zq_dtype x_dtype, zq_pre pre, const flo
         return ZQ_ERR_SHAPE;
     if (workspace_bytes < need)
         return ZQ_ERR_WORKSPACE;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     st = map_hip(zq::launch_ln_quant(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                      pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                      pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps,
@@ -617,7 +631,8 @@ ZQ_API zq_status zq_smoothquant_factors(const void *X, zq_dtype x_dtype, int64_t
         return ZQ_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return ZQ_ERR_ALIGN;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return map_hip(zq::launch_smooth_factors(X, x_dtype == ZQ_F16, M, K, eps, W, w_dtype == ZQ_F16,
                                              N, gamma, beta, smooth, gamma_out, beta_out,
                                              workspace, stream));
@@ -652,7 +667,8 @@ ZQ_API zq_status zq_pack_outlier_weights(const void *W, zq_dtype w_dtype, int64_
         return ZQ_ERR_SHAPE;
     if (!aligned16(W) || !aligned16(W16t))
         return ZQ_ERR_ALIGN;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return map_hip(zq::launch_pack_outlier_weights(W, w_dtype == ZQ_F16, N, K,
                                                    static_cast<_Float16 *>(W16t), stream));
 }
@@ -671,7 +687,8 @@ ZQ_API zq_status zq_outlier_columns(const void *X, zq_dtype x_dtype, int64_t M, 
         return st;
     if (!aligned16(slot))
         return ZQ_ERR_ALIGN;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return map_hip(zq::launch_outlier_columns(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                               pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                               pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps,
@@ -690,7 +707,8 @@ ZQ_API zq_status zq_ln_quant_decomp(const void *X, zq_dtype x_dtype, int64_t M, 
         return st;
     if (!aligned16(slot) || !aligned16(XO))
         return ZQ_ERR_ALIGN;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return map_hip(zq::launch_ln_quant_decomp(X, x_dtype == ZQ_F16, M, K, (int)pre,
                                               pre == ZQ_PRE_LAYERNORM ? gamma : nullptr,
                                               pre == ZQ_PRE_LAYERNORM ? beta : nullptr, eps, slot,
@@ -711,7 +729,8 @@ ZQ_API zq_status zq_w8a8_gemm_decomp(const int8_t *Xq, const float *x_scales, co
         return st;
     if (!aligned16(XO) || !aligned16(W16t))
         return ZQ_ERR_ALIGN;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     return gemm_decomp_dispatch(Xq, x_scales, Wq, w_scales, group_rows, bias, act, M, N, K, cols,
                                 static_cast<const _Float16 *>(XO),
                                 static_cast<const _Float16 *>(W16t), Y, stream);
@@ -768,7 +787,8 @@ ZQ_API zq_status zq_linear_w8a8_decomp(const void *X, zq_dtype x_dtype, zq_pre p
         return ZQ_ERR_WORKSPACE;
     const float *g = pre == ZQ_PRE_LAYERNORM ? gamma : nullptr;
     const float *b = pre == ZQ_PRE_LAYERNORM ? beta : nullptr;
-    clear_stale_error();
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
     st = map_hip(zq::launch_outlier_columns(X, x_dtype == ZQ_F16, M, K, (int)pre, g, b, eps, alpha,
                                             slot, cols, stream));
     if (st != ZQ_OK)

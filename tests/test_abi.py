@@ -326,6 +326,28 @@ def test_binding_rejects_cpu_tensors():
         zq.ln_quant_per_token(X)
 
 
+def test_binding_checks_workspace_tensor():
+    """The C ABI sees only a pointer and a byte count, so the binding rejects a
+    workspace on the host, on another device, non-contiguous or too small."""
+    import torch
+    gpu = torch.device("cuda:0")
+    with pytest.raises(ValueError, match="workspace is on cpu"):
+        B._need_ws(torch.zeros(1024, dtype=torch.uint8), 512, gpu)
+    with pytest.raises(TypeError):
+        B._need_ws(None, 512, gpu)
+    with pytest.raises(ValueError, match="GPU"):
+        B._need(torch.zeros((4, 4), dtype=torch.float16), "out", (torch.float16,), (4, 4))
+
+
+def test_gemm_rejects_n_not_multiple_of_4(L):
+    """N % 4 == 0 (outputs are written four columns at a time), for every call
+    that runs the GEMM, in test mode too."""
+    assert gemm(L, N=250, G=2) == SHAPE
+    assert gemm(L, N=250, G=2, ydt=3, sx=None, sw=None) == SHAPE
+    assert gemm(L, N=6, G=1) == SHAPE
+    assert linear(L, N=250, G=2) == SHAPE
+
+
 def test_missing_library_raises(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "_LIB_PATH", str(tmp_path / "absent.so"))
