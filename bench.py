@@ -10,14 +10,20 @@ prescribes.  Inputs are seeded synthetic data resident in HBM; several
 independent input/weight/output sets are rotated so that the 256 MB
 Infinity Cache cannot serve a step from the previous one.
 
+The headline workload (default: the largest, X fp16 [4096 x 5120] with 0.5%
+outlier channels, SmoothQuant fold, W [13824 x 5120]) is timed with every
+leg: the dominant kernel's roofline, the fusion ablation, the FP8 variant and
+the CPU oracle on the host cores.  The other workloads (BERT FFN-up, GPT QKV,
+decode FFN-down) follow as extra keys, each with its layer time, fraction of
+peak and its dominant kernel's roofline, and the outlier workload is timed
+again under the mixed-precision decomposition.
+
 The steps are captured in a HIP graph (on torch's stream, which is the
 stream the library launches on) so that host-side call overhead does not
-leave the GPU idle between the ~10 us layers; the timed region is one replay
-of a graph of exactly K steps, bracketed by device synchronisations.
+leave the GPU idle between layers; the timed region is one replay of a graph
+of exactly K steps, bracketed by device synchronisations.
 
-Printed: ONE JSON line with the throughput (TOPS for prefill workloads, GB/s
-for the decode workload), the dominant kernel's roofline figures measured
-with HIP events, and the CPU oracle timed on the host cores.
+Printed: ONE JSON line.
 """
 from __future__ import annotations
 
@@ -45,7 +51,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--workload", default="bert_ffn_up")
+    ap.add_argument("--workload", default="outlier_smooth",
+                    help="the headline workload (default: the largest, the outlier layer "
+                         "with the SmoothQuant fold)")
     ap.add_argument("--rotate-mb", type=float, default=600.0,
                     help="total bytes of the rotated input sets (beyond the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -58,6 +66,8 @@ def parse():
                          "mixed-precision decomposition)")
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip the chained FFN block timing (bert_ffn_up)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other workloads (BERT FFN-up, GPT QKV, decode FFN-down)")
     ap.add_argument("--no-copy-reference", action="store_true",
                     help="skip the 1 GiB device-copy bandwidth reference")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -245,38 +255,16 @@ def outlier_leg(torch, zq, w, make_inputs, args, dev):
     return out
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: the library has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr, flush=True)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    import post_w8a8_quantized_amd as zq
-    from zq_workloads import WORKLOADS, make_inputs
-
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    zq.library()
-    if args.calib_copy_mb > 0:
-        calib_copy(torch, args.calib_copy_mb)
-        return
-
-    w = WORKLOADS[args.workload]
-    decode = w.M <= 32
+def prepare(torch, zq, w, make_inputs, args, dev):
+    """Offline steps (untimed) and the rotated input sets of one workload."""
     inp = make_inputs(w)
-    dev = torch.device("cuda:0")
+    decode = w.M <= 32
     Xd = torch.from_numpy(inp.X).to(dev)
     Wd = torch.from_numpy(inp.W).to(dev)
     gamma = torch.from_numpy(inp.gamma).to(dev)
     beta = torch.from_numpy(inp.beta).to(dev)
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
-
-    # ---- offline (untimed): SmoothQuant fold and group-wise weight quantization
+    # ---- offline: SmoothQuant fold and group-wise weight quantization
     smooth = None
     if w.smooth:
         smooth, gamma, beta = zq.smoothquant_factors(Xd, Wd, w.eps, gamma, beta)
@@ -287,10 +275,6 @@ def main():
         # offline into the packed blocks the weight-streaming kernel reads.
         Wq = zq.pack_weights(Wq)
     torch.cuda.synchronize()
-    g_arg = gamma if w.pre == zq.PRE_LAYERNORM else None
-    b_arg = beta if w.pre == zq.PRE_LAYERNORM else None
-
-    # ---- rotated sets
     M, N, K, G = w.M, w.N, w.K, w.group_rows
     ws_bytes = zq.linear_workspace_bytes(M, K)
     x_el = 2 if w.x_dtype == "f16" else 4
@@ -305,6 +289,20 @@ def main():
             ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
             Y=torch.empty((M, N), dtype=torch.float16, device=dev),
         ))
+    return dict(w=w, inp=inp, decode=decode, gamma=gamma, beta=beta, bias=bias, smooth=smooth,
+                g_arg=gamma if w.pre == zq.PRE_LAYERNORM else None,
+                b_arg=beta if w.pre == zq.PRE_LAYERNORM else None,
+                sets=sets, nsets=nsets, x_el=x_el)
+
+
+def time_layer(torch, zq, st, args):
+    """HIP-event times of the prologue alone, the GEMM alone (graphs of K launches
+    each) and of K whole layer steps (one replay of a K-step graph after the
+    warmup replays), plus the dominant kernel's roofline."""
+    import numpy as np
+    w, sets, nsets, decode = st["w"], st["sets"], st["nsets"], st["decode"]
+    M, N, K, G = w.M, w.N, w.K, w.group_rows
+    g_arg, b_arg, bias = st["g_arg"], st["b_arg"], st["bias"]
     xq_off = 0
     sx_off = (M * K + 255) // 256 * 256
 
@@ -336,170 +334,292 @@ def main():
     for i in range(nsets):
         layer(i)
     torch.cuda.synchronize()
-
-    # ---- per-kernel averages over graphs of the same launches (HIP events).  They run
-    # first: their ~20 ms of work also brings the GPU to the steady state a sustained
-    # run sees (a cold GPU runs the first ~10 ms of steps ~10% slower).
+    # per-kernel averages over graphs of the same launches (HIP events).  They run
+    # first: their work also brings the GPU to the steady state a sustained run sees.
     g_pro = graph_of(torch, prologue, args.steps)
     g_gemm = graph_of(torch, gemm, args.steps)
     time_graph(torch, g_pro)
     time_graph(torch, g_gemm)
     pro_ms = time_graph(torch, g_pro)[0] / args.steps
     gemm_ms = time_graph(torch, g_gemm)[0] / args.steps
-
-    # ---- timed layer steps: the W warmup steps are replays of the same K-step graph
+    # timed layer steps: the W warmup steps are replays of the same K-step graph
     # (ceil(W / K) of them), so the timed replay runs a graph that has already been
-    # launched once: a graph's first replay carries one-time costs (~10% of a
-    # 400-step replay here) that a sustained run never pays again.
+    # launched once (a graph's first replay carries one-time costs).
     g_steps = graph_of(torch, layer, args.steps)
     warm_replays = -(-args.warmup // args.steps)
     for _ in range(warm_replays):
         time_graph(torch, g_steps)
-    warmup_steps = warm_replays * args.steps
     ms_ev, ms_wall = time_graph(torch, g_steps)
     ms_step = ms_ev / args.steps
-    # Spread: further replays of the same K-step graph (outside the timed region).
     reps = np.array([ms_step] + [time_graph(torch, g_steps)[0] / args.steps for _ in range(9)])
     p10, p50, p90 = np.percentile(reps * 1e3, [10, 50, 90])
-    spread = {"replays": int(reps.size), "p10_us": round(float(p10), 3),
-              "p50_us": round(float(p50), 3), "p90_us": round(float(p90), 3)}
     del g_steps, g_pro, g_gemm
     torch.cuda.synchronize()
 
-    # ---- fusion ablation (prefill shapes): the same layer in the unfused order
-    # (op -> fp16 -> quantizer -> int32 GEMM -> dequantizer), same rotated sets;
-    # the intermediates share one workspace.
-    ablation = None
-    if not decode and not args.no_ablation:
-        ws_unf = torch.empty(zq.linear_unfused_workspace_bytes(M, N, K), dtype=torch.uint8,
-                             device=dev)
-
-        def layer_unfused(i):
-            s = sets[i % nsets]
-            zq.linear_w8a8_unfused(s["X"], s["Wq"], s["s_w"], G, w.pre, g_arg, b_arg, w.eps,
-                                   bias, w.act, workspace=ws_unf, out=s["Y"])
-
-        for i in range(nsets):
-            layer_unfused(i)
-        g_unf = graph_of(torch, layer_unfused, args.steps)
-        time_graph(torch, g_unf)
-        unf_ms = time_graph(torch, g_unf)[0] / args.steps
-        del g_unf, ws_unf
-        torch.cuda.synchronize()
-        ablation = {"unfused_layer_step_us": round(unf_ms * 1e3, 3),
-                    "fused_layer_step_us": round(ms_step * 1e3, 3),
-                    "fusion_speedup": round(unf_ms / ms_step, 3),
-                    "unfused_order": "op->fp16, quantize, int8 GEMM->int32, dequantize"}
-
     ops = 2.0 * M * N * K
-    bytes_pro = M * K * x_el + M * K + 4 * M
-    bytes_gemm = M * K + 4 * M + N * K + 4 * (N // G) + (4 * N if bias is not None else 0) + 2 * M * N
+    bytes_pro = M * K * st["x_el"] + M * K + 4 * M
+    bytes_gemm = (M * K + 4 * M + N * K + 4 * (N // G) + (4 * N if bias is not None else 0)
+                  + 2 * M * N)
     bytes_layer = bytes_pro + bytes_gemm
     gemm_kernel = "gemm_skinny" if decode else "gemm_tiled"
     src_hash = kernel_source_hash([f"{gemm_kernel}.hip", "zq_device.h"])
     traffic = read_traffic(gemm_kernel, w.name, src_hash)
-
     if decode:
-        value = bytes_layer / (ms_step * 1e-3) / 1e9
-        unit = "GB/s"
+        value, unit, peak = bytes_layer / (ms_step * 1e-3) / 1e9, "GB/s", PEAK_HBM_GBS
         g_ach = bytes_gemm / (gemm_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(g_ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(g_ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+        roofline = {"bound": "hbm", "achieved": round(g_ach, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(g_ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                     "kernel": gemm_kernel, "avg_launch_us": round(gemm_ms * 1e3, 3),
                     "algorithmic_bytes_per_launch": bytes_gemm}
     else:
-        value = ops / (ms_step * 1e-3) / 1e12
-        unit = "TOPS"
+        value, unit, peak = ops / (ms_step * 1e-3) / 1e12, "TOPS", PEAK_INT8_TOPS
         g_ach = ops / (gemm_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(g_ach, 1), "peak": PEAK_INT8_TOPS,
                     "unit": "TOP/s", "frac": round(g_ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
                     "kernel": gemm_kernel, "avg_launch_us": round(gemm_ms * 1e3, 3),
                     "algorithmic_ops_per_launch": ops, "algorithmic_bytes_per_launch": bytes_gemm}
     # counted HBM bytes over the bytes the kernel must move (re-reads, partial lines)
-    roofline["traffic_over_algorithmic"] = (round(traffic / bytes_gemm, 3) if traffic
-                                            else None)
+    roofline["traffic_over_algorithmic"] = (round(traffic / bytes_gemm, 3) if traffic else None)
+    return dict(ms_step=ms_step, ms_wall=ms_wall, pro_ms=pro_ms, gemm_ms=gemm_ms, value=value,
+                nsets=nsets,
+                unit=unit, peak=peak, ops=ops, bytes_pro=bytes_pro, bytes_gemm=bytes_gemm,
+                bytes_layer=bytes_layer, roofline=roofline,
+                spread={"replays": int(reps.size), "p10_us": round(float(p10), 3),
+                        "p50_us": round(float(p50), 3), "p90_us": round(float(p90), 3)})
 
-    # ---- chained FFN block (BERT FFN-up shape): FFN-up then FFN-down (W2 [K x N] drawn
-    # like W), as one zq_ffn_w8a8 call against two zq_linear_w8a8 calls
+
+def fp8_leg(torch, zq, st, t, args, dev):
+    """The FP8 variant of the same layer (E4M3 codes, power-of-two scales), weights
+    quantized offline (and packed at decode shapes), same rotated inputs."""
+    w, sets, nsets, decode = st["w"], st["sets"], st["nsets"], st["decode"]
+    M, N, G = w.M, w.N, w.group_rows
+    Wd8 = torch.from_numpy(st["inp"].W).to(dev)
+    W8, s_w8 = zq.quantize_weights_grouped_fp8(Wd8, G, st["smooth"])
+    del Wd8
+    if decode:
+        W8 = zq.pack_weights(W8)
+    W8s = [W8] + [W8.clone() for _ in range(nsets - 1)]   # rotated like the int8 weights
+    Y8 = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+    def layer_fp8(i):
+        s = sets[i % nsets]
+        zq.linear_w8a8_fp8(s["X"], W8s[i % nsets], s_w8, G, w.pre, st["g_arg"], st["b_arg"],
+                           w.eps, st["bias"], w.act, workspace=s["ws"], out=Y8, N=N,
+                           packed=decode)
+
+    for i in range(nsets):
+        layer_fp8(i)
+    g8 = graph_of(torch, layer_fp8, args.steps)
+    time_graph(torch, g8)
+    ms8 = time_graph(torch, g8)[0] / args.steps
+    del g8, W8, W8s, Y8
+    torch.cuda.synchronize()
+    return {"layer_step_us": round(ms8 * 1e3, 3),
+            "value": round((t["bytes_layer"] / (ms8 * 1e-3) / 1e9) if decode
+                           else (t["ops"] / (ms8 * 1e-3) / 1e12), 2),
+            "unit": "GB/s" if decode else "TOPS"}
+
+
+def ablation_leg(torch, zq, st, t, args, dev):
+    """The same layer in the unfused order (op -> fp16 -> quantizer -> int32 GEMM
+    -> dequantizer), same rotated sets; the intermediates share one workspace."""
+    w, sets, nsets = st["w"], st["sets"], st["nsets"]
+    M, N, K, G = w.M, w.N, w.K, w.group_rows
+    ws_unf = torch.empty(zq.linear_unfused_workspace_bytes(M, N, K), dtype=torch.uint8,
+                         device=dev)
+
+    def layer_unfused(i):
+        s = sets[i % nsets]
+        zq.linear_w8a8_unfused(s["X"], s["Wq"], s["s_w"], G, w.pre, st["g_arg"], st["b_arg"],
+                               w.eps, st["bias"], w.act, workspace=ws_unf, out=s["Y"])
+
+    for i in range(nsets):
+        layer_unfused(i)
+    g_unf = graph_of(torch, layer_unfused, args.steps)
+    time_graph(torch, g_unf)
+    unf_ms = time_graph(torch, g_unf)[0] / args.steps
+    del g_unf, ws_unf
+    torch.cuda.synchronize()
+    return {"unfused_layer_step_us": round(unf_ms * 1e3, 3),
+            "fused_layer_step_us": round(t["ms_step"] * 1e3, 3),
+            "fusion_speedup": round(unf_ms / t["ms_step"], 3),
+            "unfused_order": "op->fp16, quantize, int8 GEMM->int32, dequantize"}
+
+
+def ffn_leg(torch, zq, st, args, dev):
+    """Chained FFN block at the BERT FFN-up shape: FFN-up then FFN-down (W2 [K x N]
+    drawn like W), as one zq_ffn_w8a8 call against two zq_linear_w8a8 calls, and
+    each half alone."""
+    w, sets, nsets = st["w"], st["sets"], st["nsets"]
+    M, N, K, G = w.M, w.N, w.K, w.group_rows
+    g_arg, b_arg, bias = st["g_arg"], st["b_arg"], st["bias"]
+    g2 = torch.Generator(device="cpu").manual_seed(1)
+    W2 = (0.02 * torch.randn((K, N), generator=g2, dtype=torch.float32)).to(dev)
+    W2q, s_w2 = zq.quantize_weights_grouped(W2, G)
+    b2 = (0.01 * torch.randn((K,), generator=g2, dtype=torch.float32)).to(dev)
+    del W2
+    H = torch.empty((M, N), dtype=torch.float16, device=dev)
+    ws_ffn = torch.empty(zq.ffn_workspace_bytes(M, K, N), dtype=torch.uint8, device=dev)
+    ws_lin2 = torch.empty(zq.linear_workspace_bytes(M, N), dtype=torch.uint8, device=dev)
+    Yb = [torch.empty((M, K), dtype=torch.float16, device=dev) for _ in range(nsets)]
+
+    def block_chained(i):
+        s = sets[i % nsets]
+        zq.ffn_w8a8(s["X"], s["Wq"], s["s_w"], G, W2q, s_w2, G, g_arg, b_arg, w.eps, bias, b2,
+                    workspace=ws_ffn, out=Yb[i % nsets])
+
+    def up_only(i):
+        s = sets[i % nsets]
+        zq.linear_w8a8(s["X"], s["Wq"], s["s_w"], G, w.pre, g_arg, b_arg, w.eps, bias, w.act,
+                       workspace=s["ws"], out=H)
+
+    def down_only(i):
+        zq.linear_w8a8(H, W2q, s_w2, G, zq.PRE_NONE, None, None, w.eps, b2, zq.ACT_NONE,
+                       workspace=ws_lin2, out=Yb[i % nsets])
+
+    def block_two_calls(i):
+        up_only(i)
+        down_only(i)
+
+    res = {}
+    for name, fn in (("chained", block_chained), ("two_calls", block_two_calls),
+                     ("up", up_only), ("down", down_only)):
+        for i in range(nsets):
+            fn(i)
+        g = graph_of(torch, fn, args.steps)
+        time_graph(torch, g)
+        res[name] = time_graph(torch, g)[0] / args.steps
+        del g
+    torch.cuda.synchronize()
+    ops_blk = 2.0 * 2.0 * M * N * K
+    return {"block": f"FFN {K}->{N}->{K}, {M} tokens",
+            "chained_us": round(res["chained"] * 1e3, 3),
+            "two_calls_us": round(res["two_calls"] * 1e3, 3),
+            "ffn_up_layer_us": round(res["up"] * 1e3, 3),
+            "ffn_down_layer_us": round(res["down"] * 1e3, 3),
+            "chained_TOPS": round(ops_blk / (res["chained"] * 1e-3) / 1e12, 2)}
+
+
+def cpu_leg(zq, st, t, args):
+    """The oracle on the host cores over all tokens of the workload, repeated
+    until args.cpu_seconds of wall time have passed (a reported baseline)."""
+    import numpy as np
+    from oracle import ref
+    w, inp, decode = st["w"], st["inp"], st["decode"]
+    G = w.group_rows
+    smooth = st["smooth"]
+    Wq_h, sw_h = ref.quantize_groups(
+        ref.fold_weights(inp.W, smooth.cpu().numpy()) if smooth is not None else inp.W, G)
+    g_h = st["gamma"].cpu().numpy() if w.pre == 1 else None
+    b_h = st["beta"].cpu().numpy() if w.pre == 1 else None
+    rows = np.arange(w.M, dtype=np.int64)
+
+    def oracle_passes(seconds):
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            ref.linear_rows(inp.X, w.pre, g_h, b_h, w.eps, Wq_h, sw_h, G, inp.bias, w.act, rows)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return passes, el
+
+    def rate(per):
+        return round((t["bytes_layer"] / per / 1e9) if decode else (t["ops"] / per / 1e12), 4)
+
+    cores = ref.max_threads()
+    passes, el = oracle_passes(args.cpu_seconds)
+    per = el / passes
+    cpu = {"value": rate(per), "unit": t["unit"], "cores": cores, "kind": "oracle",
+           "sample": f"all {w.M} tokens of the workload (prologue + int GEMM + epilogue), "
+                     f"{passes} passes, {per:.3f} s each, {el:.1f} s wall on {cores} threads"}
+    if decode:
+        ref.set_threads(1)
+        passes1, el1 = oracle_passes(3.0)
+        ref.set_threads(cores)
+        cpu["one_thread"] = {"value": rate(el1 / passes1), "unit": t["unit"],
+                             "sample": f"{passes1} passes, {el1 / passes1:.3f} s each"}
+    return cpu
+
+
+def summary(w, t):
+    """One workload's figures as an extra key of the JSON line."""
+    r = t["roofline"]
+    out = {"layer_step_us": round(t["ms_step"] * 1e3, 3), "value": round(t["value"], 2),
+           "unit": t["unit"], "frac_of_peak": round(t["value"] / t["peak"], 4),
+           "prologue_us": round(t["pro_ms"] * 1e3, 3),
+           "prologue_GBps": round(t["bytes_pro"] / (t["pro_ms"] * 1e-3) / 1e9, 1),
+           "prologue_frac_of_hbm": round(t["bytes_pro"] / (t["pro_ms"] * 1e-3) / 1e9
+                                         / PEAK_HBM_GBS, 4),
+           "gemm_us": round(t["gemm_ms"] * 1e3, 3), "roofline": r,
+           "config": {"M": w.M, "K": w.K, "N": w.N, "group_rows": w.group_rows,
+                      "x_dtype": w.x_dtype, "pre": PRE_NAMES[w.pre], "act": ACT_NAMES[w.act],
+                      "bias": w.has_bias, "smoothquant": w.smooth}}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import post_w8a8_quantized_amd as zq
+    from zq_workloads import WORKLOAD_ORDER, WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    zq.library()
+    if args.calib_copy_mb > 0:
+        calib_copy(torch, args.calib_copy_mb)
+        return
+    dev = torch.device("cuda:0")
+
+    # ---- the headline workload, with every leg
+    w = WORKLOADS[args.workload]
+    st = prepare(torch, zq, w, make_inputs, args, dev)
+    t = time_layer(torch, zq, st, args)
+    ablation = None
+    if not st["decode"] and not args.no_ablation:
+        ablation = ablation_leg(torch, zq, st, t, args, dev)
     ffn = None
     if w.name == "bert_ffn_up" and not args.no_ffn:
-        g2 = torch.Generator(device="cpu").manual_seed(1)
-        W2 = (0.02 * torch.randn((K, N), generator=g2, dtype=torch.float32)).to(dev)
-        W2q, s_w2 = zq.quantize_weights_grouped(W2, G)
-        b2 = (0.01 * torch.randn((K,), generator=g2, dtype=torch.float32)).to(dev)
-        del W2
-        H = torch.empty((M, N), dtype=torch.float16, device=dev)
-        ws_ffn = torch.empty(zq.ffn_workspace_bytes(M, K, N), dtype=torch.uint8, device=dev)
-        ws_lin2 = torch.empty(zq.linear_workspace_bytes(M, N), dtype=torch.uint8, device=dev)
-        Yb = [torch.empty((M, K), dtype=torch.float16, device=dev) for _ in range(nsets)]
+        ffn = ffn_leg(torch, zq, st, args, dev)
+    fp8 = None if args.no_fp8 else fp8_leg(torch, zq, st, t, args, dev)
+    cpu = None if args.no_cpu_baseline else cpu_leg(zq, st, t, args)
+    del st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
-        def block_chained(i):
-            s = sets[i % nsets]
-            zq.ffn_w8a8(s["X"], s["Wq"], s["s_w"], G, W2q, s_w2, G, g_arg, b_arg, w.eps, bias, b2,
-                        workspace=ws_ffn, out=Yb[i % nsets])
-
-        def block_two_calls(i):
-            s = sets[i % nsets]
-            zq.linear_w8a8(s["X"], s["Wq"], s["s_w"], G, w.pre, g_arg, b_arg, w.eps, bias, w.act,
-                           workspace=s["ws"], out=H)
-            zq.linear_w8a8(H, W2q, s_w2, G, zq.PRE_NONE, None, None, w.eps, b2, zq.ACT_NONE,
-                           workspace=ws_lin2, out=Yb[i % nsets])
-
-        res = {}
-        for name, fn in (("chained", block_chained), ("two_calls", block_two_calls)):
-            for i in range(nsets):
-                fn(i)
-            g = graph_of(torch, fn, args.steps)
-            time_graph(torch, g)
-            res[name] = time_graph(torch, g)[0] / args.steps
-            del g
-        torch.cuda.synchronize()
-        ops_blk = 2.0 * 2.0 * M * N * K
-        ffn = {"block": f"FFN {K}->{N}->{K}, {M} tokens",
-               "chained_us": round(res["chained"] * 1e3, 3),
-               "two_calls_us": round(res["two_calls"] * 1e3, 3),
-               "chained_TOPS": round(ops_blk / (res["chained"] * 1e-3) / 1e12, 2)}
-        del ws_ffn, ws_lin2, Yb, H, W2q, s_w2, b2
-
-    # ---- FP8 variant of the same layer (E4M3 codes, power-of-two scales), weights
-    # quantized offline (and packed at decode shapes), same rotated inputs
-    fp8 = None
-    if not args.no_fp8:
-        Wd8 = torch.from_numpy(inp.W).to(dev)
-        W8, s_w8 = zq.quantize_weights_grouped_fp8(Wd8, G, smooth)
-        del Wd8
-        if decode:
-            W8 = zq.pack_weights(W8)
-        W8s = [W8] + [W8.clone() for _ in range(nsets - 1)]   # rotated like the int8 weights
-        Y8 = torch.empty((M, N), dtype=torch.float16, device=dev)
-
-        def layer_fp8(i):
-            s = sets[i % nsets]
-            zq.linear_w8a8_fp8(s["X"], W8s[i % nsets], s_w8, G, w.pre, g_arg, b_arg, w.eps, bias,
-                               w.act, workspace=s["ws"], out=Y8, N=N, packed=decode)
-
-        for i in range(nsets):
-            layer_fp8(i)
-        g8 = graph_of(torch, layer_fp8, args.steps)
-        time_graph(torch, g8)
-        ms8 = time_graph(torch, g8)[0] / args.steps
-        del g8, W8, W8s, Y8
-        torch.cuda.synchronize()
-        fp8 = {"layer_step_us": round(ms8 * 1e3, 3),
-               "value": round((bytes_layer / (ms8 * 1e-3) / 1e9) if decode
-                              else (ops / (ms8 * 1e-3) / 1e12), 2),
-               "unit": "GB/s" if decode else "TOPS"}
-
-    # ---- the outlier workload (X fp16 [4096 x 5120], 0.5% of channels x100, LayerNorm;
-    # W [13824 x 5120]) under its two treatments: the SmoothQuant fold with the fused
-    # W8A8 layer (G = 128), and the mixed-precision decomposition (outlier columns in
-    # fp16, per-output-channel int8 weights, alpha = 6).  Each on its own rotated sets.
+    # ---- the outlier workload under the mixed-precision decomposition (its own sets)
     decomp = None
     if not args.no_decomp:
         decomp = outlier_leg(torch, zq, WORKLOADS["outlier_smooth"], make_inputs, args, dev)
+        torch.cuda.empty_cache()
+
+    # ---- the other workloads: layer, prologue, GEMM, roofline, FP8 (and the FFN
+    # block at the BERT FFN-up shape); each on its own rotated sets
+    others = {}
+    if not args.no_others:
+        for name in WORKLOAD_ORDER:
+            if name == w.name or name == "tiny":
+                continue
+            wo = WORKLOADS[name]
+            so = prepare(torch, zq, wo, make_inputs, args, dev)
+            to = time_layer(torch, zq, so, args)
+            others[name] = summary(wo, to)
+            if not args.no_fp8:
+                others[name]["fp8_variant"] = fp8_leg(torch, zq, so, to, args, dev)
+            if name == "bert_ffn_up" and not args.no_ffn:
+                others[name]["ffn_block"] = ffn_leg(torch, zq, so, args, dev)
+            del so
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
 
     # ---- achievable HBM bandwidth for context: a 1 GiB device-to-device copy
-    # (torch's copy kernel; read + write bytes over the HIP-event time of 5 copies)
     hbm_ref = None
     if not args.no_copy_reference:
         torch.cuda.synchronize()
@@ -519,76 +639,46 @@ def main():
                    "bytes_moved": 2 * nb, "what": "1 GiB device copy (read + write), context only"}
         del ca, cb
 
-    # ---- CPU oracle on the host cores (a reported baseline, not the target)
-    cpu = None
-    if not args.no_cpu_baseline:
-        from oracle import ref
-        Wq_h, sw_h = ref.quantize_groups(
-            ref.fold_weights(inp.W, smooth.cpu().numpy()) if smooth is not None else inp.W, G)
-        g_h = gamma.cpu().numpy() if w.pre == 1 else None
-        b_h = beta.cpu().numpy() if w.pre == 1 else None
-        rows = np.arange(M, dtype=np.int64)
-
-        def oracle_passes(seconds):
-            passes, t0 = 0, time.perf_counter()
-            while True:
-                ref.linear_rows(inp.X, w.pre, g_h, b_h, w.eps, Wq_h, sw_h, G, inp.bias, w.act,
-                                rows)
-                passes += 1
-                el = time.perf_counter() - t0
-                if el >= seconds:
-                    return passes, el
-
-        def rate(per):
-            return round((bytes_layer / per / 1e9) if decode else (ops / per / 1e12), 4)
-
-        cores = ref.max_threads()
-        passes, el = oracle_passes(args.cpu_seconds)
-        per = el / passes
-        cpu = {"value": rate(per), "unit": unit, "cores": cores, "kind": "oracle",
-               "sample": f"all {M} tokens of the workload (prologue + int GEMM + epilogue), "
-                         f"{passes} passes, {per:.3f} s each, {el:.1f} s wall on {cores} threads"}
-        if decode:
-            # the few-token shapes also on one core (at least one pass, about 3 s)
-            ref.set_threads(1)
-            passes1, el1 = oracle_passes(3.0)
-            ref.set_threads(cores)
-            cpu["one_thread"] = {"value": rate(el1 / passes1), "unit": unit,
-                                 "sample": f"{passes1} passes, {el1 / passes1:.3f} s each"}
-
+    warmup_steps = -(-args.warmup // args.steps) * args.steps
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
-        "unit": unit,
+        "value": round(t["value"], 2),
+        "unit": t["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": warmup_steps,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(t["ms_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": w.name, "M": M, "K": K, "N": N, "group_rows": G,
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "group_rows": w.group_rows,
                    "x_dtype": w.x_dtype, "pre": PRE_NAMES[w.pre], "act": ACT_NAMES[w.act],
-                   "bias": bias is not None, "smoothquant": w.smooth,
-                   "weights": "packed 32x512 blocks" if decode else "row-major",
-                   "rotated_sets": nsets, "graph_steps": args.steps},
-        "frac_of_peak": round(value / (PEAK_HBM_GBS if decode else PEAK_INT8_TOPS), 4),
-        "breakdown_us": {"layer_step": round(ms_step * 1e3, 3), "prologue": round(pro_ms * 1e3, 3),
-                         "gemm": round(gemm_ms * 1e3, 3),
-                         "prologue_GBps": round(bytes_pro / (pro_ms * 1e-3) / 1e9, 1),
-                         "timed_region_wall_ms": round(ms_wall, 3),
-                         "layer_step_spread": spread},
-        "roofline": roofline,
+                   "bias": w.has_bias, "smoothquant": w.smooth,
+                   "weights": "packed 32x512 blocks" if st_decode(w) else "row-major",
+                   "rotated_sets": t.get("nsets"), "graph_steps": args.steps},
+        "frac_of_peak": round(t["value"] / t["peak"], 4),
+        "breakdown_us": {"layer_step": round(t["ms_step"] * 1e3, 3),
+                         "prologue": round(t["pro_ms"] * 1e3, 3),
+                         "gemm": round(t["gemm_ms"] * 1e3, 3),
+                         "prologue_GBps": round(t["bytes_pro"] / (t["pro_ms"] * 1e-3) / 1e9, 1),
+                         "timed_region_wall_ms": round(t["ms_wall"], 3),
+                         "layer_step_spread": t["spread"]},
+        "roofline": t["roofline"],
         "cpu_baseline": cpu,
         "hbm_copy_reference": hbm_ref,
         "ablation": ablation,
         "ffn_block": ffn,
         "fp8_variant": fp8,
         "outlier_decomposition": decomp,
+        "other_workloads": others,
     }
     print(json.dumps(out), flush=True)
+
+
+def st_decode(w):
+    return w.M <= 32
 
 
 if __name__ == "__main__":
