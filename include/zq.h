@@ -191,6 +191,32 @@ zq_status zq_linear_w8a8(const void *X, zq_dtype x_dtype, zq_pre pre, const floa
                          int64_t M, int64_t N, int64_t K,
                          void *workspace, size_t workspace_bytes, void *Y, hipStream_t stream);
 
+/*
+ * zq_linear_w8a8_noalloc -- zq_linear_w8a8 for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The codes and scales go
+ * to a fixed array inside the library instead of a caller workspace; the
+ * call itself allocates nothing.
+ *
+ *   Arguments and results as zq_linear_w8a8, without workspace arguments.
+ *   The array holds ZQ_NOALLOC_SCRATCH_BYTES (32 MiB) on each GPU the call
+ *   runs on, from that GPU's first such call until the process ends.
+ *   Requires zq_linear_workspace_bytes(M, K) <= ZQ_NOALLOC_SCRATCH_BYTES
+ *   (e.g. 4096 tokens x 5120 features), else ZQ_ERR_WORKSPACE; other rules
+ *   and errors as zq_linear_w8a8.  The device is the calling thread's current
+ *   HIP device.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (other streams, other threads) race and give wrong results; calls
+ *   in order on one stream are safe.  Not reentrant across streams.
+ */
+#define ZQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+zq_status zq_linear_w8a8_noalloc(const void *X, zq_dtype x_dtype, zq_pre pre, const float *gamma,
+                                 const float *beta, float eps, const int8_t *Wq,
+                                 const float *w_scales, int64_t group_rows, const float *bias,
+                                 zq_act act, int64_t M, int64_t N, int64_t K, void *Y,
+                                 hipStream_t stream);
+
 /* Bytes of workspace zq_linear_w8a8 needs: the int8 codes (M*K rounded up to
  * 256) then the per-token scales (4*M rounded up to 256).  Returns 0 for
  * sizes that zq_linear_w8a8 would reject.  Layout: codes at offset 0, scales

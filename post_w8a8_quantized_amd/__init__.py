@@ -43,6 +43,8 @@ from ._binding import (  # noqa: F401
     pack_outlier_weights,
     w8a8_gemm_decomp,
     linear_w8a8,
+    linear_w8a8_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     linear_unfused_workspace_bytes,
     linear_w8a8_fp8,
     linear_w8a8_packed,
@@ -67,7 +69,8 @@ __all__ = [
     "library", "library_path",
     "linear_decomp_workspace_bytes", "linear_w8a8_decomp", "ln_quant_decomp", "outlier_columns",
     "pack_outlier_weights", "w8a8_gemm_decomp",
-    "linear_unfused_workspace_bytes", "linear_w8a8", "linear_w8a8_packed", "linear_w8a8_unfused",
+    "linear_unfused_workspace_bytes", "linear_w8a8", "linear_w8a8_noalloc",
+    "NOALLOC_SCRATCH_BYTES", "linear_w8a8_packed", "linear_w8a8_unfused",
     "linear_workspace_bytes", "ln_quant_per_token",
     "pack_weights", "packed_weights_bytes", "quantize_weights_grouped", "smoothquant_factors",
     "smoothquant_workspace_bytes", "w8a8_gemm_dequant", "w8a8_gemm_dequant_packed",

@@ -42,6 +42,8 @@ _SIGS = {
     "zq_linear_w8a8": (_i, [_p, _i, _i, _p, _p, _f, _p, _p, _i64, _p, _i, _i64, _i64, _i64, _p, _sz,
                            _p, _p]),
     "zq_linear_workspace_bytes": (_sz, [_i64, _i64]),
+    "zq_linear_w8a8_noalloc": (_i, [_p, _i, _i, _p, _p, _f, _p, _p, _i64, _p, _i, _i64, _i64, _i64,
+                                    _p, _p]),
     "zq_smoothquant_factors": (_i, [_p, _i, _i64, _i64, _f, _p, _i, _i64, _p, _p, _p, _p, _p, _p,
                                    _sz, _p]),
     "zq_smoothquant_workspace_bytes": (_sz, [_i64, _i64]),
@@ -265,6 +267,34 @@ def linear_w8a8(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor, group
     _call("zq_linear_w8a8", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps, _ptr(Wq),
           _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(workspace),
           workspace.numel() * workspace.element_size(), _ptr(Y), _stream(X))
+    return Y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # ZQ_NOALLOC_SCRATCH_BYTES in zq.h
+
+
+def linear_w8a8_noalloc(X: torch.Tensor, Wq: torch.Tensor, w_scales: torch.Tensor,
+                        group_rows: int, pre: int = PRE_LAYERNORM, gamma=None, beta=None,
+                        eps: float = 1e-5, bias=None, act: int = ACT_NONE,
+                        out: Optional[torch.Tensor] = None):
+    """The fused layer with its codes and scales in the library's fixed per-GPU
+    array (zq_linear_w8a8_noalloc): no workspace, nothing allocated by the call.
+    Pass `out` to allocate nothing at all.  Calls that may overlap on one GPU race."""
+    _need(X, "X", (torch.float32, torch.float16))
+    M, K = X.shape
+    _need(Wq, "Wq", (torch.int8,), None, X.device)
+    N = Wq.shape[0]
+    _need(w_scales, "w_scales", (torch.float32,), (N // group_rows,), X.device)
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, (torch.float32,), (K,), X.device)
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), (N,), X.device)
+    Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    _need(Y, "out", (torch.float16,), (M, N), X.device)
+    with torch.cuda.device(X.device):
+        _call("zq_linear_w8a8_noalloc", _ptr(X), _fdtype(X), pre, _ptr(gamma), _ptr(beta), eps,
+              _ptr(Wq), _ptr(w_scales), group_rows, _ptr(bias), act, M, N, K, _ptr(Y), _stream(X))
     return Y
 
 

@@ -4,6 +4,8 @@
 #include "zq.h"
 #include "zq_kernels.h"
 
+#include <mutex>
+
 #define ZQ_API extern "C" __attribute__((visibility("default")))
 
 namespace {
@@ -256,6 +258,76 @@ ZQ_API zq_status zq_linear_w8a8_packed(const void *X, zq_dtype x_dtype, zq_pre p
 {
     return linear_impl(X, x_dtype, pre, gamma, beta, eps, Wp, w_scales, group_rows, bias, act, M,
                        N, K, workspace, workspace_bytes, Y, true, stream);
+}
+
+// ---- The layer for callers that cannot allocate ----
+//
+// zq_linear_w8a8_noalloc runs zq_linear_w8a8 with its workspace (the int8
+// codes and the per-token scales) in a fixed device array of this file
+// instead of a caller buffer.  Each GPU the library runs on holds its own copy
+// of the array until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address is looked
+// up once per device with hipGetSymbolAddress and only that address is
+// passed on.
+static __device__ __align__(256) uint8_t scratch[ZQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of the scratch array on the current device.  The first
+// call on a device, with that device current, looks it up; later calls reuse
+// it.  Nothing is allocated here or anywhere on this path.
+zq_status scratch_on_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();  // this call's own failure, reported as ZQ_ERR_HIP
+        return ZQ_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return ZQ_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return ZQ_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ZQ_OK;
+}
+
+}  // namespace
+
+ZQ_API zq_status zq_linear_w8a8_noalloc(const void *X, zq_dtype x_dtype, zq_pre pre,
+                                        const float *gamma, const float *beta, float eps,
+                                        const int8_t *Wq, const float *w_scales,
+                                        int64_t group_rows, const float *bias, zq_act act,
+                                        int64_t M, int64_t N, int64_t K, void *Y,
+                                        hipStream_t stream)
+{
+    if (!X || !Wq || !w_scales || !Y)
+        return ZQ_ERR_NULL;
+    const size_t need = zq_linear_workspace_bytes(M, K);
+    if (need == 0)
+        return ZQ_ERR_SHAPE;
+    if (need > (size_t)ZQ_NOALLOC_SCRATCH_BYTES)
+        return ZQ_ERR_WORKSPACE;
+    if (hip_error_pending())
+        return ZQ_ERR_HIP;
+    void *ws = nullptr;
+    const zq_status st = scratch_on_current_device(&ws);
+    if (st != ZQ_OK)
+        return st;
+    // The prologue writes every code and scale the GEMM then reads, so nothing
+    // in the array needs clearing between calls.
+    return linear_impl(X, x_dtype, pre, gamma, beta, eps, Wq, w_scales, group_rows, bias, act, M,
+                       N, K, ws, (size_t)ZQ_NOALLOC_SCRATCH_BYTES, Y, false, stream);
 }
 
 ZQ_API size_t zq_packed_weights_bytes(int64_t N, int64_t K)

@@ -26,7 +26,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = zq.exported_symbols()
-    assert len(names) == 28
+    assert len(names) == 29
     out = subprocess.run(["nm", "-D", "--defined-only", zq.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -324,6 +324,26 @@ def test_binding_rejects_cpu_tensors():
     X = torch.zeros((4, 16), dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         zq.ln_quant_per_token(X)
+
+
+def noalloc(L, X=A, dt=1, pre=1, Wq=A, sw=A, G=128, M=16, N=256, K=256, Y=A, act=0):
+    return L.zq_linear_w8a8_noalloc(X, dt, pre, None, None, 1e-5, Wq, sw, G, None, act, M, N, K, Y,
+                                    None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(X=None), NULL), (dict(Wq=None), NULL), (dict(sw=None), NULL), (dict(Y=None), NULL),
+    (dict(K=24), SHAPE), (dict(M=0), SHAPE),
+    (dict(M=8200, K=4096), WS),            # codes + scales beyond the 32 MiB array
+])
+def test_noalloc_validation(L, kw, want):
+    assert noalloc(L, **kw) == want
+
+
+def test_noalloc_limit(L):
+    # the largest token count whose codes and scales fit at K = 4096
+    lim = 32 << 20
+    assert L.zq_linear_workspace_bytes(8176, 4096) <= lim < L.zq_linear_workspace_bytes(8200, 4096)
 
 
 def test_binding_checks_workspace_tensor():
