@@ -22,6 +22,7 @@
 #include "zq_kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace zq {
 namespace {
@@ -177,20 +178,24 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
     }
 
     if (pre == 1) {
-        // LayerNorm: the mean, taken about the row's first element x0 (so a
-        // row of equal values gets its value back exactly and y = beta), then
-        // the biased variance about the mean.
-        const float x0 = live ? (float)xrow[0] : 0.0f;
+        // LayerNorm: the mean, then the biased variance about the mean.  A row
+        // of equal values c must give mean = c exactly (then y = beta).  fp16
+        // rows of at most 8192 elements sum to K c exactly in fp32 (11
+        // significant bits times at most 2^13), so they are summed as they are;
+        // other rows are summed about their first element x0.
+        constexpr bool kShift = !std::is_same<T, _Float16>::value || NCH * TT * 8 > 8192;
+        const float x0 = kShift && live ? (float)xrow[0] : 0.0f;
         float s = 0.0f;
 #pragma unroll
         for (int i = 0; i < NCH; i++) {
-            if (t + TT * i < nchunks) {
+            if (!kShift || t + TT * i < nchunks) {
 #pragma unroll
                 for (int e = 0; e < 8; e++)
-                    s += y[i][e] - x0;
+                    s += kShift ? y[i][e] - x0 : y[i][e];
             }
         }
         const float mean = x0 + token_reduce(s, false) / (float)K;
+        // y now holds x - mean, reused by the affine step below.
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < NCH; i++) {
@@ -198,7 +203,8 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
                     const float d = y[i][e] - mean;
-                    ss += d * d;
+                    ss = fmaf(d, d, ss);
+                    y[i][e] = d;
                 }
             }
         }
@@ -224,7 +230,7 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
                 }
 #pragma unroll
                 for (int e = 0; e < 8; e++)               // y = (x - mean) * rstd * g + b
-                    y[i][e] = fmaf(y[i][e] - mean, rstd * g[e], b[e]);
+                    y[i][e] = fmaf(y[i][e], rstd * g[e], b[e]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; e++)
