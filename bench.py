@@ -68,6 +68,8 @@ def parse():
                     help="skip the chained FFN block timing (bert_ffn_up)")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other workloads (BERT FFN-up, GPT QKV, decode FFN-down)")
+    ap.add_argument("--no-clock-sample", action="store_true",
+                    help="skip sampling the GPU clock and power with amd-smi (after the timing)")
     ap.add_argument("--no-copy-reference", action="store_true",
                     help="skip the 1 GiB device-copy bandwidth reference")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -146,6 +148,55 @@ def calib_copy(torch, mb):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes": n, "launches": 5}), flush=True)
+
+
+def sample_clock_power(torch, g, steps, seconds=2.0):
+    """Replays graph g (steps layer steps) back to back for about `seconds` while
+    amd-smi samples the socket power and the per-XCD graphics clocks; returns
+    their medians (None when amd-smi is not available).  Outside any timed region."""
+    import shutil
+    import statistics
+    import subprocess
+    import threading
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    rows, stop = [], [False]
+
+    def sampler():
+        while not stop[0]:
+            r = subprocess.run([exe, "metric", "-p", "-c", "--csv"], capture_output=True, text=True)
+            lines = [ln for ln in r.stdout.strip().splitlines() if ln.strip()]
+            if len(lines) >= 2:
+                rows.append(dict(zip(lines[0].split(","), lines[-1].split(","))))
+            time.sleep(0.2)
+
+    th = threading.Thread(target=sampler)
+    torch.cuda.synchronize()
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        g.replay()
+        torch.cuda.synchronize()
+    stop[0] = True
+    th.join()
+    rows = rows[2:-1] if len(rows) > 4 else rows   # drop the ramp at both ends
+
+    def med(keys):
+        vals = []
+        for r in rows:
+            for k in keys:
+                try:
+                    vals.append(float(r[k]))
+                except (KeyError, ValueError):
+                    pass
+        return round(statistics.median(vals), 1) if vals else None
+
+    clk_keys = [k for k in (rows[0] if rows else {}) if k.startswith("gfx_") and k.endswith("_clk")
+                and "min" not in k and "max" not in k]
+    return {"samples": len(rows), "socket_power_W": med(["socket_power"]),
+            "gfx_clock_MHz": med(clk_keys),
+            "what": "amd-smi during back-to-back replays of the layer-step graph (not timed)"}
 
 
 def outlier_leg(torch, zq, w, make_inputs, args, dev):
@@ -295,7 +346,7 @@ def prepare(torch, zq, w, make_inputs, args, dev):
                 sets=sets, nsets=nsets, x_el=x_el)
 
 
-def time_layer(torch, zq, st, args):
+def time_layer(torch, zq, st, args, sample=False):
     """HIP-event times of the prologue alone, the GEMM alone (graphs of K launches
     each) and of K whole layer steps (one replay of a K-step graph after the
     warmup replays), plus the dominant kernel's roofline."""
@@ -353,6 +404,7 @@ def time_layer(torch, zq, st, args):
     ms_step = ms_ev / args.steps
     reps = np.array([ms_step] + [time_graph(torch, g_steps)[0] / args.steps for _ in range(9)])
     p10, p50, p90 = np.percentile(reps * 1e3, [10, 50, 90])
+    clock_power = sample_clock_power(torch, g_steps, args.steps) if sample else None
     del g_steps, g_pro, g_gemm
     torch.cuda.synchronize()
 
@@ -381,7 +433,7 @@ def time_layer(torch, zq, st, args):
     # counted HBM bytes over the bytes the kernel must move (re-reads, partial lines)
     roofline["traffic_over_algorithmic"] = (round(traffic / bytes_gemm, 3) if traffic else None)
     return dict(ms_step=ms_step, ms_wall=ms_wall, pro_ms=pro_ms, gemm_ms=gemm_ms, value=value,
-                nsets=nsets,
+                nsets=nsets, clock_power=clock_power,
                 unit=unit, peak=peak, ops=ops, bytes_pro=bytes_pro, bytes_gemm=bytes_gemm,
                 bytes_layer=bytes_layer, roofline=roofline,
                 spread={"replays": int(reps.size), "p10_us": round(float(p10), 3),
@@ -581,7 +633,7 @@ def main():
     # ---- the headline workload, with every leg
     w = WORKLOADS[args.workload]
     st = prepare(torch, zq, w, make_inputs, args, dev)
-    t = time_layer(torch, zq, st, args)
+    t = time_layer(torch, zq, st, args, sample=not args.no_clock_sample)
     ablation = None
     if not st["decode"] and not args.no_ablation:
         ablation = ablation_leg(torch, zq, st, t, args, dev)
@@ -667,6 +719,7 @@ def main():
                          "layer_step_spread": t["spread"]},
         "roofline": t["roofline"],
         "cpu_baseline": cpu,
+        "clock_power": t["clock_power"],
         "hbm_copy_reference": hbm_ref,
         "ablation": ablation,
         "ffn_block": ffn,
