@@ -74,3 +74,40 @@ def test_noalloc_rejects_sizes_beyond_the_array(zq):
     with pytest.raises(zq.ZQError, match="ZQ_ERR_WORKSPACE"):
         zq.linear_w8a8_noalloc(X, Wq, s_w, G, out=Y)
     assert bool((Y == 7.0).all())
+
+
+def test_noalloc_captured_in_a_graph(zq):
+    """The callers it is for: captured in a HIP graph, every replay gives the
+    eager zq_linear_w8a8 bits, with an eager no-alloc call on other inputs (which
+    overwrites the shared array) and unrelated work between the replays."""
+    say("noalloc graph")
+    rng = np.random.default_rng(9)
+    M, K, N, G = 300, 768, 512, 128
+    X, Wq, s_w, g, b, bias = _case(rng, M, K, N, G, np.float16)
+    X2 = dev((rng.standard_normal((M, K)) * 3).astype(np.float16))
+    want = host(zq.linear_w8a8(X, Wq, s_w, G, zq.PRE_LAYERNORM, g, b, 1e-5, bias, zq.ACT_GELU))
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    Y2 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+
+    def call():
+        zq.linear_w8a8_noalloc(X, Wq, s_w, G, zq.PRE_LAYERNORM, g, b, 1e-5, bias, zq.ACT_GELU,
+                               out=Y)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(3):
+        Y.fill_(0)
+        zq.linear_w8a8_noalloc(X2, Wq, s_w, G, out=Y2)       # overwrites the array
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(Y).view(np.uint16), want.view(np.uint16)), f"replay {r}"
+        del junk
