@@ -133,7 +133,8 @@ zq_status zq_quantize_weights_grouped(const void *W, zq_dtype w_dtype, const flo
  *   eps       LayerNorm epsilon (e.g. 1e-5).
  *   Xq        [M x K] int8 out, 16-byte aligned.
  *   x_scales  [M] fp32 out: s_x[m] = fl32(max_k |y[m, k]| / 127).
- * Requires M >= 1, 1 <= K <= ZQ_MAX_K, K % 16 == 0.
+ * Requires M >= 1, 1 <= K <= ZQ_MAX_K, K % 16 == 0.  X must be finite: the
+ * codes and scale of a token whose row holds an Inf or NaN are unspecified.
  */
 zq_status zq_ln_quant_per_token(const void *X, zq_dtype x_dtype, int64_t M, int64_t K,
                                 zq_pre pre, const float *gamma, const float *beta, float eps,

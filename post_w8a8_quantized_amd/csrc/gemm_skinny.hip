@@ -38,22 +38,6 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kPackRows = 32;   // weight rows per packed block
 constexpr int kPackBytes = 512; // bytes of each row per packed block
 
-// POLICY is the cache-policy operand of the load (2 = nt: streamed, not kept).
-template <int POLICY>
-__device__ __forceinline__ void dma16(const int8_t *src, int8_t *lds_base)
-{
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0,
-                                     POLICY);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // F8: the operands are OCP E4M3 codes and the product is
 // v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales), accumulating in fp32;
 // OUT_I32 then writes the raw fp32 accumulators.

@@ -63,22 +63,6 @@ __device__ __forceinline__ int swz(int row)
     return BK == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
 }
 
-// Wait until at most n vector-memory operations of this wave are outstanding
-// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
-// left at their no-wait maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ void dma16(const int8_t *src, int8_t *lds_base)
-{
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
-}
-
 template <int BM, int BN, int WM, int WN, int BK, int NSTAGE>
 struct Cfg {
     static constexpr int NW = WM * WN;                // waves per workgroup

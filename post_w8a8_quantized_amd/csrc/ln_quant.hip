@@ -14,7 +14,9 @@
 // about the mean, absmax) run on DPP without touching LDS (and through LDS
 // only across the waves of one token), and codes go out as 8-byte groups.
 // The same kernel provides the fp16-output op of the unfused order, the FP8
-// codes, and the two passes of the mixed-precision decomposition.
+// codes, and the two passes of the mixed-precision decomposition.  fp16 rows
+// of at most 8192 elements quantized to int8 or FP8 (the prefill layers) take
+// k_ln_quant_f16, the same arithmetic instantiated per op.
 //
 // A few tokens with long rows (the decode shape) are spread over many
 // workgroups per row instead (see k_rowseg_quant).
@@ -76,19 +78,45 @@ __device__ __forceinline__ void load8(const float *p, float (&v)[8])
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// Codes of 8 values with scale s (rs = fl32(1/s), fast = rcp_quant_ok(s)).
+// Codes of 8 values with scale s (rs = fl32(1/s), fast = rcp_quant_ok(s)),
+// the values being elements of the vector whose absmax gave s.
+//
+// Reciprocal path, all 8 at once: u = fma(y, rs, 1.5 * 2^23) rounds y * rs to
+// the nearest integer r (the spacing of floats in [2^23, 2^24) is 1), so the
+// low byte of u's bits is r as a two's-complement int8 (|r| <= 127 leaves the
+// upper bits at those of 1.5 * 2^23); r = u - 1.5 * 2^23 exactly, and
+// |fma(y, rs, -r)| is y * rs's distance to r.  When every distance is at most
+// 1/2 - 2^-13 (no value within 2^-13 of a half-integer), r is also the integer
+// nearest to y / s (y * rs is within 2^-17 of y / s below 128), i.e. the same
+// code as quant_code; otherwise, in about one group of 8 in 10^3, the group
+// takes quant_code.  One test per group instead of a branch per value.
 __device__ __forceinline__ uint2 quant8(const float (&y)[8], float s, float rs, bool fast)
 {
-    int q[8];
+    constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
     if (fast) {
+        uint32_t u[8];
+        float far = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; e++)
-            q[e] = quant_code_rcp(y[e], s, rs);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            q[e] = quant_code(y[e], s);
+        for (int e = 0; e < 8; e++) {
+            const float ru = fmaf(y[e], rs, kRound);
+            u[e] = __float_as_uint(ru);
+            far = fmaxf(far, fabsf(fmaf(y[e], rs, -(ru - kRound))));
+        }
+        if (far <= 0.4998779296875f) {
+            uint2 packed;
+            packed.x = __builtin_amdgcn_perm(__builtin_amdgcn_perm(u[3], u[2], 0x0c0c0400u),
+                                             __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u),
+                                             0x05040100u);
+            packed.y = __builtin_amdgcn_perm(__builtin_amdgcn_perm(u[7], u[6], 0x0c0c0400u),
+                                             __builtin_amdgcn_perm(u[5], u[4], 0x0c0c0400u),
+                                             0x05040100u);
+            return packed;
+        }
     }
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        q[e] = quant_code(y[e], s);
     uint2 packed;
     packed.x = pack4_i8(q[0], q[1], q[2], q[3]);
     packed.y = pack4_i8(q[4], q[5], q[6], q[7]);
@@ -336,6 +364,162 @@ __global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant(
     }
     if (t == 0)
         sx[m] = scale;
+}
+
+// ---- fp16 rows of at most 8192 elements, int8 or FP8 codes: the main path ----
+//
+// The arithmetic of k_ln_quant for these rows (the same bits), built once per
+// op so each instantiation holds only its own registers (LayerNorm with 3
+// pieces per lane: 52 VGPRs; k_ln_quant, whose op is chosen at run time,
+// carries GeLU's registers into its LayerNorm code: 67).  Each cross-wave reduction
+// writes its own LDS entries, so one barrier per reduction suffices, and the
+// barrier waits for LDS traffic only (no drain of outstanding stores).
+// Measured on the 4096 x 5120 LayerNorm prologue: 21.2 us against 23.0 us for
+// k_ln_quant; 4096 x 8192: 31.0 against 35.0 us.  Giving each token group two
+// or four tokens at once (shared reductions and gamma / beta loads) was
+// slower (22.9 and 30.5 us), as were two waves per token (21.1 us, with a
+// different summation order) and a persistent form that streams rows into an
+// LDS ring by DMA (24.3 us).
+template <int NCH, int WPT, int TPB, int PRE, bool FP8>
+__global__ __launch_bounds__(kWave * WPT * TPB) void k_ln_quant_f16(
+    const _Float16 *__restrict__ X, int M, int K, const float *__restrict__ gamma,
+    const float *__restrict__ beta, float eps, int8_t *__restrict__ Xq, float *__restrict__ sx)
+{
+    constexpr int TT = kWave * WPT;  // threads per token
+    static_assert(NCH * TT * 8 <= 8192, "fp16 rows summed unshifted have at most 8192 elements");
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int tok = wave / WPT;
+    const int wig = wave % WPT;
+    const int t = wig * kWave + lane;
+    const int64_t m = (int64_t)blockIdx.x * TPB + tok;
+    const bool live = m < M;
+    const int nchunks = K / 8;
+
+    // [0] sum, [1] sum of squares, [2] absmax: each entry is written once.
+    __shared__ float red[3][TPB][WPT > 1 ? WPT : 1];
+    auto token_reduce = [&](float v, int k, bool is_max) -> float {
+        v = is_max ? wave_max(v) : wave_sum(v);
+        if constexpr (WPT > 1) {
+            if (lane == 0)
+                red[k][tok][wig] = v;
+            lds_barrier();
+            float r = red[k][tok][0];
+#pragma unroll
+            for (int w = 1; w < WPT; w++)
+                r = is_max ? fmaxf(r, red[k][tok][w]) : r + red[k][tok][w];
+            v = r;
+        }
+        return v;
+    };
+
+    float y[NCH][8];
+    const _Float16 *xrow = X + m * (int64_t)K;
+#pragma unroll
+    for (int i = 0; i < NCH; i++) {
+        const int c = t + TT * i;
+        if (live && c < nchunks) {
+            Chunk<_Float16>::load_nt(xrow + (int64_t)c * 8, y[i]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                y[i][e] = 0.0f;
+        }
+    }
+
+    if constexpr (PRE == 1) {
+        // Summed unshifted (exact for a row of equal values), the variance
+        // about the mean with x - mean kept, rstd once per token in fp64.
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NCH; i++)
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                s += y[i][e];
+        const float mean = 0.0f + token_reduce(s, 0, false) / (float)K;
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            if (t + TT * i < nchunks) {
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float d = y[i][e] - mean;
+                    ss = fmaf(d, d, ss);
+                    y[i][e] = d;
+                }
+            }
+        }
+        const float rstd =
+            (float)(1.0 / sqrt((double)(token_reduce(ss, 1, false) / (float)K) + (double)eps));
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + TT * i;
+            if (c < nchunks) {
+                float g[8], b[8];
+                if (gamma) {
+                    load8(gamma + c * 8, g);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) g[e] = 1.0f;
+                }
+                if (beta) {
+                    load8(beta + c * 8, b);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) b[e] = 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    y[i][e] = fmaf(y[i][e], rstd * g[e], b[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    y[i][e] = 0.0f;
+            }
+        }
+    } else if constexpr (PRE == 2) {
+#pragma unroll
+        for (int i = 0; i < NCH; i++)
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                y[i][e] = gelu_erf(y[i][e]);
+    }
+
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; i++)
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            a = fmaxf(a, fabsf(y[i][e]));
+    a = token_reduce(a, 2, true);
+    if (!live)
+        return;
+
+    int8_t *qrow = Xq + m * (int64_t)K;
+    if constexpr (FP8) {
+        int e;
+        const float scale = fp8_scale(a, e);
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + TT * i;
+            if (c < nchunks)
+                *reinterpret_cast<uint2 *>(qrow + (int64_t)c * 8) = quant8_fp8(y[i], scale, e);
+        }
+        if (t == 0)
+            sx[m] = scale;
+    } else {
+        const float scale = a / 127.0f;
+        const bool fast = rcp_quant_ok(scale);
+        const float rs = fast ? 1.0f / scale : 0.0f;
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + TT * i;
+            if (c < nchunks)
+                *reinterpret_cast<uint2 *>(qrow + (int64_t)c * 8) = quant8(y[i], scale, rs, fast);
+        }
+        if (t == 0)
+            sx[m] = scale;
+    }
 }
 
 // ---- Few tokens with long rows (the decode shape): a row over many workgroups ----
@@ -866,6 +1050,41 @@ hipError_t launch_cfg(const T *X, int64_t M, int64_t K, int pre, const float *ga
     return hipErrorInvalidValue;
 }
 
+// k_ln_quant_f16, one instantiation per op and per exact piece count NCH
+// (so only a lane's last piece can lie past the row's end).
+template <int WPT, int TPB, int PRE, bool FP8>
+hipError_t launch_f16_op(const _Float16 *X, int64_t M, int64_t K, const float *gamma,
+                         const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream)
+{
+    const int64_t per = (K / 8 + kWave * WPT - 1) / (kWave * WPT);
+    const dim3 grid((unsigned)((M + TPB - 1) / TPB));
+    const dim3 block(kWave * WPT * TPB);
+#define ZQ_F16_CASE(n)                                                                            \
+    case n:                                                                                       \
+        hipLaunchKernelGGL((k_ln_quant_f16<n, WPT, TPB, PRE, FP8>), grid, block, 0, stream, X,    \
+                           (int)M, (int)K, gamma, beta, eps, Xq, sx);                             \
+        return hipGetLastError();
+    switch (per) {
+    ZQ_F16_CASE(1)
+    ZQ_F16_CASE(2)
+    ZQ_F16_CASE(3)
+    ZQ_F16_CASE(4)
+    default: return hipErrorInvalidValue;
+    }
+#undef ZQ_F16_CASE
+}
+
+template <int WPT, int TPB, bool FP8>
+hipError_t launch_f16(const _Float16 *X, int64_t M, int64_t K, int pre, const float *gamma,
+                      const float *beta, float eps, int8_t *Xq, float *sx, hipStream_t stream)
+{
+    if (pre == 1)
+        return launch_f16_op<WPT, TPB, 1, FP8>(X, M, K, gamma, beta, eps, Xq, sx, stream);
+    if (pre == 2)
+        return launch_f16_op<WPT, TPB, 2, FP8>(X, M, K, gamma, beta, eps, Xq, sx, stream);
+    return launch_f16_op<WPT, TPB, 0, FP8>(X, M, K, gamma, beta, eps, Xq, sx, stream);
+}
+
 // Waves per token by row length.  Rows up to 2048 elements take one wave
 // (four tokens per block).  Up to 8192 they take four waves (one token per
 // block): each lane then holds at most four 16-byte pieces of the row, few
@@ -878,6 +1097,12 @@ hipError_t launch_rows(const T *X, int64_t M, int64_t K, int pre, const float *g
                        _Float16 *Y16, float alpha = 0.0f,
                        int32_t *slot = nullptr, _Float16 *XO = nullptr)
 {
+    if constexpr (std::is_same<T, _Float16>::value && !OUT_F16 && DEC == 0) {
+        if (K <= 2048)
+            return launch_f16<1, 4, FP8>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream);
+        if (K <= 8192)
+            return launch_f16<4, 1, FP8>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream);
+    }
     if (K <= 2048)
         return launch_cfg<T, 1, 4, OUT_F16, FP8, DEC, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx,
                                                          stream, Y16, alpha, slot, XO);

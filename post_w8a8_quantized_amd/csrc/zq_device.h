@@ -202,4 +202,51 @@ __device__ __forceinline__ void atomic_max_nonneg(uint32_t *addr, float v)
     atomicMax(addr, __float_as_uint(v));
 }
 
+
+// ---- LDS DMA (global_load_lds_dwordx4) and its wait ----
+
+// Each lane's 16 bytes at src go to LDS at lds_base + 16 * lane (lds_base is
+// the same for the whole wave).  POLICY is the load's cache-policy operand
+// (0: default, 2: non-temporal, for data read once).
+template <int POLICY = 0>
+__device__ __forceinline__ void dma16(const int8_t *src, int8_t *lds_base)
+{
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0,
+                                     POLICY);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their no-wait maxima).  The counter covers loads, LDS DMA and stores
+// alike, in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS data written with ordinary ds_write: this wave's
+// LDS operations complete (lgkmcnt(0)), then s_barrier.  Its global loads,
+// stores and LDS DMA stay in flight (__syncthreads, and a release fence even
+// when limited to LDS, wait for all of them, LDS DMA included).  The
+// single-thread fences and the scheduling barrier keep the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until this wave's LDS reads and writes have completed (lgkmcnt(0)).
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+}
+
 }  // namespace zq
