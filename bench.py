@@ -21,7 +21,10 @@ again under the mixed-precision decomposition.
 The steps are captured in a HIP graph (on torch's stream, which is the
 stream the library launches on) so that host-side call overhead does not
 leave the GPU idle between layers; the timed region is one replay of a graph
-of exactly K steps, bracketed by device synchronisations.
+of exactly K steps, bracketed by device synchronisations.  The prologue's and
+the GEMM's average launch durations (the roofline's) come from K more steps
+with HIP events between the two kernels, queued behind replays of that graph
+so that they run in the same back-to-back state (kernel_times).
 
 Printed: ONE JSON line.
 """
@@ -69,7 +72,9 @@ def parse():
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other workloads (BERT FFN-up, GPT QKV, decode FFN-down)")
     ap.add_argument("--no-clock-sample", action="store_true",
-                    help="skip sampling the GPU clock and power with amd-smi (after the timing)")
+                    help="skip the untimed back-to-back steps before each workload's warmup (2 s "
+                         "for the headline, during which amd-smi samples the GPU clock and power; "
+                         "0.5 s for the others); for profiler runs")
     ap.add_argument("--no-copy-reference", action="store_true",
                     help="skip the 1 GiB device-copy bandwidth reference")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -138,6 +143,20 @@ def time_graph(torch, g):
     return e0.elapsed_time(e1), wall
 
 
+def settled_ms(torch, g, steps, args):
+    """Milliseconds per step of one replay of graph g (`steps` steps), after the
+    warmup replays and, unless --no-clock-sample, 0.3 s of back-to-back replays
+    (the GPU runs slower for a while after any idle time; settle_and_sample)."""
+    if not args.no_clock_sample:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            g.replay()
+            torch.cuda.synchronize()
+    for _ in range(-(-args.warmup // steps)):
+        time_graph(torch, g)
+    return time_graph(torch, g)[0] / steps
+
+
 def calib_copy(torch, mb):
     n = int(mb * 1024 * 1024)
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -150,36 +169,59 @@ def calib_copy(torch, mb):
     print(json.dumps({"calib_copy_bytes": n, "launches": 5}), flush=True)
 
 
-def sample_clock_power(torch, g, steps, seconds=2.0):
-    """Replays graph g (steps layer steps) back to back for about `seconds` while
-    amd-smi samples the socket power and the per-XCD graphics clocks; returns
-    their medians (None when amd-smi is not available).  Outside any timed region."""
+def settle_and_sample(torch, g, seconds=2.0, sample=True):
+    """Replays graph g (K layer steps) back to back for about `seconds`, right
+    before the warmup and timed replays, so that those run at the clock and
+    power the GPU sustains under this load: after any idle time the GPU comes
+    back slower (measured on the headline layer: 295 us per step back to back,
+    ~305 us with 2 ms of host idle before each replay, ~340 us with 50 ms, and
+    ~20 ms of work to recover).  With `sample`, amd-smi samples the socket
+    power and the per-XCD graphics clocks meanwhile; returns their medians
+    (None without sampling or amd-smi, or under a profiler, whose preloaded
+    library would also attach to amd-smi's process).  Untimed."""
     import shutil
     import statistics
     import subprocess
     import threading
-    exe = shutil.which("amd-smi")
-    if exe is None:
-        return None
+    cmd = None
+    profiled = any(k.startswith("ROCPROF") for k in os.environ) or \
+        "rocprofiler" in os.environ.get("LD_PRELOAD", "")
+    exe = None if (profiled or not sample) else shutil.which("amd-smi")
+    if exe is not None:
+        # amd-smi is a Python script: run it with this interpreter as a child
+        # process (no `env` hop that would exec a second program).
+        exe = os.path.realpath(exe)
+        with open(exe, "rb") as fh:
+            first = fh.readline()
+        cmd = [sys.executable, exe] if first.startswith(b"#!") and b"python" in first else [exe]
     rows, stop = [], [False]
 
     def sampler():
         while not stop[0]:
-            r = subprocess.run([exe, "metric", "-p", "-c", "--csv"], capture_output=True, text=True)
+            r = subprocess.run(cmd + ["metric", "-p", "-c", "--csv"], capture_output=True, text=True)
             lines = [ln for ln in r.stdout.strip().splitlines() if ln.strip()]
             if len(lines) >= 2:
                 rows.append(dict(zip(lines[0].split(","), lines[-1].split(","))))
             time.sleep(0.2)
 
-    th = threading.Thread(target=sampler)
+    th = threading.Thread(target=sampler) if cmd else None
     torch.cuda.synchronize()
-    th.start()
+    if th:
+        th.start()
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         g.replay()
         torch.cuda.synchronize()
     stop[0] = True
-    th.join()
+    # keep the GPU busy until the sampler's last amd-smi call has returned, so
+    # that no idle time separates this from the warmup replays
+    while th is not None and th.is_alive():
+        g.replay()
+        torch.cuda.synchronize()
+    if th:
+        th.join()
+    if not cmd:
+        return None
     rows = rows[2:-1] if len(rows) > 4 else rows   # drop the ramp at both ends
 
     def med(keys):
@@ -196,7 +238,8 @@ def sample_clock_power(torch, g, steps, seconds=2.0):
                 and "min" not in k and "max" not in k]
     return {"samples": len(rows), "socket_power_W": med(["socket_power"]),
             "gfx_clock_MHz": med(clk_keys),
-            "what": "amd-smi during back-to-back replays of the layer-step graph (not timed)"}
+            "what": "amd-smi during 2 s of back-to-back replays of the layer-step graph "
+                    "before the warmup and timed replays (untimed)"}
 
 
 def outlier_leg(torch, zq, w, make_inputs, args, dev):
@@ -282,8 +325,7 @@ def outlier_leg(torch, zq, w, make_inputs, args, dev):
         for i in range(nsets):
             fn(i)
         g = graph_of(torch, fn, args.steps)
-        time_graph(torch, g)
-        res[name] = time_graph(torch, g)[0] / args.steps
+        res[name] = settled_ms(torch, g, args.steps, args)
         del g
     torch.cuda.synchronize()
     n_out = int(parts(sets[0])[1][0].item())
@@ -346,10 +388,40 @@ def prepare(torch, zq, w, make_inputs, args, dev):
                 sets=sets, nsets=nsets, x_el=x_el)
 
 
+def kernel_times(torch, g_steps, ms_step, prologue, gemm, steps):
+    """Average launch durations of the prologue and the GEMM as they run inside
+    layer steps.  ROCm's PyTorch records no timing events inside a captured
+    graph, so the K steps run eagerly, the prologue and the GEMM as the two
+    boundary calls with HIP events on the launch stream before, between and
+    after them.  They are queued behind replays of the timed graph (at least
+    ~5 ms of GPU work), so the GPU never waits for the host and the kernels
+    run in the same back-to-back state as in the timed replay.  Returns
+    (prologue ms, GEMM ms, idle fraction of the steps' span)."""
+    import numpy as np
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    lead = max(1, -(-5.0 // (ms_step * steps)))
+    torch.cuda.synchronize()
+    for _ in range(int(lead)):
+        g_steps.replay()
+    for i in range(steps):
+        a, b, c = ev[i]
+        a.record()
+        prologue(i)
+        b.record()
+        gemm(i)
+        c.record()
+    torch.cuda.synchronize()
+    pro = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    gem = np.array([b.elapsed_time(c) for _, b, c in ev])
+    span = ev[0][0].elapsed_time(ev[-1][2])
+    gap = max(0.0, 1.0 - float(pro.sum() + gem.sum()) / span) if span > 0 else 0.0
+    return float(pro.mean()), float(gem.mean()), gap
+
+
 def time_layer(torch, zq, st, args, sample=False):
-    """HIP-event times of the prologue alone, the GEMM alone (graphs of K launches
-    each) and of K whole layer steps (one replay of a K-step graph after the
-    warmup replays), plus the dominant kernel's roofline."""
+    """HIP-event time of K whole layer steps (one replay of a K-step graph after
+    the warmup replays), the prologue's and the GEMM's average launch durations
+    in the same steps (kernel_times), and the dominant kernel's roofline."""
     import numpy as np
     w, sets, nsets, decode = st["w"], st["sets"], st["nsets"], st["decode"]
     M, N, K, G = w.M, w.N, w.K, w.group_rows
@@ -385,18 +457,13 @@ def time_layer(torch, zq, st, args, sample=False):
     for i in range(nsets):
         layer(i)
     torch.cuda.synchronize()
-    # per-kernel averages over graphs of the same launches (HIP events).  They run
-    # first: their work also brings the GPU to the steady state a sustained run sees.
-    g_pro = graph_of(torch, prologue, args.steps)
-    g_gemm = graph_of(torch, gemm, args.steps)
-    time_graph(torch, g_pro)
-    time_graph(torch, g_gemm)
-    pro_ms = time_graph(torch, g_pro)[0] / args.steps
-    gemm_ms = time_graph(torch, g_gemm)[0] / args.steps
     # timed layer steps: the W warmup steps are replays of the same K-step graph
     # (ceil(W / K) of them), so the timed replay runs a graph that has already been
     # launched once (a graph's first replay carries one-time costs).
     g_steps = graph_of(torch, layer, args.steps)
+    clock_power = None
+    if not args.no_clock_sample:
+        clock_power = settle_and_sample(torch, g_steps, 2.0 if sample else 0.5, sample)
     warm_replays = -(-args.warmup // args.steps)
     for _ in range(warm_replays):
         time_graph(torch, g_steps)
@@ -404,8 +471,8 @@ def time_layer(torch, zq, st, args, sample=False):
     ms_step = ms_ev / args.steps
     reps = np.array([ms_step] + [time_graph(torch, g_steps)[0] / args.steps for _ in range(9)])
     p10, p50, p90 = np.percentile(reps * 1e3, [10, 50, 90])
-    clock_power = sample_clock_power(torch, g_steps, args.steps) if sample else None
-    del g_steps, g_pro, g_gemm
+    pro_ms, gemm_ms, gap = kernel_times(torch, g_steps, ms_step, prologue, gemm, args.steps)
+    del g_steps
     torch.cuda.synchronize()
 
     ops = 2.0 * M * N * K
@@ -432,6 +499,9 @@ def time_layer(torch, zq, st, args, sample=False):
                     "algorithmic_ops_per_launch": ops, "algorithmic_bytes_per_launch": bytes_gemm}
     # counted HBM bytes over the bytes the kernel must move (re-reads, partial lines)
     roofline["traffic_over_algorithmic"] = (round(traffic / bytes_gemm, 3) if traffic else None)
+    roofline["launch_timing"] = ("HIP events around each launch in K eager layer steps queued "
+                                 "behind replays of the timed graph; GPU idle between the "
+                                 f"step's kernels: {gap * 100:.2f}% of the steps' span")
     return dict(ms_step=ms_step, ms_wall=ms_wall, pro_ms=pro_ms, gemm_ms=gemm_ms, value=value,
                 nsets=nsets, clock_power=clock_power,
                 unit=unit, peak=peak, ops=ops, bytes_pro=bytes_pro, bytes_gemm=bytes_gemm,
@@ -462,8 +532,7 @@ def fp8_leg(torch, zq, st, t, args, dev):
     for i in range(nsets):
         layer_fp8(i)
     g8 = graph_of(torch, layer_fp8, args.steps)
-    time_graph(torch, g8)
-    ms8 = time_graph(torch, g8)[0] / args.steps
+    ms8 = settled_ms(torch, g8, args.steps, args)
     del g8, W8, W8s, Y8
     torch.cuda.synchronize()
     return {"layer_step_us": round(ms8 * 1e3, 3),
@@ -488,8 +557,7 @@ def ablation_leg(torch, zq, st, t, args, dev):
     for i in range(nsets):
         layer_unfused(i)
     g_unf = graph_of(torch, layer_unfused, args.steps)
-    time_graph(torch, g_unf)
-    unf_ms = time_graph(torch, g_unf)[0] / args.steps
+    unf_ms = settled_ms(torch, g_unf, args.steps, args)
     del g_unf, ws_unf
     torch.cuda.synchronize()
     return {"unfused_layer_step_us": round(unf_ms * 1e3, 3),
@@ -539,8 +607,7 @@ def ffn_leg(torch, zq, st, args, dev):
         for i in range(nsets):
             fn(i)
         g = graph_of(torch, fn, args.steps)
-        time_graph(torch, g)
-        res[name] = time_graph(torch, g)[0] / args.steps
+        res[name] = settled_ms(torch, g, args.steps, args)
         del g
     torch.cuda.synchronize()
     ops_blk = 2.0 * 2.0 * M * N * K
