@@ -1,0 +1,64 @@
+"""Host-side logic of bench.py, on the CPU: the one-GPU refusal and the rule that
+a committed traffic summary counts only when it was taken on the current kernel
+source."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+@pytest.fixture()
+def fake_root(tmp_path, monkeypatch):
+    csrc = tmp_path / "post_w8a8_quantized_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "k.hip").write_text("kernel source v1\n")
+    (csrc / "zq_device.h").write_text("helpers\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    return tmp_path
+
+
+def write_summary(root, src_hash, total):
+    (root / "profiles" / "traffic_k_wl.txt").write_text(
+        "# HBM traffic per launch of k\n"
+        f"source_hash = {src_hash}\n"
+        "launches = 10\n"
+        f"hbm_bytes_per_launch = {total}\n")
+
+
+def test_traffic_read_only_for_the_current_source(fake_root):
+    h = bench.kernel_source_hash(["k.hip", "zq_device.h"])
+    assert h == bench.kernel_source_hash(["k.hip", "zq_device.h"])
+    write_summary(fake_root, h, 123456)
+    assert bench.read_traffic("k", "wl", h) == 123456.0
+    # the kernel changes after the counters were taken: the figure no longer counts
+    (fake_root / "post_w8a8_quantized_amd" / "csrc" / "k.hip").write_text("kernel source v2\n")
+    h2 = bench.kernel_source_hash(["k.hip", "zq_device.h"])
+    assert h2 != h
+    assert bench.read_traffic("k", "wl", h2) is None
+    # a shared header counts as part of the source
+    write_summary(fake_root, h2, 7)
+    (fake_root / "post_w8a8_quantized_amd" / "csrc" / "zq_device.h").write_text("helpers v2\n")
+    assert bench.read_traffic("k", "wl", bench.kernel_source_hash(["k.hip", "zq_device.h"])) is None
+
+
+def test_missing_or_malformed_summary(fake_root):
+    assert bench.read_traffic("k", "other", "abc") is None
+    (fake_root / "profiles" / "traffic_k_wl.txt").write_text("source_hash = abc\n")
+    assert bench.read_traffic("k", "wl", "abc") is None
