@@ -75,6 +75,8 @@ def test_fp8_weights_exact(zq, N, K, G, dt, smooth):
     (16, 28672, ref.PRE_GELU, np.float16, False),      # row over many workgroups
     (5, 10240, ref.PRE_LAYERNORM, np.float16, True),   # 16 waves per token
     (50, 1040, ref.PRE_NONE, np.float16, False),
+    (100, 5120, ref.PRE_LAYERNORM, np.float16, True),  # four waves per token, 3 pieces
+    (80, 3072, ref.PRE_GELU, np.float16, False),       # four waves per token, 2 pieces
 ])
 def test_fp8_prologue(zq, M, K, pre, dt, affine):
     say("fp8 prologue", M, K, pre, dt.__name__)

@@ -220,6 +220,15 @@ PROLOGUE_CASES = [
     (3, 4080, ref.PRE_GELU, np.float16, False),      # just below the long-row threshold
     (11, 12304, ref.PRE_LAYERNORM, np.float32, True),
     (1, 131072, ref.PRE_GELU, np.float16, False),
+    # fp16 rows of at most 8192 elements and more than 64 tokens (the per-op
+    # kernel): each piece count per lane, a last piece holding 2 of 256 chunks,
+    # token counts that leave a partial block
+    (101, 2048, ref.PRE_LAYERNORM, np.float16, True),   # one wave per token, 4 pieces
+    (70, 2064, ref.PRE_LAYERNORM, np.float16, True),    # four waves, 2 pieces, ragged
+    (90, 5120, ref.PRE_GELU, np.float16, False),        # 3 pieces
+    (67, 6160, ref.PRE_NONE, np.float16, False),        # 4 pieces, ragged
+    (130, 8192, ref.PRE_LAYERNORM, np.float16, True),   # 4 whole pieces
+    (66, 1040, ref.PRE_NONE, np.float16, False),        # one wave per token, 3 pieces
 ]
 
 
