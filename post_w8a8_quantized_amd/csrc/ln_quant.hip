@@ -1098,17 +1098,19 @@ hipError_t launch_rows(const T *X, int64_t M, int64_t K, int pre, const float *g
                        int32_t *slot = nullptr, _Float16 *XO = nullptr)
 {
     if constexpr (std::is_same<T, _Float16>::value && !OUT_F16 && DEC == 0) {
+        // fp16 rows up to 8192 elements to codes: k_ln_quant_f16
         if (K <= 2048)
             return launch_f16<1, 4, FP8>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream);
         if (K <= 8192)
             return launch_f16<4, 1, FP8>(X, M, K, pre, gamma, beta, eps, Xq, sx, stream);
+    } else {
+        if (K <= 2048)
+            return launch_cfg<T, 1, 4, OUT_F16, FP8, DEC, 4>(X, M, K, pre, gamma, beta, eps, Xq,
+                                                             sx, stream, Y16, alpha, slot, XO);
+        if (K <= 8192)
+            return launch_cfg<T, 4, 1, OUT_F16, FP8, DEC, 4>(X, M, K, pre, gamma, beta, eps, Xq,
+                                                             sx, stream, Y16, alpha, slot, XO);
     }
-    if (K <= 2048)
-        return launch_cfg<T, 1, 4, OUT_F16, FP8, DEC, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx,
-                                                         stream, Y16, alpha, slot, XO);
-    if (K <= 8192)
-        return launch_cfg<T, 4, 1, OUT_F16, FP8, DEC, 4>(X, M, K, pre, gamma, beta, eps, Xq, sx,
-                                                         stream, Y16, alpha, slot, XO);
     return launch_cfg<T, 16, 1, OUT_F16, FP8, DEC, 16>(X, M, K, pre, gamma, beta, eps, Xq, sx,
                                                        stream, Y16, alpha, slot, XO);
 }
