@@ -229,6 +229,8 @@ PROLOGUE_CASES = [
     (67, 6160, ref.PRE_NONE, np.float16, False),        # 4 pieces, ragged
     (130, 8192, ref.PRE_LAYERNORM, np.float16, True),   # 4 whole pieces
     (66, 1040, ref.PRE_NONE, np.float16, False),        # one wave per token, 3 pieces
+    (1, 768, ref.PRE_LAYERNORM, np.float16, True),      # one token: three idle waves
+    (2, 4080, ref.PRE_NONE, np.float16, False),         # two tokens of four waves each
 ]
 
 
