@@ -198,7 +198,11 @@ def settle_and_sample(torch, g, seconds=2.0, sample=True):
 
     def sampler():
         while not stop[0]:
-            r = subprocess.run(cmd + ["metric", "-p", "-c", "--csv"], capture_output=True, text=True)
+            try:
+                r = subprocess.run(cmd + ["metric", "-p", "-c", "--csv"], capture_output=True,
+                                   text=True, timeout=10)
+            except (subprocess.TimeoutExpired, OSError):
+                return
             lines = [ln for ln in r.stdout.strip().splitlines() if ln.strip()]
             if len(lines) >= 2:
                 rows.append(dict(zip(lines[0].split(","), lines[-1].split(","))))
@@ -213,13 +217,13 @@ def settle_and_sample(torch, g, seconds=2.0, sample=True):
         g.replay()
         torch.cuda.synchronize()
     stop[0] = True
-    # keep the GPU busy until the sampler's last amd-smi call has returned, so
-    # that no idle time separates this from the warmup replays
-    while th is not None and th.is_alive():
+    # keep the GPU busy until the sampler's last amd-smi call has returned (each
+    # call is bounded), so that no idle time separates this from the warmup replays
+    while th is not None and th.is_alive() and time.perf_counter() - t0 < seconds + 15.0:
         g.replay()
         torch.cuda.synchronize()
     if th:
-        th.join()
+        th.join(timeout=15.0)
     if not cmd:
         return None
     rows = rows[2:-1] if len(rows) > 4 else rows   # drop the ramp at both ends
