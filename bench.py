@@ -208,7 +208,7 @@ def settle_and_sample(torch, g, seconds=2.0, sample=True):
                 rows.append(dict(zip(lines[0].split(","), lines[-1].split(","))))
             time.sleep(0.2)
 
-    th = threading.Thread(target=sampler) if cmd else None
+    th = threading.Thread(target=sampler, daemon=True) if cmd else None
     torch.cuda.synchronize()
     if th:
         th.start()
