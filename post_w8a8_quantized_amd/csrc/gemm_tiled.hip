@@ -100,8 +100,10 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     tn = r / gm;
 }
 
-// Every configuration runs two waves per SIMD (eight-wave workgroups, or two
-// four-wave workgroups of the small tile per CU): 256 registers per wave.
+// Every configuration is built for two waves per SIMD (eight-wave workgroups,
+// or two four-wave workgroups of the small tile per CU): 256 registers per
+// wave.  The tail tile of the round split holds 120 KB of LDS, so it runs one
+// four-wave workgroup per CU.
 constexpr int kWavesPerSimd = 2;
 
 // F8: the operands are OCP E4M3 codes and the product is
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(WM *WN * 64)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_tiled(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int M, int N, int K,
-    void *__restrict__ Y, int tiles_m, int tiles_n, float *__restrict__ row_part,
+    void *__restrict__ Y, int ldy, int tiles_m, int tiles_n, float *__restrict__ row_part,
     int part_groups, OutlierOperands dec)
 {
     using C = Cfg<BM, BN, WM, WN, BK, NSTAGE>;
@@ -431,7 +433,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
                     using Raw4 = std::conditional_t<F8, v4f, v4i>;
                     const Raw4 o = {acc[a][b][4 * q + 0], acc[a][b][4 * q + 1],
                                     acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
-                    *reinterpret_cast<Raw4 *>(static_cast<int32_t *>(Y) + (int64_t)m * N + n) = o;
+                    *reinterpret_cast<Raw4 *>(static_cast<int32_t *>(Y) + (int64_t)m * ldy + n) = o;
                 }
         }
         return;
@@ -451,7 +453,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
     int8_t *const stage_out =
         (wb == 0 ? lds0 : wb == 1 ? lds1 : wb == 2 ? lds2 : lds3) + (wave / NSTAGE) * 32 * RS;
     _Float16 *const Yh = static_cast<_Float16 *>(Y);
-    const bool rows16 = (N & 7) == 0;            // 16-byte aligned rows of Y
+    const bool rows16 = (ldy & 7) == 0;          // 16-byte aligned rows of Y
 
     if constexpr (ODEC) {
         // Dequantize in place: from here on acc holds fp32 bits.
@@ -635,7 +637,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
                 const int n = n0 + wn * C::TWN + 8 * c;
                 if (CHECK && m >= M)
                     continue;
-                _Float16 *dst = Yh + (int64_t)m * N + n;
+                _Float16 *dst = Yh + (int64_t)m * ldy + n;
                 // Non-temporal stores: nothing in this kernel reads Y again, and
                 // the whole tile's output leaves at once at the end of the
                 // tile (measured: BERT FFN-up GEMM 25.1 -> 22.3 us, GPT QKV
@@ -670,17 +672,22 @@ template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool F8 = false, b
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
                       void *Y, bool out_i32, hipStream_t stream, float *row_part,
-                      const OutlierOperands *dec = nullptr)
+                      const OutlierOperands *dec = nullptr, int64_t ldy = -1,
+                      int part_groups = -1)
 {
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)(tiles_m * tiles_n));
     const dim3 block(WM * WN * 64);
     const OutlierOperands od = dec ? *dec : OutlierOperands{nullptr, nullptr, nullptr};
+    // ldy: Y's row stride in elements (N unless this launch covers a column
+    // range of a wider Y); part_groups: row_part's row stride in groups.
+    const int y_stride = (int)(ldy < 0 ? N : ldy);
+    const int groups = part_groups < 0 ? tiles_n * WN : part_groups;
 #define ZQ_GEMM_LAUNCH(I32, A, D)                                                                 \
     hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, BK, NSTAGE, I32, A, F8, D>), grid, block, 0,  \
-                       stream, Xq, sx, Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y, tiles_m,  \
-                       tiles_n, row_part, tiles_n * WN, od)
+                       stream, Xq, sx, Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y, y_stride, \
+                       tiles_m, tiles_n, row_part, groups, od)
     if constexpr (ODEC) {
         static_assert(!F8, "the outlier epilogue follows the int8 GEMM");
         if (act == 1)
@@ -750,7 +757,41 @@ hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8
 #define ZQ_CFG(BM, BN, WM, WN, BK, NS)                                                           \
     launch_cfg<BM, BN, WM, WN, BK, NS>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K, Y,      \
                                        out_i32, stream, row_part)
-    switch (pick_tile(M, N)) {
+    const int tile = pick_tile(M, N);
+    if (tile == 1 && row_part == nullptr) {
+        // 256x256 tiles whose last round would be at most half full: the columns
+        // up to the last whole round stay 256x256, the rest go to a second
+        // launch of 128x192 tiles that spreads them over the whole device (a
+        // partly filled round costs nearly a full one).  That launch has at
+        // most one workgroup per CU, so its tile takes four waves of 64x96 (six
+        // MFMA blocks per five fragment loads) and a three-slab pipeline.
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            cus > 0) {
+            const int64_t tiles_m = (M + 255) / 256;
+            const int64_t total = tiles_m * ((N + 255) / 256);
+            const int64_t rounds = total / cus;
+            const int64_t n_split = rounds * cus / tiles_m * 256;
+            const int64_t tail_tiles = (M + 127) / 128 * ((N - n_split + 191) / 192);
+            if (rounds >= 1 && 2 * (total - rounds * cus) <= cus && n_split > 0 && n_split < N &&
+                n_split % G == 0 && tail_tiles <= cus) {
+                const size_t el = out_i32 ? sizeof(int32_t) : sizeof(_Float16);
+                hipError_t e = launch_cfg<256, 256, 4, 2, 128, 2>(
+                    Xq, x_scales, Wq, w_scales, G, bias, act, M, n_split, K, Y, out_i32, stream,
+                    nullptr, nullptr, N);
+                if (e != hipSuccess)
+                    return e;
+                return launch_cfg<128, 192, 2, 2, 128, 3>(
+                    Xq, x_scales, Wq + n_split * K, w_scales ? w_scales + n_split / G : nullptr, G,
+                    bias ? bias + n_split : nullptr, act, M, N - n_split, K,
+                    static_cast<int8_t *>(Y) + n_split * el, out_i32, stream, nullptr, nullptr, N);
+            }
+        } else {
+            (void)hipGetLastError();
+        }
+    }
+    switch (tile) {
     case 0: return ZQ_CFG(256, 192, 4, 2, 128, 2);
     case 1: return ZQ_CFG(256, 256, 4, 2, 128, 2);
     default: return ZQ_CFG(128, 128, 2, 2, 64, 4);

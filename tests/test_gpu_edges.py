@@ -4,7 +4,9 @@
   workloads (full size; the oracle takes sampled tokens, every output
   column) and at shapes that take each tile configuration, including tile
   counts that are not a multiple of the XCD count, ragged M and N tails and
-  a K that ends inside a slab.
+  a K that ends inside a slab, and where a partly filled last round of
+  256 x 256 tiles is split off into a second launch of 128 x 192 tiles (int32
+  and the fp16 dequant epilogue).
 - LayerNorm of rows whose values are all equal ("探秘Transformer系列之（36）"
   1.2.2: the quantizer follows the LayerNorm; a row of equal values has zero
   variance, so y = beta exactly): codes and scales must equal the oracle's
@@ -16,7 +18,7 @@ import numpy as np
 import pytest
 
 from oracle import ref
-from tests._match import assert_codes, assert_scales, say
+from tests._match import assert_codes, assert_scales, assert_y, say
 from zq_workloads import random_affine, random_int8
 
 pytestmark = pytest.mark.gpu
@@ -75,6 +77,51 @@ def test_gemm_int32_workload_shapes(zq, M, N, K):
     want = ref.gemm_i32(Xq[rows], Wq)
     bad = np.argwhere(got[rows] != want)
     assert bad.size == 0, f"{len(bad)} accumulators differ, first at (row {rows[bad[0][0]]}, col {bad[0][1]})"
+
+
+# Shapes whose 256 x 256 tiles would leave a last round at most half full, so
+# the columns past the last whole round go to a second launch of 128 x 192
+# tiles: ragged M, a ragged tail of columns, output rows only 8-byte aligned
+# (N % 8 == 4), a K that ends inside a slab, and the weight-group scales and
+# bias taken from the middle of their arrays in the second launch.
+ROUND_SPLIT = [
+    # M, N, K, G
+    (1796, 18436, 208, 4),
+    (4096, 13312, 1040, 128),
+]
+
+
+@pytest.mark.parametrize("M,N,K,G", ROUND_SPLIT)
+def test_gemm_round_split(zq, M, N, K, G):
+    say("round split", M, N, K, G)
+    rng = np.random.default_rng(M + 5 * N + 11 * K + G)
+    Xq = random_int8(rng, (M, K))
+    Wq = random_int8(rng, (N, K))
+    s_x = (np.exp(rng.standard_normal(M)) * 0.01).astype(np.float32)
+    s_w = (np.exp(rng.standard_normal(N // G)) * 2e-4).astype(np.float32)
+    bias = (0.01 * rng.standard_normal(N)).astype(np.float32)
+    rows = sample_rows(M, rng)
+    acc = ref.gemm_i32(Xq[rows], Wq)
+
+    got_i32 = host(zq.w8a8_gemm_dequant(dev(Xq), None, dev(Wq), None, G, out_dtype=torch.int32,
+                                        path=zq.PATH_TILED))
+    bad = np.argwhere(got_i32[rows] != acc)
+    assert bad.size == 0, f"{len(bad)} accumulators differ, first at (row {rows[bad[0][0]]}, col {bad[0][1]})"
+    del got_i32
+
+    for act in (0, 1):
+        want = ref.epilogue(acc, s_x[rows], s_w, G, bias, act)
+        guard = 4096
+        buf = torch.full((M * N + guard,), 7.0, dtype=torch.float16, device="cuda")
+        zq.w8a8_gemm_dequant(dev(Xq), dev(s_x), dev(Wq), dev(s_w), G, dev(bias), act,
+                             path=zq.PATH_TILED, out=buf[:M * N].view(M, N))
+        flat = host(buf)
+        assert np.all(flat[M * N:] == 7.0)
+        got = flat[:M * N].reshape(M, N)[rows]
+        assert_y(got, want)
+        ulp = np.spacing(np.abs(want).astype(np.float16)).astype(np.float64)
+        off = np.abs(got.astype(np.float64) - want.astype(np.float64)) > ulp
+        assert off.mean() <= 1e-3, off.mean()
 
 
 # ---------------------------------------------------------------- constant rows
