@@ -398,22 +398,31 @@ def kernel_times(torch, g_steps, ms_step, prologue, gemm, steps):
     graph, so the K steps run eagerly, the prologue and the GEMM as the two
     boundary calls with HIP events on the launch stream before, between and
     after them.  They are queued behind replays of the timed graph (at least
-    ~5 ms of GPU work), so the GPU never waits for the host and the kernels
-    run in the same back-to-back state as in the timed replay.  Returns
-    (prologue ms, GEMM ms, idle fraction of the steps' span)."""
+    ~25 ms of GPU work, far more than the host needs to queue the K steps,
+    with Python's garbage collector held off meanwhile), so the GPU never
+    waits for the host and the kernels run in the same back-to-back state as
+    in the timed replay.  Returns (prologue ms, GEMM ms, idle fraction of the
+    steps' span)."""
+    import gc
     import numpy as np
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    lead = max(1, -(-5.0 // (ms_step * steps)))
+    lead = max(1, -(-25.0 // (ms_step * steps)))
     torch.cuda.synchronize()
-    for _ in range(int(lead)):
-        g_steps.replay()
-    for i in range(steps):
-        a, b, c = ev[i]
-        a.record()
-        prologue(i)
-        b.record()
-        gemm(i)
-        c.record()
+    gc_was_on = gc.isenabled()
+    gc.disable()
+    try:
+        for _ in range(int(lead)):
+            g_steps.replay()
+        for i in range(steps):
+            a, b, c = ev[i]
+            a.record()
+            prologue(i)
+            b.record()
+            gemm(i)
+            c.record()
+    finally:
+        if gc_was_on:
+            gc.enable()
     torch.cuda.synchronize()
     pro = np.array([a.elapsed_time(b) for a, b, _ in ev])
     gem = np.array([b.elapsed_time(c) for _, b, c in ev])

@@ -139,8 +139,8 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
     // at the start so that they have arrived by the epilogue.
     constexpr int kOutCols = 64;
     __shared__ int out_cols[ODEC ? kOutCols + 1 : 1];
-    // ODEC, interior tiles with at most kPanel outlier columns (and N % 8 == 0,
-    // for 16-byte aligned weight rows): the tile's
+    // ODEC, interior tiles with at most kPanel outlier columns (and ldy % 8 ==
+    // 0, for 16-byte aligned weight rows): the tile's
     // outlier operands are copied HBM -> LDS by DMA during the main loop:
     // the weight panel [kPanel x BN] fp16 (row p = W16t[O_p, n0 .. n0 + BN)) and
     // the activation panel [BM x kPanel] fp16 (row m = XO[m0 + m, 0 .. kPanel)).
@@ -321,7 +321,8 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
     // too, and the final drain before the epilogue certainly does.  Lanes past
     // the outlier count (or past K in the activation rows) fetch the zero block.
     const int n_out = ODEC ? out_cols[0] : 0;
-    const bool use_panels = ODEC && n_out > 0 && n_out <= kPanel && n0 + BN <= N && (N & 7) == 0;
+    const bool use_panels =
+        ODEC && n_out > 0 && n_out <= kPanel && n0 + BN <= N && (ldy & 7) == 0;
     auto issue_panels = [&] {
         if constexpr (ODEC) {
             if (!use_panels)
@@ -333,7 +334,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
             for (int j = wave; j < NWD; j += C::NW) {
                 const int idx = j * 64 + lane;
                 const int p = idx / WCH, c = idx % WCH;
-                const _Float16 *src = p < n_out ? dec.wt + (int64_t)out_cols[1 + p] * N + n0 + 8 * c
+                const _Float16 *src = p < n_out ? dec.wt + (int64_t)out_cols[1 + p] * ldy + n0 + 8 * c
                                                 : reinterpret_cast<const _Float16 *>(g_zero16);
                 dma16(reinterpret_cast<const int8_t *>(src),
                       reinterpret_cast<int8_t *>(panel_w) + j * 1024);
@@ -557,7 +558,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_t
                     h8 v;
 #pragma unroll
                     for (int i = 0; i < 8; i++)
-                        v[i] = oc[i] >= 0 ? dec.wt[(int64_t)oc[i] * N + n] : (_Float16)0.0f;
+                        v[i] = oc[i] >= 0 ? dec.wt[(int64_t)oc[i] * ldy + n] : (_Float16)0.0f;
                     wo[h][a] = v;
                 }
             }
@@ -747,6 +748,50 @@ int pick_tile(int64_t M, int64_t N)
     return best;
 }
 
+// The round split.  A partly filled last round of tiles costs nearly a full
+// round, so when bm x bn tiles would leave a last round at most half full, the
+// columns up to the last whole round keep those tiles and the rest go to a
+// second launch of 128x192 tiles that spreads them over the whole device.
+// That launch has at most one workgroup per CU, so its tile takes four waves
+// of 64x96 (six MFMA blocks per five fragment loads) and a three-slab
+// pipeline.  Returns the first column of the second launch, or 0 when the
+// split does not apply (no whole round, a tail wider than one round of
+// 128x192 tiles, or a split inside a weight group).
+int64_t round_split_cols(int64_t M, int64_t N, int64_t G, int bm, int bn)
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int64_t tiles_m = (M + bm - 1) / bm;
+    const int64_t total = tiles_m * ((N + bn - 1) / bn);
+    const int64_t rounds = total / cus;
+    const int64_t n_split = rounds * cus / tiles_m * bn;
+    const int64_t tail_tiles = (M + 127) / 128 * ((N - n_split + 191) / 192);
+    if (rounds >= 1 && 2 * (total - rounds * cus) <= cus && n_split > 0 && n_split < N &&
+        n_split % G == 0 && tail_tiles <= cus)
+        return n_split;
+    return 0;
+}
+
+// Weight rows, weight-group scales, bias and output columns from column n0 on.
+struct TailOperands {
+    const int8_t *w;
+    const float *sw;
+    const float *bias;
+    void *y;
+};
+TailOperands tail_operands(const int8_t *Wq, const float *w_scales, const float *bias, void *Y,
+                           int64_t n0, int64_t K, int64_t G, bool out_4byte)
+{
+    const size_t el = out_4byte ? 4 : sizeof(_Float16);
+    return {Wq + n0 * K, w_scales ? w_scales + n0 / G : nullptr, bias ? bias + n0 : nullptr,
+            static_cast<int8_t *>(Y) + n0 * el};
+}
+
 }  // namespace
 
 hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8_t *Wq,
@@ -759,36 +804,17 @@ hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8
                                        out_i32, stream, row_part)
     const int tile = pick_tile(M, N);
     if (tile == 1 && row_part == nullptr) {
-        // 256x256 tiles whose last round would be at most half full: the columns
-        // up to the last whole round stay 256x256, the rest go to a second
-        // launch of 128x192 tiles that spreads them over the whole device (a
-        // partly filled round costs nearly a full one).  That launch has at
-        // most one workgroup per CU, so its tile takes four waves of 64x96 (six
-        // MFMA blocks per five fragment loads) and a three-slab pipeline.
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            cus > 0) {
-            const int64_t tiles_m = (M + 255) / 256;
-            const int64_t total = tiles_m * ((N + 255) / 256);
-            const int64_t rounds = total / cus;
-            const int64_t n_split = rounds * cus / tiles_m * 256;
-            const int64_t tail_tiles = (M + 127) / 128 * ((N - n_split + 191) / 192);
-            if (rounds >= 1 && 2 * (total - rounds * cus) <= cus && n_split > 0 && n_split < N &&
-                n_split % G == 0 && tail_tiles <= cus) {
-                const size_t el = out_i32 ? sizeof(int32_t) : sizeof(_Float16);
-                hipError_t e = launch_cfg<256, 256, 4, 2, 128, 2>(
-                    Xq, x_scales, Wq, w_scales, G, bias, act, M, n_split, K, Y, out_i32, stream,
-                    nullptr, nullptr, N);
-                if (e != hipSuccess)
-                    return e;
-                return launch_cfg<128, 192, 2, 2, 128, 3>(
-                    Xq, x_scales, Wq + n_split * K, w_scales ? w_scales + n_split / G : nullptr, G,
-                    bias ? bias + n_split : nullptr, act, M, N - n_split, K,
-                    static_cast<int8_t *>(Y) + n_split * el, out_i32, stream, nullptr, nullptr, N);
-            }
-        } else {
-            (void)hipGetLastError();
+        const int64_t n_split = round_split_cols(M, N, G, 256, 256);
+        if (n_split > 0) {
+            hipError_t e = launch_cfg<256, 256, 4, 2, 128, 2>(
+                Xq, x_scales, Wq, w_scales, G, bias, act, M, n_split, K, Y, out_i32, stream,
+                nullptr, nullptr, N);
+            if (e != hipSuccess)
+                return e;
+            const TailOperands t = tail_operands(Wq, w_scales, bias, Y, n_split, K, G, out_i32);
+            return launch_cfg<128, 192, 2, 2, 128, 3>(Xq, x_scales, t.w, t.sw, G, t.bias, act, M,
+                                                      N - n_split, K, t.y, out_i32, stream,
+                                                      nullptr, nullptr, N);
         }
     }
     switch (tile) {
@@ -819,9 +845,23 @@ hipError_t launch_gemm_tiled_decomp(const int8_t *Xq, const float *x_scales, con
     launch_cfg<BM, BN, WM, WN, BK, NS, false, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, \
                                                     N, K, Y, false, stream, nullptr, &dec)
     // The 256x256 tiles' slabs leave no LDS for the outlier panels: their
-    // problems take 256x192.
-    if (pick_tile(M, N) != 2)
+    // problems take 256x192, with the round split.
+    if (pick_tile(M, N) != 2) {
+        const int64_t n_split = round_split_cols(M, N, G, 256, 192);
+        if (n_split > 0) {
+            hipError_t e = launch_cfg<256, 192, 4, 2, 128, 2, false, true>(
+                Xq, x_scales, Wq, w_scales, G, bias, act, M, n_split, K, Y, false, stream,
+                nullptr, &dec, N);
+            if (e != hipSuccess)
+                return e;
+            const TailOperands t = tail_operands(Wq, w_scales, bias, Y, n_split, K, G, false);
+            const OutlierOperands tail_dec{cols, XO, W16t + n_split};
+            return launch_cfg<128, 192, 2, 2, 128, 3, false, true>(
+                Xq, x_scales, t.w, t.sw, G, t.bias, act, M, N - n_split, K, t.y, false, stream,
+                nullptr, &tail_dec, N);
+        }
         return ZQ_CFGD(256, 192, 4, 2, 128, 2);
+    }
     return ZQ_CFGD(128, 128, 2, 2, 64, 4);
 #undef ZQ_CFGD
 }
@@ -838,8 +878,21 @@ hipError_t launch_gemm_tiled_fp8(const int8_t *Xq, const float *x_scales, const 
 #define ZQ_CFG8(BM, BN, WM, WN)                                                                   \
     launch_cfg<BM, BN, WM, WN, 128, 2, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K,   \
                                              Y, out_raw, stream, nullptr)
-    if (pick_tile(M, N) != 2)
+    if (pick_tile(M, N) != 2) {
+        const int64_t n_split = round_split_cols(M, N, G, 256, 192);
+        if (n_split > 0) {
+            hipError_t e = launch_cfg<256, 192, 4, 2, 128, 2, true>(
+                Xq, x_scales, Wq, w_scales, G, bias, act, M, n_split, K, Y, out_raw, stream,
+                nullptr, nullptr, N);
+            if (e != hipSuccess)
+                return e;
+            const TailOperands t = tail_operands(Wq, w_scales, bias, Y, n_split, K, G, out_raw);
+            return launch_cfg<128, 192, 2, 2, 128, 3, true>(Xq, x_scales, t.w, t.sw, G, t.bias,
+                                                            act, M, N - n_split, K, t.y, out_raw,
+                                                            stream, nullptr, nullptr, N);
+        }
         return ZQ_CFG8(256, 192, 4, 2);
+    }
     return ZQ_CFG8(128, 128, 2, 2);
 #undef ZQ_CFG8
 }

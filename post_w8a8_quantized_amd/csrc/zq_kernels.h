@@ -11,7 +11,8 @@ namespace zq {
 // The fp16 part of the mixed-precision decomposition, as the GEMM epilogues
 // read it: cols[0] = P, cols[1 + p] = the p-th outlier column; xo [M x K]
 // fp16 holds token m's value of column cols[1 + p] at xo[m * K + p]; wt
-// [K x N] fp16 is W transposed.
+// [K x N] fp16 is W transposed (for a launch over a column range of Y, wt
+// points at the range's first column and its rows keep Y's row stride).
 struct OutlierOperands {
     const int32_t *cols;
     const _Float16 *xo;

@@ -224,6 +224,35 @@ def test_gemm_decomp_on_oracle_operands(zq, M, N, K, G, act, bias, frac, gain, a
     assert_y(host(got), want)
 
 
+# Shapes whose 256 x 192 tiles would leave a last round at most half full, so
+# the columns past the last whole round go to a second launch of 128 x 192
+# tiles: a 4-column tail whose output rows (N % 8 == 4) rule out the LDS
+# panels, and a 1024-column tail whose interior tiles take them (P <= 32).
+# Sampled tokens, every column.
+@pytest.mark.parametrize("M,N,K,G,act,frac,seed", [
+    (1796, 18436, 256, 4, ref.ACT_GELU, 0.03, 31),
+    (4096, 13312, 256, 128, ref.ACT_NONE, 0.04, 32),
+])
+def test_gemm_decomp_round_split(zq, M, N, K, G, act, frac, seed):
+    say("decomp gemm round split", M, N, K, G, act, frac, seed)
+    inp = make_inputs(workload(M, K, N, G, "f16", ref.PRE_LAYERNORM, act, True, frac, 40.0, seed))
+    Y, cols, Xq, s_x, Wq, s_w = _oracle_operands(inp.X, inp.W, ref.PRE_LAYERNORM, G, ALPHA)
+    assert 0 < cols.size <= 32
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.integers(0, M, 32)]))
+    acc = ref.gemm_i32(Xq[rows], Wq)
+    want = ref.decomp_epilogue(acc, s_x[rows], s_w, G, Y[rows], cols, inp.W, inp.bias, act)
+    XO = np.zeros((M, K), dtype=np.float16)
+    XO[:, :cols.size] = ref.round_to_f16(Y[:, cols]).astype(np.float16)
+    cl = np.zeros(K + 1, dtype=np.int32)
+    cl[0] = cols.size
+    cl[1:1 + cols.size] = cols
+    Wt = np.ascontiguousarray(ref.round_to_f16(inp.W).astype(np.float16).T)
+    got = zq.w8a8_gemm_decomp(dev(Xq), dev(s_x), dev(Wq), dev(s_w), G, dev(cl), dev(XO), dev(Wt),
+                              dev(inp.bias), act)
+    assert_y(host(got)[rows], want)
+
+
 # (M, N, K, G, pre, act, x dtype, bias, outlier fraction, gain, seed)
 LAYER_CASES = [
     (200, 256, 1024, 1, ref.PRE_LAYERNORM, ref.ACT_NONE, "f16", True, 0.01, 60.0, 21),

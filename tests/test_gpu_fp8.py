@@ -219,6 +219,33 @@ def test_fp8_gemm_epilogue(zq, M, N, K, G, act):
     assert_y(Y, ref.epilogue_f64acc(ref.gemm_fp8(q_ref, wq_ref), s_ref, sw_ref, G, bias, act))
 
 
+# Shapes whose 256 x 192 tiles would leave a last round at most half full, so
+# the columns past the last whole round go to a second launch of 128 x 192
+# tiles: a 4-column tail with ragged M, and a 1024-column tail (ragged against
+# 192) whose weight-group scales and bias start at column 12288; K ends half
+# way into a 128-byte slab.
+@pytest.mark.parametrize("M,N,K,G", [(1796, 18436, 320, 4), (4096, 13312, 1088, 128)])
+def test_fp8_gemm_round_split(zq, M, N, K, G):
+    say("fp8 round split", M, N, K, G)
+    rng = np.random.default_rng(M + 7 * N + K + G)
+    Xq = random_codes(rng, (M, K))
+    Wq = random_codes(rng, (N, K))
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.integers(0, M, 32)]))
+    want_acc = ref.gemm_fp8(Xq[rows], Wq)
+    acc = host(zq.fp8_gemm_dequant(dev(Xq), None, dev(Wq), None, G, out_dtype=torch.float32))
+    bound = fp8_accumulation_bound(Xq[rows], Wq, 64)
+    err = np.abs(acc[rows].astype(np.float64) - want_acc)
+    say(f"fp8 split acc: largest error {np.max(err / bound):.3f} of the bound")
+    assert np.all(err <= bound)
+    del acc
+    s_x = (np.exp(rng.standard_normal(M)) * 0.01).astype(np.float32)
+    s_w = (np.exp(rng.standard_normal(N // G)) * 2e-4).astype(np.float32)
+    bias = (0.01 * rng.standard_normal(N)).astype(np.float32)
+    for act in (0, 1):
+        Y = host(zq.fp8_gemm_dequant(dev(Xq), dev(s_x), dev(Wq), dev(s_w), G, dev(bias), act))
+        assert_y(Y[rows], ref.epilogue_f64acc(want_acc, s_x[rows], s_w, G, bias, act))
+
+
 @pytest.mark.parametrize("name", ["tiny", "bert_ffn_up", "decode_ffn_down"])
 def test_fp8_layer_workloads(zq, name):
     """The FP8 layer at the workload's size (tokens sampled for the oracle),
