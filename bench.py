@@ -402,7 +402,7 @@ def kernel_times(torch, g_steps, ms_step, prologue, gemm, steps):
     with Python's garbage collector held off meanwhile), so the GPU never
     waits for the host and the kernels run in the same back-to-back state as
     in the timed replay.  Returns (prologue ms, GEMM ms, idle fraction of the
-    steps' span)."""
+    steps' span, [p10, p50, p90] of the GEMM's per-step durations in us)."""
     import gc
     import numpy as np
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -428,7 +428,8 @@ def kernel_times(torch, g_steps, ms_step, prologue, gemm, steps):
     gem = np.array([b.elapsed_time(c) for _, b, c in ev])
     span = ev[0][0].elapsed_time(ev[-1][2])
     gap = max(0.0, 1.0 - float(pro.sum() + gem.sum()) / span) if span > 0 else 0.0
-    return float(pro.mean()), float(gem.mean()), gap
+    spread = [round(float(np.percentile(gem, q)) * 1e3, 3) for q in (10, 50, 90)]
+    return float(pro.mean()), float(gem.mean()), gap, spread
 
 
 def time_layer(torch, zq, st, args, sample=False):
@@ -484,7 +485,8 @@ def time_layer(torch, zq, st, args, sample=False):
     ms_step = ms_ev / args.steps
     reps = np.array([ms_step] + [time_graph(torch, g_steps)[0] / args.steps for _ in range(9)])
     p10, p50, p90 = np.percentile(reps * 1e3, [10, 50, 90])
-    pro_ms, gemm_ms, gap = kernel_times(torch, g_steps, ms_step, prologue, gemm, args.steps)
+    pro_ms, gemm_ms, gap, gemm_spread = kernel_times(torch, g_steps, ms_step, prologue, gemm,
+                                                     args.steps)
     del g_steps
     torch.cuda.synchronize()
 
@@ -515,6 +517,7 @@ def time_layer(torch, zq, st, args, sample=False):
     roofline["launch_timing"] = ("HIP events around each launch in K eager layer steps queued "
                                  "behind replays of the timed graph; GPU idle between the "
                                  f"step's kernels: {gap * 100:.2f}% of the steps' span")
+    roofline["launch_us_p10_p50_p90"] = gemm_spread
     return dict(ms_step=ms_step, ms_wall=ms_wall, pro_ms=pro_ms, gemm_ms=gemm_ms, value=value,
                 nsets=nsets, clock_power=clock_power,
                 unit=unit, peak=peak, ops=ops, bytes_pro=bytes_pro, bytes_gemm=bytes_gemm,

@@ -712,12 +712,12 @@ struct Shape {
 };
 // Tile configurations (waves: WM x WN; slab: BK bytes, NSTAGE deep):
 //  0: 256x192, 4x2 waves, 128 B x2    1: 256x256, 4x2 waves, 128 B x2
-//  2: 128x128, 2x2 waves, 64 B x4
-constexpr int kNumShapes = 3;
-constexpr Shape kShapes[kNumShapes] = {{256, 192}, {256, 256}, {128, 128}};
+//  2: 128x128, 2x2 waves, 64 B x4    3: 128x96, 4x1 waves, 128 B x3
+constexpr int kNumShapes = 4;
+constexpr Shape kShapes[kNumShapes] = {{256, 192}, {256, 256}, {128, 128}, {128, 96}};
 
 // Bigger tiles move fewer bytes from L2 per MFMA; the choice trades that
-// against how evenly the tiles fill 256 CUs.  ZQ_GEMM_TILE=0..2 forces one
+// against how evenly the tiles fill 256 CUs.  ZQ_GEMM_TILE=0..3 forces one
 // (a measurement aid).
 int pick_tile(int64_t M, int64_t N)
 {
@@ -730,9 +730,11 @@ int pick_tile(int64_t M, int64_t N)
     const double cus = 256.0;
     // Measured on MI355X: 256x256 does ~10% more work per unit of time than
     // 256x192 when both fill their rounds equally (outlier shape 274 vs 284 us),
-    // 128x128 ~25% less (it covers small problems).  Score = weight x the
-    // fraction of the rounds' CU slots that tiles fill.
-    const double weight[kNumShapes] = {1.0, 1.1, 0.7};
+    // 128x128 ~25% less (it covers small problems), 128x96 ~0.83 of 128x128
+    // (4096 x 3072 -> 768: 256 tiles of 128x96 in 16.2-16.7 us against 192
+    // tiles of 128x128 in 17.8-18.1 us).  Score = weight x the fraction of the
+    // rounds' CU slots that tiles fill.
+    const double weight[kNumShapes] = {1.0, 1.1, 0.7, 0.58};
     int best = 2;
     double best_score = -1.0;
     for (int i = 0; i < kNumShapes; i++) {
@@ -820,6 +822,7 @@ hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8
     switch (tile) {
     case 0: return ZQ_CFG(256, 192, 4, 2, 128, 2);
     case 1: return ZQ_CFG(256, 256, 4, 2, 128, 2);
+    case 3: return ZQ_CFG(128, 96, 4, 1, 128, 3);
     default: return ZQ_CFG(128, 128, 2, 2, 64, 4);
     }
 #undef ZQ_CFG
@@ -830,6 +833,7 @@ int64_t gemm_tiled_row_groups(int64_t M, int64_t N)
     switch (pick_tile(M, N)) {
     case 0: return (N + 191) / 192 * 2;   // 256x192, two waves across
     case 1: return (N + 255) / 256 * 2;   // 256x256, two waves across
+    case 3: return (N + 95) / 96;         // 128x96, one wave across
     default: return (N + 127) / 128 * 2;  // 128x128, two waves across
     }
 }
@@ -845,8 +849,9 @@ hipError_t launch_gemm_tiled_decomp(const int8_t *Xq, const float *x_scales, con
     launch_cfg<BM, BN, WM, WN, BK, NS, false, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, \
                                                     N, K, Y, false, stream, nullptr, &dec)
     // The 256x256 tiles' slabs leave no LDS for the outlier panels: their
-    // problems take 256x192, with the round split.
-    if (pick_tile(M, N) != 2) {
+    // problems take 256x192, with the round split; 128x128 covers the problems
+    // of the small tiles.
+    if (pick_tile(M, N) <= 1) {
         const int64_t n_split = round_split_cols(M, N, G, 256, 192);
         if (n_split > 0) {
             hipError_t e = launch_cfg<256, 192, 4, 2, 128, 2, false, true>(
@@ -874,11 +879,12 @@ hipError_t launch_gemm_tiled_fp8(const int8_t *Xq, const float *x_scales, const 
     // FP8 k-steps are 64 bytes: only the 128-byte slab configurations apply
     // (two k-steps per slab).  The FP8 fragments are twice as wide, so the
     // 256x256 tile would not fit the registers of two waves per SIMD: its
-    // problems take 256x192; 128x128 covers small problems.
+    // problems take 256x192 (with the round split); 128x128 covers the
+    // problems of the small tiles.
 #define ZQ_CFG8(BM, BN, WM, WN)                                                                   \
     launch_cfg<BM, BN, WM, WN, 128, 2, true>(Xq, x_scales, Wq, w_scales, G, bias, act, M, N, K,   \
                                              Y, out_raw, stream, nullptr)
-    if (pick_tile(M, N) != 2) {
+    if (pick_tile(M, N) <= 1) {
         const int64_t n_split = round_split_cols(M, N, G, 256, 192);
         if (n_split > 0) {
             hipError_t e = launch_cfg<256, 192, 4, 2, 128, 2, true>(

@@ -1,8 +1,9 @@
 """Parity of each HIP entry point with the CPU oracle, through the C ABI.
 
-Sizes span several tiles and ragged tails of the tiled GEMM (128 x 128 output
-tiles, 64-byte k slabs) and of the skinny GEMM (16-row blocks, 64-byte k
-blocks split over 8 waves), plus the degenerate cases of the method.
+Sizes span several tiles and ragged tails of the tiled GEMM (each of its tile
+shapes: 256 x 256, 256 x 192, 128 x 128 and 128 x 96, with 64- or 128-byte k
+slabs) and of the skinny GEMM (16-row blocks, 64-byte k blocks split over 8
+waves), plus the degenerate cases of the method.
 """
 from __future__ import annotations
 
@@ -46,6 +47,7 @@ TILED_SHAPES = [
     (1000, 516, 784),
     (4096, 256, 128),
     (4096, 8180, 64),    # 256x256 tiles with 4x2 waves, ragged last column tile
+    (700, 300, 336),     # 128x96 tiles, ragged M, N and K
 ]
 
 
