@@ -43,6 +43,7 @@
 //    maxima, one per wave (for a downstream quantizer), and the
 //    mixed-precision decomposition's fp16 outlier part in the epilogue.
 
+#include <atomic>
 #include "zq_device.h"
 #include "zq_kernels.h"
 
@@ -83,6 +84,10 @@ struct Cfg {
     static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
     static_assert(NSTAGE >= 2 && NSTAGE <= 4, "pipeline depth");
     static_assert(BN <= NT, "column parameters are staged one per thread");
+    // Waves per SIMD the configuration runs at: eight-wave workgroups take a
+    // CU each (two waves per SIMD); four-wave ones two per CU when their slabs
+    // leave room for a second workgroup in the 160 KB of LDS, else one.
+    static constexpr int WPS = NW == 8 ? 2 : (2 * (NSTAGE * STAGE + 8 * 1024) <= 160 * 1024 ? 2 : 1);
 };
 
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
@@ -100,11 +105,10 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     tn = r / gm;
 }
 
-// Every configuration is built for two waves per SIMD (eight-wave workgroups,
-// or two four-wave workgroups of the small tile per CU): 256 registers per
-// wave.  The tail tile of the round split holds 120 KB of LDS, so it runs one
-// four-wave workgroup per CU.
-constexpr int kWavesPerSimd = 2;
+// Configurations run two waves per SIMD (eight-wave workgroups, or two
+// four-wave workgroups of the 128x128 tile per CU: 256 registers per wave),
+// or one where a four-wave tile's slabs fill more than half of the LDS (the
+// round split's 128x192 tail, the 128x96 tile: up to 512 registers).
 
 // F8: the operands are OCP E4M3 codes and the product is
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) accumulating in fp32;
@@ -119,7 +123,8 @@ constexpr int kWavesPerSimd = 2;
 template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool OUT_I32, int ACT, bool F8,
           bool ODEC = false>
 __global__ __launch_bounds__(WM *WN * 64)
-__attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_gemm_tiled(
+__attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS,
+                                    Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS))) void k_gemm_tiled(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int M, int N, int K,
     void *__restrict__ Y, int ldy, int tiles_m, int tiles_n, float *__restrict__ row_part,
@@ -716,9 +721,36 @@ struct Shape {
 constexpr int kNumShapes = 4;
 constexpr Shape kShapes[kNumShapes] = {{256, 192}, {256, 256}, {128, 128}, {128, 96}};
 
+// Compute units of the current device, queried once per device (256 on
+// MI355X, also the answer when no device can be queried).
+int device_cus()
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev >= 0 && dev < kMaxDevices)
+        cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 // Bigger tiles move fewer bytes from L2 per MFMA; the choice trades that
-// against how evenly the tiles fill 256 CUs.  ZQ_GEMM_TILE=0..3 forces one
-// (a measurement aid).
+// against how evenly the tiles fill the device's CUs.  ZQ_GEMM_TILE=0..3
+// forces one (a measurement aid).
 int pick_tile(int64_t M, int64_t N)
 {
     static const int forced = [] {
@@ -727,7 +759,7 @@ int pick_tile(int64_t M, int64_t N)
     }();
     if (forced >= 0 && forced < kNumShapes)
         return forced;
-    const double cus = 256.0;
+    const double cus = (double)device_cus();
     // Measured on MI355X: 256x256 does ~10% more work per unit of time than
     // 256x192 when both fill their rounds equally (outlier shape 274 vs 284 us),
     // 128x128 ~25% less (it covers small problems), 128x96 ~0.83 of 128x128
@@ -761,13 +793,7 @@ int pick_tile(int64_t M, int64_t N)
 // 128x192 tiles, or a split inside a weight group).
 int64_t round_split_cols(int64_t M, int64_t N, int64_t G, int bm, int bn)
 {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0) {
-        (void)hipGetLastError();
-        return 0;
-    }
+    const int64_t cus = device_cus();
     const int64_t tiles_m = (M + bm - 1) / bm;
     const int64_t total = tiles_m * ((N + bn - 1) / bn);
     const int64_t rounds = total / cus;
