@@ -635,9 +635,22 @@ def ffn_leg(torch, zq, st, args, dev):
             "chained_TOPS": round(ops_blk / (res["chained"] * 1e-3) / 1e12, 2)}
 
 
-def cpu_leg(zq, st, t, args):
+def cpu_model():
+    """The host CPU's model name (Linux), for the baseline's context."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_leg(zq, st, t, args, seconds=None):
     """The oracle on the host cores over all tokens of the workload, repeated
-    until args.cpu_seconds of wall time have passed (a reported baseline)."""
+    until `seconds` (default args.cpu_seconds) of wall time have passed (a
+    reported baseline); for few-token workloads also on one thread."""
     import numpy as np
     from oracle import ref
     w, inp, decode = st["w"], st["inp"], st["decode"]
@@ -662,11 +675,12 @@ def cpu_leg(zq, st, t, args):
         return round((t["bytes_layer"] / per / 1e9) if decode else (t["ops"] / per / 1e12), 4)
 
     cores = ref.max_threads()
-    passes, el = oracle_passes(args.cpu_seconds)
+    passes, el = oracle_passes(args.cpu_seconds if seconds is None else seconds)
     per = el / passes
     cpu = {"value": rate(per), "unit": t["unit"], "cores": cores, "kind": "oracle",
            "sample": f"all {w.M} tokens of the workload (prologue + int GEMM + epilogue), "
-                     f"{passes} passes, {per:.3f} s each, {el:.1f} s wall on {cores} threads"}
+                     f"{passes} passes, {per:.3f} s each, {el:.1f} s wall on {cores} threads",
+           "host": {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count()}}
     if decode:
         ref.set_threads(1)
         passes1, el1 = oracle_passes(3.0)
@@ -674,6 +688,18 @@ def cpu_leg(zq, st, t, args):
         cpu["one_thread"] = {"value": rate(el1 / passes1), "unit": t["unit"],
                              "sample": f"{passes1} passes, {el1 / passes1:.3f} s each"}
     return cpu
+
+
+def min_traffic(w, t):
+    """At decode shapes: the layer's rate over the bytes a single kernel would
+    move (X in, Y out, the weights, their scales and bias), i.e. without the
+    codes' and scales' round trip between the prologue and the GEMM."""
+    if t["unit"] != "GB/s":
+        return {}
+    min_bytes = t["bytes_layer"] - 2 * (w.M * w.K + 4 * w.M)
+    rate = min_bytes / (t["ms_step"] * 1e-3) / 1e9
+    return {"min_traffic_bytes": min_bytes, "min_traffic_GBps": round(rate, 1),
+            "min_traffic_frac_of_hbm": round(rate / PEAK_HBM_GBS, 4)}
 
 
 def summary(w, t):
@@ -686,6 +712,7 @@ def summary(w, t):
            "prologue_frac_of_hbm": round(t["bytes_pro"] / (t["pro_ms"] * 1e-3) / 1e9
                                          / PEAK_HBM_GBS, 4),
            "gemm_us": round(t["gemm_ms"] * 1e3, 3), "roofline": r,
+           **min_traffic(w, t),
            "config": {"M": w.M, "K": w.K, "N": w.N, "group_rows": w.group_rows,
                       "x_dtype": w.x_dtype, "pre": PRE_NAMES[w.pre], "act": ACT_NAMES[w.act],
                       "bias": w.has_bias, "smoothquant": w.smooth}}
@@ -750,6 +777,8 @@ def main():
                 others[name]["fp8_variant"] = fp8_leg(torch, zq, so, to, args, dev)
             if name == "bert_ffn_up" and not args.no_ffn:
                 others[name]["ffn_block"] = ffn_leg(torch, zq, so, args, dev)
+            if so["decode"] and not args.no_cpu_baseline:
+                others[name]["cpu_baseline"] = cpu_leg(zq, so, to, args, seconds=4.0)
             del so
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
@@ -794,6 +823,7 @@ def main():
                    "weights": "packed 32x512 blocks" if st_decode(w) else "row-major",
                    "rotated_sets": t.get("nsets"), "graph_steps": args.steps},
         "frac_of_peak": round(t["value"] / t["peak"], 4),
+        **min_traffic(w, t),
         "breakdown_us": {"layer_step": round(t["ms_step"] * 1e3, 3),
                          "prologue": round(t["pro_ms"] * 1e3, 3),
                          "gemm": round(t["gemm_ms"] * 1e3, 3),

@@ -62,3 +62,16 @@ def test_missing_or_malformed_summary(fake_root):
     assert bench.read_traffic("k", "other", "abc") is None
     (fake_root / "profiles" / "traffic_k_wl.txt").write_text("source_hash = abc\n")
     assert bench.read_traffic("k", "wl", "abc") is None
+
+
+def test_min_traffic_leaves_out_the_codes_round_trip():
+    class Decode:
+        M, K = 16, 28672
+    # the decode layer's bytes: X fp16, codes and scales out and back in, the
+    # packed weights with their group scales, Y fp16 (no bias)
+    X, codes, W, sw, Y = 16 * 28672 * 2, 16 * 28672 + 4 * 16, 8192 * 28672, 4 * 64, 16 * 8192 * 2
+    layer = X + 2 * codes + W + sw + Y
+    got = bench.min_traffic(Decode, {"unit": "GB/s", "bytes_layer": layer, "ms_step": 0.04})
+    assert got["min_traffic_bytes"] == X + W + sw + Y
+    assert abs(got["min_traffic_GBps"] - (X + W + sw + Y) / 40e-6 / 1e9) < 0.1
+    assert bench.min_traffic(Decode, {"unit": "TOPS", "bytes_layer": layer, "ms_step": 0.04}) == {}
