@@ -17,7 +17,10 @@
 //  - The prefill tiles (256x192 and 256x256) run eight waves, two per SIMD,
 //    each owning a 64x96 (or 128x64) output block: five or six 16-byte LDS
 //    reads per lane feed six or eight MFMAs per k-step.  128x128 tiles with
-//    four waves cover small problems.
+//    four waves cover small problems, 128x96 tiles (four waves of 32x96)
+//    grids that 128x128 tiles would leave short of a round.  A last round of
+//    large tiles at most half full is split off into a second launch of
+//    128x192 tiles (four waves of 64x96) over the whole device.
 //  - k slabs of BK bytes move HBM -> LDS with global_load_lds_dwordx4 (no
 //    VGPR staging, no ds_write): lane l of a wave-wide load lands at
 //    LDS[base + 16 l], so the bank swizzle is applied by choosing which
