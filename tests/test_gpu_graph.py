@@ -15,12 +15,14 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-@pytest.mark.parametrize("M", [16, 300])
-def test_graph_replays_match_eager(M):
+# (M, K, N, G): the weight-streaming and the tiled GEMM, and a shape whose GEMM
+# is the round split (two launches: 256x256 tiles, then 128x192 tiles)
+@pytest.mark.parametrize("M,K,N,G", [(16, 768, 512, 128), (300, 768, 512, 128),
+                                     (1796, 256, 18436, 4)])
+def test_graph_replays_match_eager(M, K, N, G):
     import post_w8a8_quantized_amd as zq
-    say("graph replay", M)
+    say("graph replay", M, K, N, G)
     rng = np.random.default_rng(M)
-    K, N, G = 768, 512, 128
     X = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float16)).cuda()
     g, b = (torch.from_numpy(a).cuda() for a in random_affine(rng, K))
     Wq = torch.from_numpy(random_int8(rng, (N, K))).cuda()
