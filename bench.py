@@ -705,7 +705,8 @@ def min_traffic(w, t):
 def summary(w, t):
     """One workload's figures as an extra key of the JSON line."""
     r = t["roofline"]
-    out = {"layer_step_us": round(t["ms_step"] * 1e3, 3), "value": round(t["value"], 2),
+    out = {"layer_step_us": round(t["ms_step"] * 1e3, 3), "layer_step_spread": t["spread"],
+           "value": round(t["value"], 2),
            "unit": t["unit"], "frac_of_peak": round(t["value"] / t["peak"], 4),
            "prologue_us": round(t["pro_ms"] * 1e3, 3),
            "prologue_GBps": round(t["bytes_pro"] / (t["pro_ms"] * 1e-3) / 1e9, 1),
