@@ -20,7 +20,10 @@
 //    four waves cover small problems, 128x96 tiles (four waves of 32x96)
 //    grids that 128x128 tiles would leave short of a round.  A last round of
 //    large tiles at most half full is split off into a second launch of
-//    128x192 tiles (four waves of 64x96) over the whole device.
+//    128x192 tiles over the whole device: eight waves, two groups of four
+//    64x96 blocks that take alternate halves of every slab's k-steps and add
+//    their int32 partial sums through LDS at the end (int8; the FP8 and
+//    outlier-part forms keep four waves).
 //  - k slabs of BK bytes move HBM -> LDS with global_load_lds_dwordx4 (no
 //    VGPR staging, no ds_write): lane l of a wave-wide load lands at
 //    LDS[base + 16 l], so the bank swizzle is applied by choosing which
@@ -67,9 +70,9 @@ __device__ __forceinline__ int swz(int row)
     return BK == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NSTAGE>
+template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, int KW = 1>
 struct Cfg {
-    static constexpr int NW = WM * WN;                // waves per workgroup
+    static constexpr int NW = WM * WN * KW;           // waves per workgroup
     static constexpr int NT = NW * 64;
     static constexpr int TWM = BM / WM;               // tokens per wave
     static constexpr int TWN = BN / WN;               // output columns per wave
@@ -81,6 +84,7 @@ struct Cfg {
     static constexpr int LW = BN / RPI / NW;          // DMAs per wave per slab, W
     static constexpr int STAGE = (BM + BN) * BK;      // bytes per slab
     static constexpr int KS = BK / 32;                // MFMA k-steps per slab
+    static_assert(KW == 1 || KW == 2, "one or two wave groups along k");
     static_assert(BK == 64 || BK == 128, "slab depth");
     static_assert(TWM % 32 == 0 && TWN % 32 == 0, "wave tile must be 32-aligned");
     static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "DMAs must divide evenly");
@@ -124,16 +128,17 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
 // sum_p XO[m, p] W16t[O_p, n] onto them: W16t is the A operand and XO the
 // B operand, so the fp16 product has the int8 accumulator layout.
 template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool OUT_I32, int ACT, bool F8,
-          bool ODEC = false>
-__global__ __launch_bounds__(WM *WN * 64)
-__attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS,
-                                    Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS))) void k_gemm_tiled(
+          bool ODEC = false, int KW = 1>
+__global__ __launch_bounds__(WM *WN *KW * 64)
+__attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE, KW>::WPS,
+                                    Cfg<BM, BN, WM, WN, BK, NSTAGE, KW>::WPS))) void k_gemm_tiled(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int G, const float *__restrict__ bias, int M, int N, int K,
     void *__restrict__ Y, int ldy, int tiles_m, int tiles_n, float *__restrict__ row_part,
     int part_groups, OutlierOperands dec)
 {
-    using C = Cfg<BM, BN, WM, WN, BK, NSTAGE>;
+    using C = Cfg<BM, BN, WM, WN, BK, NSTAGE, KW>;
+    static_assert(KW == 1 || (!ODEC && !F8), "k-split tiles: int8 without the outlier part");
     // One LDS object per slab buffer, referenced statically from an unrolled
     // main loop, so the compiler can tell a read of one buffer from the
     // in-flight DMAs into the others and need not wait for all of them.
@@ -165,8 +170,12 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS,
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
-    const int wm = wave % WM;
-    const int wn = wave / WM;
+    // KW = 2: waves wave and wave + WM * WN own the same output block and take
+    // the first and the second half of every slab's k-steps (wave group wk).
+    const int wk = KW == 1 ? 0 : wave / (WM * WN);
+    const int wo = KW == 1 ? wave : wave % (WM * WN);
+    const int wm = wo % WM;
+    const int wn = wo / WM;
 
     if (!OUT_I32 && tid < BN) {
         const int n = min(n0 + tid, N - 1);
@@ -236,6 +245,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS,
     // (one chunk).  FP8: a k-step is 64 bytes, lane holds bytes 32 fhalf .. +32 (two
     // chunks, each at its own swizzled position).
     constexpr int KS = F8 ? BK / 64 : BK / 32;
+    constexpr int KSW = KS / KW;   // k-steps per slab of one wave group
+    const int kbase = KW == 1 ? 0 : wk * KSW;
     using Acc = std::conditional_t<F8, v16f, v16i>;
     using Frag = std::conditional_t<F8, v8i, v4i>;
     Acc acc[C::FN][C::FM];
@@ -316,13 +327,13 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS,
     barrier();
 
     Frag fx[2][C::FM], fw[2][C::FN];
-    load_frags(bufs[0], 0, fx[0], fw[0]);
+    load_frags(bufs[0], kbase, fx[0], fw[0]);
 
-    // One slab: KS MFMA k-steps.  The LDS reads for the next k-step are issued
-    // before the current k-step's MFMAs.  Before the last k-step's MFMAs the
-    // slab hands over: wait for slab kt+1, barrier (after which this slab's
-    // buffer is free), refill it with slab kt+NSTAGE, read slab kt+1's first
-    // fragments.
+    // One slab: KS MFMA k-steps (with KW = 2, each wave group takes KS / 2 of
+    // them).  The LDS reads for the next k-step are issued before the current
+    // k-step's MFMAs.  Before the last k-step's MFMAs the slab hands over: wait
+    // for slab kt+1, barrier (after which this slab's buffer is free), refill
+    // it with slab kt+NSTAGE, read slab kt+1's first fragments.
     // The outlier panels go out with the first slab refill: by then the
     // outlier list is in LDS (the first barrier has passed).  They are the
     // youngest DMAs of that moment, so the slab waits that follow cover them
@@ -362,11 +373,12 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS,
     auto slab = [&](int kt, auto S) {
         constexpr int s = decltype(S)::value;
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-            const bool last = ks + 1 == KS;
-            // Fragments for the next k-step (this slab's, or the next slab's first).
+        for (int ks = 0; ks < KSW; ks++) {
+            const bool last = ks + 1 == KSW;
+            // Fragments for the wave group's next k-step (this slab's, or the
+            // next slab's first).
             const int8_t *nstage = last ? bufs[(s + 1) % NSTAGE] : bufs[s];
-            const int nks = last ? 0 : ks + 1;
+            const int nks = kbase + (last ? 0 : ks + 1);
             if (!last) {
                 // The reads feeding this k-step were issued a k-step ago.
                 __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -410,7 +422,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS,
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    static_assert(KS % 2 == 0, "fragment buffers alternate within a slab");
+    static_assert(KSW % 2 == 0, "fragment buffers alternate within a slab");
     for (int kt = 0; kt < nkp; kt += NSTAGE) {
         slab(kt, std::integral_constant<int, 0>{});
         slab(kt + 1, std::integral_constant<int, 1>{});
@@ -425,12 +437,63 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS,
     wait_vmcnt<0>();
     barrier();
 
+    // KW = 2: the two wave groups hold partial sums of the same output block
+    // over disjoint k-steps.  Fragment row b is finished by wave group b % 2:
+    // each wave hands its other rows to its partner through the (now free)
+    // slab buffers, 16 bytes per lane and store, and adds the partner's
+    // partials of its own rows (int32: exact in any order).
+    if constexpr (KW == 2) {
+        static_assert(C::FM % 2 == 0, "fragment rows split evenly between the wave groups");
+        constexpr int PART = C::FN * (C::FM / 2) * 16 * kWave * 4;  // bytes per wave
+        constexpr int PER_BUF = C::STAGE / PART;
+        static_assert(PER_BUF * NSTAGE >= C::NW, "every wave's partials fit the slab buffers");
+        auto region = [&](int r) {
+            const int bi = r / PER_BUF;
+            int8_t *b = bi == 0 ? lds0 : bi == 1 ? lds1 : bi == 2 ? lds2 : lds3;
+            return reinterpret_cast<v4i *>(b + (r % PER_BUF) * PART);
+        };
+        v4i *const give = region(wo + WM * WN * (1 - wk));  // read by the partner
+        const v4i *const take = region(wo + WM * WN * wk);  // written by the partner
+#pragma unroll
+        for (int a = 0; a < C::FN; a++)
+#pragma unroll
+            for (int b = 0; b < C::FM; b++) {
+                if (b % 2 == wk)
+                    continue;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    give[((a * (C::FM / 2) + b / 2) * 4 + q) * kWave + lane] =
+                        v4i{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                            acc[a][b][4 * q + 3]};
+            }
+        barrier();
+#pragma unroll
+        for (int a = 0; a < C::FN; a++)
+#pragma unroll
+            for (int b = 0; b < C::FM; b++) {
+                if (b % 2 != wk)
+                    continue;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const v4i p = take[((a * (C::FM / 2) + b / 2) * 4 + q) * kWave + lane];
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        acc[a][b][4 * q + i] += p[i];
+                }
+            }
+        barrier();  // the slab buffers stage the outputs below
+    }
+    // Rows of fragments this wave finishes.
+    auto own_row = [&](int b) { return KW == 1 || b % 2 == wk; };
+
     // Epilogue.  Accumulator register r of fragment (a, b) holds
     // token  m = m0 + wm*TWM + b*32 + lane%32 and
     // column n = n0 + wn*TWN + a*32 + 8*(r/4) + 4*(lane/32) + r%4.
     if constexpr (OUT_I32) {
 #pragma unroll
         for (int b = 0; b < C::FM; b++) {
+            if (!own_row(b))
+                continue;
             const int m = m0 + wm * C::TWM + b * 32 + frow;
 #pragma unroll
             for (int a = 0; a < C::FN; a++)
@@ -599,6 +662,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS,
         constexpr bool AMAX = decltype(fold_amax)::value;  // row_part given
 #pragma unroll
         for (int b = 0; b < C::FM; b++) {
+            if (!own_row(b))
+                continue;
             float rmax = 0.0f;
 #pragma unroll
             for (int a = 0; a < C::FN; a++) {
@@ -677,7 +742,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM, BN, WM, WN, BK, NSTAGE>::WPS,
     }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool F8 = false, bool ODEC = false>
+template <int BM, int BN, int WM, int WN, int BK, int NSTAGE, bool F8 = false, bool ODEC = false,
+          int KW = 1>
 hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                       int64_t G, const float *bias, int act, int64_t M, int64_t N, int64_t K,
                       void *Y, bool out_i32, hipStream_t stream, float *row_part,
@@ -687,18 +753,18 @@ hipError_t launch_cfg(const int8_t *Xq, const float *sx, const int8_t *Wq, const
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)(tiles_m * tiles_n));
-    const dim3 block(WM * WN * 64);
+    const dim3 block(WM * WN * KW * 64);
     const OutlierOperands od = dec ? *dec : OutlierOperands{nullptr, nullptr, nullptr};
     // ldy: Y's row stride in elements (N unless this launch covers a column
     // range of a wider Y); part_groups: row_part's row stride in groups.
     const int y_stride = (int)(ldy < 0 ? N : ldy);
     const int groups = part_groups < 0 ? tiles_n * WN : part_groups;
 #define ZQ_GEMM_LAUNCH(I32, A, D)                                                                 \
-    hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, BK, NSTAGE, I32, A, F8, D>), grid, block, 0,  \
-                       stream, Xq, sx, Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y, y_stride, \
-                       tiles_m, tiles_n, row_part, groups, od)
+    hipLaunchKernelGGL((k_gemm_tiled<BM, BN, WM, WN, BK, NSTAGE, I32, A, F8, D, KW>), grid, block, \
+                       0, stream, Xq, sx, Wq, sw, (int)G, bias, (int)M, (int)N, (int)K, Y,          \
+                       y_stride, tiles_m, tiles_n, row_part, groups, od)
     if constexpr (ODEC) {
-        static_assert(!F8, "the outlier epilogue follows the int8 GEMM");
+        static_assert(!F8 && KW == 1, "the outlier epilogue follows the int8 GEMM");
         if (act == 1)
             ZQ_GEMM_LAUNCH(false, 1, true);
         else
@@ -789,9 +855,11 @@ int pick_tile(int64_t M, int64_t N)
 // round, so when bm x bn tiles would leave a last round at most half full, the
 // columns up to the last whole round keep those tiles and the rest go to a
 // second launch of 128x192 tiles that spreads them over the whole device.
-// That launch has at most one workgroup per CU, so its tile takes four waves
-// of 64x96 (six MFMA blocks per five fragment loads) and a three-slab
-// pipeline.  Returns the first column of the second launch, or 0 when the
+// That launch has at most one workgroup per CU and a three-slab pipeline; its
+// waves own 64x96 blocks (six MFMA blocks per five fragment loads).  The int8
+// form runs two such waves per block, each over half of every slab's k-steps
+// (two waves per SIMD; at the outlier layer's shape 36.6 us per tail launch
+// against 37.4 us with four waves, medians of ~1140 traced dispatches each).  Returns the first column of the second launch, or 0 when the
 // split does not apply (no whole round, a tail wider than one round of
 // 128x192 tiles, or a split inside a weight group).
 int64_t round_split_cols(int64_t M, int64_t N, int64_t G, int bm, int bn)
@@ -843,9 +911,9 @@ hipError_t launch_gemm_tiled(const int8_t *Xq, const float *x_scales, const int8
             if (e != hipSuccess)
                 return e;
             const TailOperands t = tail_operands(Wq, w_scales, bias, Y, n_split, K, G, out_i32);
-            return launch_cfg<128, 192, 2, 2, 128, 3>(Xq, x_scales, t.w, t.sw, G, t.bias, act, M,
-                                                      N - n_split, K, t.y, out_i32, stream,
-                                                      nullptr, nullptr, N);
+            return launch_cfg<128, 192, 2, 2, 128, 3, false, false, 2>(
+                Xq, x_scales, t.w, t.sw, G, t.bias, act, M, N - n_split, K, t.y, out_i32, stream,
+                nullptr, nullptr, N);
         }
     }
     switch (tile) {
