@@ -16,7 +16,9 @@ leg: the dominant kernel's roofline, the fusion ablation, the FP8 variant and
 the CPU oracle on the host cores.  The other workloads (BERT FFN-up, GPT QKV,
 decode FFN-down) follow as extra keys, each with its layer time, fraction of
 peak and its dominant kernel's roofline, and the outlier workload is timed
-again under the mixed-precision decomposition.
+again under the mixed-precision decomposition.  For the prefill workloads the
+vendor library's int8 GEMM (torch._int_mm, hipBLASLt) is timed on the same
+codes for context (library_leg).
 
 The steps are captured in a HIP graph (on torch's stream, which is the
 stream the library launches on) so that host-side call overhead does not
@@ -77,6 +79,9 @@ def parse():
                          "0.5 s for the others); for profiler runs")
     ap.add_argument("--no-copy-reference", action="store_true",
                     help="skip the 1 GiB device-copy bandwidth reference")
+    ap.add_argument("--no-library-reference", action="store_true",
+                    help="skip the vendor int8 GEMM (torch._int_mm, hipBLASLt) comparison "
+                         "(prefill workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat full oracle passes until this much wall time has passed")
     ap.add_argument("--calib-copy-mb", type=float, default=0.0,
@@ -557,6 +562,73 @@ def fp8_leg(torch, zq, st, t, args, dev):
             "unit": "GB/s" if decode else "TOPS"}
 
 
+def library_leg(torch, zq, st, args, dev):
+    """Context, not the product path: the vendor library's int8 GEMM (torch._int_mm,
+    which runs hipBLASLt) on the layer's own codes and weights, int32 out, against
+    this library's GEMM on the same operands in its int32 test mode and with its
+    fused fp16 dequant epilogue.  Each is timed over `steps` eager launches queued
+    back to back (HIP events around them, rotated sets, after 0.3 s of untimed
+    launches), three rounds in alternation, median per launch.  Also checks that
+    the two int32 products agree bit for bit."""
+    w, sets, nsets = st["w"], st["sets"], st["nsets"]
+    M, N, K, G = w.M, w.N, w.K, w.group_rows
+    codes = [zq.ln_quant_per_token(s["X"], w.pre, st["g_arg"], st["b_arg"], w.eps) for s in sets]
+    y32 = torch.empty((M, N), dtype=torch.int32, device=dev)
+    y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+    torch.cuda.synchronize()
+    equal = bool(torch.equal(torch._int_mm(codes[0][0], sets[0]["Wq"].t()),
+                             zq.w8a8_gemm_dequant(codes[0][0], None, sets[0]["Wq"], None, G,
+                                                  out_dtype=torch.int32, out=y32)))
+
+    def lib(i):
+        torch._int_mm(codes[i % nsets][0], sets[i % nsets]["Wq"].t())
+
+    def ours32(i):
+        zq.w8a8_gemm_dequant(codes[i % nsets][0], None, sets[i % nsets]["Wq"], None, G,
+                             out_dtype=torch.int32, out=y32)
+
+    def ours16(i):
+        Xq, sx = codes[i % nsets]
+        zq.w8a8_gemm_dequant(Xq, sx, sets[i % nsets]["Wq"], sets[i % nsets]["s_w"], G,
+                             st["bias"], w.act, out=y16)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            for i in range(nsets):
+                fn(i)
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    us = {"lib": [], "i32": [], "f16": []}
+    for _ in range(3):
+        us["lib"].append(timed(lib))
+        us["i32"].append(timed(ours32))
+        us["f16"].append(timed(ours16))
+    med = {k: sorted(v)[1] for k, v in us.items()}
+    ops = 2.0 * M * N * K
+    del codes, y32, y16
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"what": "torch._int_mm (hipBLASLt) int8 x int8 -> int32 on the layer's codes and "
+                    "weights vs this library's GEMM on the same operands; eager launches, "
+                    "context only",
+            "library_int32_us": round(med["lib"], 2),
+            "library_int32_TOPS": round(ops / (med["lib"] * 1e-6) / 1e12, 1),
+            "ours_int32_us": round(med["i32"], 2),
+            "ours_int32_TOPS": round(ops / (med["i32"] * 1e-6) / 1e12, 1),
+            "ours_fp16_dequant_us": round(med["f16"], 2),
+            "ours_int32_over_library_time": round(med["i32"] / med["lib"], 3),
+            "int32_results_equal": equal}
+
+
 def ablation_leg(torch, zq, st, t, args, dev):
     """The same layer in the unfused order (op -> fp16 -> quantizer -> int32 GEMM
     -> dequantizer), same rotated sets; the intermediates share one workspace."""
@@ -752,6 +824,9 @@ def main():
     if w.name == "bert_ffn_up" and not args.no_ffn:
         ffn = ffn_leg(torch, zq, st, args, dev)
     fp8 = None if args.no_fp8 else fp8_leg(torch, zq, st, t, args, dev)
+    libref = None
+    if not st["decode"] and not args.no_library_reference:
+        libref = library_leg(torch, zq, st, args, dev)
     cpu = None if args.no_cpu_baseline else cpu_leg(zq, st, t, args)
     del st
     torch.cuda.synchronize()
@@ -776,6 +851,8 @@ def main():
             others[name] = summary(wo, to)
             if not args.no_fp8:
                 others[name]["fp8_variant"] = fp8_leg(torch, zq, so, to, args, dev)
+            if not so["decode"] and not args.no_library_reference:
+                others[name]["library_reference"] = library_leg(torch, zq, so, args, dev)
             if name == "bert_ffn_up" and not args.no_ffn:
                 others[name]["ffn_block"] = ffn_leg(torch, zq, so, args, dev)
             if so["decode"] and not args.no_cpu_baseline:
@@ -835,6 +912,7 @@ def main():
         "cpu_baseline": cpu,
         "clock_power": t["clock_power"],
         "hbm_copy_reference": hbm_ref,
+        "library_reference": libref,
         "ablation": ablation,
         "ffn_block": ffn,
         "fp8_variant": fp8,
