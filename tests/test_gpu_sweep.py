@@ -1,0 +1,160 @@
+"""A seeded random sweep of the whole layer over its argument space, through
+the C ABI, against the oracle.
+
+Each case draws M, K, N, the group size G, the pre-op (none, LayerNorm,
+GeLU), the epilogue activation, the input dtype, whether LayerNorm has an
+affine and whether there is a bias, and (few tokens) row-major or packed
+weights ("探秘Transformer系列之（36）" 1.2.2: per-token activations, group-wise
+weights, the INT8 GEMM's INT32 accumulation scaled before the FP16 result).
+One call of the layer, then:
+
+- the weight codes and scales the library quantizes equal the oracle's;
+- the codes and per-token scales the layer leaves in its workspace follow
+  the prologue rules (codes +-1 on at most floor(1e-4 n) near-ties, scales
+  within 4 ulps);
+- the int32 GEMM on the workspace's own codes is bit-exact;
+- Y matches the oracle's layer (max and normwise error bounds), and matches
+  the oracle's epilogue applied to the GPU's own codes and scales to 1 fp16
+  ulp on all but 1e-3 of the outputs.
+
+Every case has at least 10^4 activation codes, and the oracle's integer
+products stay under ~1e8 multiply-adds per case, so the sweep runs in
+seconds.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import ref
+from tests._match import assert_codes, assert_scales, assert_y, say
+from zq_workloads import random_affine
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@dataclasses.dataclass(frozen=True)
+class Case:
+    seed: int
+    M: int
+    K: int
+    N: int
+    G: int
+    pre: int
+    act: int
+    f32: bool
+    affine: bool
+    bias: bool
+    packed: bool
+
+    def __str__(self):
+        return (f"s{self.seed}-M{self.M}-K{self.K}-N{self.N}-G{self.G}-pre{self.pre}-act{self.act}"
+                f"-{'f32' if self.f32 else 'f16'}{'-aff' if self.affine else ''}"
+                f"{'-bias' if self.bias else ''}{'-packed' if self.packed else ''}")
+
+
+def draw_cases(n: int = 48, seed: int = 20261204):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        few = i % 3 == 0
+        M = int(rng.integers(1, 33)) if few else int(rng.integers(33, 700))
+        k_lo = -(-10_000 // M // 16)                # at least 10^4 codes
+        k_hi = max(k_lo + 1, 768 if few else 320)    # K up to 12272 (few tokens) or 5104
+        K = 16 * int(rng.integers(k_lo, k_hi))
+        G = int(rng.choice([1, 4, 16, 32, 64, 128]))
+        step = int(np.lcm(G, 4))                     # N % G == 0 and N % 4 == 0
+        N = step * int(rng.integers(1, max(2, 1024 // step + 1)))
+        while M * N * K > 1e8 and N > step:
+            N -= step
+        cases.append(Case(seed=i, M=M, K=K, N=N, G=G, pre=int(rng.integers(0, 3)),
+                          act=int(rng.integers(0, 2)), f32=bool(rng.random() < 0.25),
+                          affine=bool(rng.random() < 0.5), bias=bool(rng.random() < 0.6),
+                          packed=bool(few and rng.random() < 0.5)))
+    return cases
+
+
+CASES = draw_cases()
+
+
+@pytest.fixture(scope="module")
+def zq():
+    import post_w8a8_quantized_amd as m
+    assert torch.cuda.is_available(), "a GPU device node exists but torch sees no GPU"
+    m.library()
+    return m
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def test_cases_cover_the_argument_space():
+    """The drawn cases reach every pre-op, activation, dtype and weight layout,
+    both GEMM paths, every group size, and ragged shapes."""
+    seen = lambda f: {f(c) for c in CASES}
+    assert seen(lambda c: c.pre) == {0, 1, 2}
+    assert seen(lambda c: c.act) == {0, 1}
+    assert seen(lambda c: c.f32) == {False, True}
+    assert seen(lambda c: c.packed) == {False, True}
+    assert seen(lambda c: c.M <= 32) == {False, True}
+    assert seen(lambda c: c.G) == {1, 4, 16, 32, 64, 128}
+    assert any(c.M % 128 and c.N % 128 and c.K % 128 for c in CASES)
+    assert all(c.M * c.K >= 10_000 for c in CASES)
+
+
+@pytest.mark.parametrize("case", CASES, ids=str)
+def test_layer_sweep(zq, case):
+    say("sweep", case)
+    c = case
+    rng = np.random.default_rng(1000 + c.seed)
+    dt = np.float32 if c.f32 else np.float16
+    X = (rng.standard_normal((c.M, c.K)) * np.exp(rng.standard_normal((c.M, 1)))).astype(dt)
+    W = (0.02 * rng.standard_normal((c.N, c.K)) *
+         np.exp(0.5 * rng.standard_normal((c.N, 1)))).astype(np.float32)
+    g, b = random_affine(rng, c.K) if c.affine and c.pre == ref.PRE_LAYERNORM else (None, None)
+    bias = (0.01 * rng.standard_normal(c.N)).astype(np.float32) if c.bias else None
+    eps = 1e-5
+
+    Wq, s_w = ref.quantize_groups(W, c.G)
+    Wq_d, sw_d = zq.quantize_weights_grouped(dev(W), c.G)
+    assert np.array_equal(host(Wq_d), Wq), "weight codes"
+    assert np.array_equal(host(sw_d), s_w), "weight scales"
+
+    ws = torch.zeros(zq.linear_workspace_bytes(c.M, c.K), dtype=torch.uint8, device="cuda")
+    if c.packed:
+        Y = zq.linear_w8a8_packed(dev(X), zq.pack_weights(Wq_d), sw_d, c.G, c.N, c.pre, dev(g),
+                                  dev(b), eps, dev(bias), c.act, workspace=ws)
+    else:
+        Y = zq.linear_w8a8(dev(X), Wq_d, sw_d, c.G, c.pre, dev(g), dev(b), eps, dev(bias), c.act,
+                           workspace=ws)
+    Y = host(Y)
+    w = host(ws)
+    codes = w[:c.M * c.K].view(np.int8).reshape(c.M, c.K)
+    off = (c.M * c.K + 255) // 256 * 256
+    scales = w[off:off + 4 * c.M].view(np.float32).copy()
+
+    q_ref, sx_ref = ref.prologue(X, c.pre, g, b, eps)
+    assert_codes(codes, q_ref)
+    assert_scales(scales, sx_ref)
+
+    acc_gpu = host(zq.w8a8_gemm_dequant(dev(codes), None, Wq_d, None, c.G,
+                                        out_dtype=torch.int32))
+    acc = ref.gemm_i32(codes, Wq)
+    bad = np.argwhere(acc_gpu != acc)
+    assert bad.size == 0, f"{len(bad)} accumulators differ, first at {tuple(bad[0])}"
+
+    assert_y(Y, ref.epilogue(ref.gemm_i32(q_ref, Wq), sx_ref, s_w, c.G, bias, c.act))
+    own = ref.epilogue(acc, scales, s_w, c.G, bias, c.act)
+    ulp = np.spacing(np.abs(own).astype(np.float16)).astype(np.float64)
+    off_ulp = np.abs(Y.astype(np.float64) - own.astype(np.float64)) > ulp
+    assert off_ulp.mean() <= 1e-3, f"{off_ulp.sum()} outputs beyond 1 fp16 ulp of the oracle's epilogue"
