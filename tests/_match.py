@@ -9,6 +9,8 @@
 - Per-token scales: within 4 fp32 ulps.
 - fp16 outputs: max |dY| <= 1e-2 * max |Y_ref| and normwise mean relative
   error sum |dY| / sum |Y_ref| <= 1e-3.
+- FP8 (E4M3) activation codes: the same byte, or the neighbouring code of the
+  same sign, on at most max(1, 1e-4 n) elements.
 """
 from __future__ import annotations
 
@@ -64,3 +66,14 @@ def assert_y(got: np.ndarray, want: np.ndarray, what: str = "Y"):
     assert max_rel <= 1e-2, f"{what}: max |dY| / max |Y| = {max_rel:.3e}"
     assert mean_rel <= 1e-3, f"{what}: sum |dY| / sum |Y| = {mean_rel:.3e}"
     return max_rel, mean_rel
+
+
+def assert_fp8_codes(got, want):
+    """Same byte, or the neighbouring code of the same sign (a near-tie decided
+    on a value one fp32 ulp away), on at most max(1, 1e-4 n) elements."""
+    g = np.asarray(got).astype(np.int16)
+    w = np.asarray(want).astype(np.int16)
+    off = g != w
+    same_sign = (g & 0x80) == (w & 0x80)
+    assert np.all(np.abs(g - w)[off] <= 1) and np.all(same_sign[off]), "codes differ by more than one step"
+    assert off.sum() <= max(1, int(1e-4 * g.size)), f"{off.sum()} codes differ"

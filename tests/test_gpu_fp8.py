@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from oracle import ref
-from tests._match import assert_scales, assert_y, say
+from tests._match import assert_fp8_codes, assert_scales, assert_y, say
 from zq_workloads import WORKLOADS, make_inputs, random_affine
 
 pytestmark = pytest.mark.gpu
@@ -32,17 +32,6 @@ def dev(a):
 def host(t):
     torch.cuda.synchronize()
     return t.cpu().numpy()
-
-
-def assert_fp8_codes(got, want):
-    """Same byte, or the neighbouring code of the same sign (a near-tie decided
-    on a value one fp32 ulp away), on at most max(1, 1e-4 n) elements."""
-    g = got.astype(np.int16)
-    w = want.astype(np.int16)
-    off = g != w
-    same_sign = (g & 0x80) == (w & 0x80)
-    assert np.all(np.abs(g - w)[off] <= 1) and np.all(same_sign[off]), "codes differ by more than one step"
-    assert off.sum() <= max(1, int(1e-4 * g.size)), f"{off.sum()} codes differ"
 
 
 def random_codes(rng, shape):

@@ -17,6 +17,12 @@ One call of the layer, then:
   the oracle's epilogue applied to the GPU's own codes and scales to 1 fp16
   ulp on all but 1e-3 of the outputs.
 
+The first 24 cases also run the FP8 (E4M3) layer ("探秘Transformer系列之（36）"
+ZeroQuant-FP paragraph: FP8 codes with power-of-two scales): weight codes and
+scales exact, workspace codes within one code step on near-ties, scales equal
+up to 4 ulps, Y within the output tolerance of the oracle's FP8 layer and of
+the oracle's product of the GPU's own codes.
+
 Every case has at least 10^4 activation codes, and the oracle's integer
 products stay under ~1e8 multiply-adds per case, so the sweep runs in
 seconds.
@@ -29,7 +35,7 @@ import numpy as np
 import pytest
 
 from oracle import ref
-from tests._match import assert_codes, assert_scales, assert_y, say
+from tests._match import assert_codes, assert_fp8_codes, assert_scales, assert_y, say
 from zq_workloads import random_affine
 
 pytestmark = pytest.mark.gpu
@@ -158,3 +164,38 @@ def test_layer_sweep(zq, case):
     ulp = np.spacing(np.abs(own).astype(np.float16)).astype(np.float64)
     off_ulp = np.abs(Y.astype(np.float64) - own.astype(np.float64)) > ulp
     assert off_ulp.mean() <= 1e-3, f"{off_ulp.sum()} outputs beyond 1 fp16 ulp of the oracle's epilogue"
+
+
+@pytest.mark.parametrize("case", CASES[:24], ids=str)
+def test_layer_sweep_fp8(zq, case):
+    say("sweep fp8", case)
+    c = case
+    rng = np.random.default_rng(2000 + c.seed)
+    dt = np.float32 if c.f32 else np.float16
+    X = (rng.standard_normal((c.M, c.K)) * np.exp(rng.standard_normal((c.M, 1)))).astype(dt)
+    W = (0.02 * rng.standard_normal((c.N, c.K)) *
+         np.exp(0.5 * rng.standard_normal((c.N, 1)))).astype(np.float32)
+    g, b = random_affine(rng, c.K) if c.affine and c.pre == ref.PRE_LAYERNORM else (None, None)
+    bias = (0.01 * rng.standard_normal(c.N)).astype(np.float32) if c.bias else None
+    eps = 1e-5
+
+    Wq, s_w = ref.quantize_groups_fp8(W, c.G)
+    Wq_d, sw_d = zq.quantize_weights_grouped_fp8(dev(W), c.G)
+    assert np.array_equal(host(Wq_d), Wq), "FP8 weight codes"
+    assert np.array_equal(host(sw_d), s_w), "FP8 weight scales"
+
+    ws = torch.zeros(zq.linear_workspace_bytes(c.M, c.K), dtype=torch.uint8, device="cuda")
+    W_arg = zq.pack_weights(Wq_d.view(torch.int8)).view(torch.uint8) if c.packed else Wq_d
+    Y = host(zq.linear_w8a8_fp8(dev(X), W_arg, sw_d, c.G, c.pre, dev(g), dev(b), eps, dev(bias),
+                                c.act, workspace=ws, N=c.N, packed=c.packed))
+    w = host(ws)
+    codes = w[:c.M * c.K].reshape(c.M, c.K).copy()
+    off = (c.M * c.K + 255) // 256 * 256
+    scales = w[off:off + 4 * c.M].view(np.float32).copy()
+
+    q_ref, sx_ref = ref.prologue_fp8(X, c.pre, g, b, eps)
+    assert_fp8_codes(codes, q_ref)
+    assert_scales(scales, sx_ref)
+    assert_y(Y, ref.linear_fp8(X, c.pre, g, b, eps, Wq, s_w, c.G, bias, c.act)[0])
+    assert_y(Y, ref.epilogue_f64acc(ref.gemm_fp8(codes, Wq), scales, s_w, c.G, bias, c.act),
+             "Y against the oracle's product of the GPU's codes")
