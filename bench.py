@@ -47,6 +47,7 @@ if ROOT not in sys.path:
 METRIC = "W8A8 fused linear TOPS (% int8 MFMA peak) prefill; GB/s (% HBM) decode"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+PEAK_CLOCK_MHZ = 2400.0     # the graphics clock the published MFMA peak assumes
 PRE_NAMES = {0: "none", 1: "layernorm", 2: "gelu"}
 ACT_NAMES = {0: "none", 1: "gelu"}
 
@@ -523,6 +524,15 @@ def time_layer(torch, zq, st, args, sample=False):
                                  "behind replays of the timed graph; GPU idle between the "
                                  f"step's kernels: {gap * 100:.2f}% of the steps' span")
     roofline["launch_us_p10_p50_p90"] = gemm_spread
+    # Context for a compute-bound kernel: the published peak assumes 2.4 GHz; the
+    # same peak scaled to the graphics clock amd-smi read during back-to-back
+    # steps of this layer (the chip holds its power limit there).  `frac` above
+    # stays against the published peak.
+    clk = (clock_power or {}).get("gfx_clock_MHz")
+    if not decode and clk:
+        peak_clk = PEAK_INT8_TOPS * clk / PEAK_CLOCK_MHZ
+        roofline["at_sampled_clock"] = {"gfx_clock_MHz": clk, "peak": round(peak_clk, 1),
+                                        "frac": round(g_ach / peak_clk, 4)}
     return dict(ms_step=ms_step, ms_wall=ms_wall, pro_ms=pro_ms, gemm_ms=gemm_ms, value=value,
                 nsets=nsets, clock_power=clock_power,
                 unit=unit, peak=peak, ops=ops, bytes_pro=bytes_pro, bytes_gemm=bytes_gemm,

@@ -119,13 +119,15 @@ __global__ __launch_bounds__(256) void k_transpose_to_f16(const T *__restrict__ 
     const int tx = threadIdx.x % 64;
     const int ty = threadIdx.x / 64;
 #pragma unroll
-    for (int r = ty; r < 64; r += 4) {
+    for (int i = 0; i < 16; i++) {
+        const int r = ty + 4 * i;
         const int n = n0 + r, k = k0 + tx;
         tile[r][tx] = (n < N && k < K) ? (_Float16)W[(int64_t)n * K + k] : (_Float16)0.0f;
     }
     __syncthreads();
 #pragma unroll
-    for (int r = ty; r < 64; r += 4) {
+    for (int i = 0; i < 16; i++) {
+        const int r = ty + 4 * i;
         const int k = k0 + r, n = n0 + tx;
         if (k < K && n < N)
             Wt[(int64_t)k * N + n] = tile[tx][r];
