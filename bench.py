@@ -639,6 +639,17 @@ def library_leg(torch, zq, st, args, dev):
             "int32_results_equal": equal}
 
 
+def guarded_library_leg(torch, zq, st, args, dev):
+    """library_leg, or the reason it could not run (the vendor call is context
+    only: a torch build without it, or one that rejects the shape, must not
+    cost the benchmark line)."""
+    try:
+        return library_leg(torch, zq, st, args, dev)
+    except (RuntimeError, AttributeError, TypeError) as e:
+        torch.cuda.synchronize()
+        return {"error": f"{type(e).__name__}: {e}"[:300]}
+
+
 def ablation_leg(torch, zq, st, t, args, dev):
     """The same layer in the unfused order (op -> fp16 -> quantizer -> int32 GEMM
     -> dequantizer), same rotated sets; the intermediates share one workspace."""
@@ -836,7 +847,7 @@ def main():
     fp8 = None if args.no_fp8 else fp8_leg(torch, zq, st, t, args, dev)
     libref = None
     if not st["decode"] and not args.no_library_reference:
-        libref = library_leg(torch, zq, st, args, dev)
+        libref = guarded_library_leg(torch, zq, st, args, dev)
     cpu = None if args.no_cpu_baseline else cpu_leg(zq, st, t, args)
     del st
     torch.cuda.synchronize()
@@ -862,7 +873,7 @@ def main():
             if not args.no_fp8:
                 others[name]["fp8_variant"] = fp8_leg(torch, zq, so, to, args, dev)
             if not so["decode"] and not args.no_library_reference:
-                others[name]["library_reference"] = library_leg(torch, zq, so, args, dev)
+                others[name]["library_reference"] = guarded_library_leg(torch, zq, so, args, dev)
             if name == "bert_ffn_up" and not args.no_ffn:
                 others[name]["ffn_block"] = ffn_leg(torch, zq, so, args, dev)
             if so["decode"] and not args.no_cpu_baseline:

@@ -1,6 +1,6 @@
-"""Host-side logic of bench.py, on the CPU: the one-GPU refusal and the rule that
+"""Host-side logic of bench.py, on the CPU: the one-GPU refusal, the rule that
 a committed traffic summary counts only when it was taken on the current kernel
-source."""
+source, and the vendor-GEMM comparison reporting its own failure."""
 from __future__ import annotations
 
 import os
@@ -75,3 +75,28 @@ def test_min_traffic_leaves_out_the_codes_round_trip():
     assert got["min_traffic_bytes"] == X + W + sw + Y
     assert abs(got["min_traffic_GBps"] - (X + W + sw + Y) / 40e-6 / 1e9) < 0.1
     assert bench.min_traffic(Decode, {"unit": "TOPS", "bytes_layer": layer, "ms_step": 0.04}) == {}
+
+
+def test_library_reference_failure_is_reported_not_raised(monkeypatch):
+    """The vendor-GEMM comparison is context only: if torch cannot run it, the
+    benchmark line carries the reason instead of failing."""
+    class Cuda:
+        synced = 0
+
+        @classmethod
+        def synchronize(cls):
+            cls.synced += 1
+
+    class Torch:
+        cuda = Cuda
+
+    def boom(*a, **k):
+        raise RuntimeError("_int_mm is not supported for this shape")
+
+    monkeypatch.setattr(bench, "library_leg", boom)
+    out = bench.guarded_library_leg(Torch, None, {}, None, None)
+    assert out == {"error": "RuntimeError: _int_mm is not supported for this shape"}
+    assert Cuda.synced == 1
+
+    monkeypatch.setattr(bench, "library_leg", lambda *a: {"library_int32_us": 1.0})
+    assert bench.guarded_library_leg(Torch, None, {}, None, None) == {"library_int32_us": 1.0}
