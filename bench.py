@@ -75,9 +75,9 @@ def parse():
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other workloads (BERT FFN-up, GPT QKV, decode FFN-down)")
     ap.add_argument("--no-clock-sample", action="store_true",
-                    help="skip the untimed back-to-back steps before each workload's warmup (2 s "
-                         "for the headline, during which amd-smi samples the GPU clock and power; "
-                         "0.5 s for the others); for profiler runs")
+                    help="skip the untimed back-to-back steps (2 s) before each workload's "
+                         "warmup, during which amd-smi samples the GPU clock and power; for "
+                         "profiler runs")
     ap.add_argument("--no-copy-reference", action="store_true",
                     help="skip the 1 GiB device-copy bandwidth reference")
     ap.add_argument("--no-library-reference", action="store_true",
@@ -806,6 +806,7 @@ def summary(w, t):
            "prologue_frac_of_hbm": round(t["bytes_pro"] / (t["pro_ms"] * 1e-3) / 1e9
                                          / PEAK_HBM_GBS, 4),
            "gemm_us": round(t["gemm_ms"] * 1e3, 3), "roofline": r,
+           "clock_power": t["clock_power"],
            **min_traffic(w, t),
            "config": {"M": w.M, "K": w.K, "N": w.N, "group_rows": w.group_rows,
                       "x_dtype": w.x_dtype, "pre": PRE_NAMES[w.pre], "act": ACT_NAMES[w.act],
@@ -868,7 +869,7 @@ def main():
                 continue
             wo = WORKLOADS[name]
             so = prepare(torch, zq, wo, make_inputs, args, dev)
-            to = time_layer(torch, zq, so, args)
+            to = time_layer(torch, zq, so, args, sample=not args.no_clock_sample)
             others[name] = summary(wo, to)
             if not args.no_fp8:
                 others[name]["fp8_variant"] = fp8_leg(torch, zq, so, to, args, dev)
