@@ -23,6 +23,12 @@ scales exact, workspace codes within one code step on near-ties, scales equal
 up to 4 ulps, Y within the output tolerance of the oracle's FP8 layer and of
 the oracle's product of the GPU's own codes.
 
+The first 20 cases also run the mixed-precision decomposition ("探秘Transformer
+系列之（36）" 1.1, LLM.int8(): input channels whose |y| exceeds alpha stay in
+fp16, the rest W8A8) on inputs with a seeded set of amplified channels, with
+alpha = 6.0 or the nearest listed value that no column maximum sits on: Y
+within the output tolerance of the oracle's decomposed layer.
+
 Every case has at least 10^4 activation codes, and the oracle's integer
 products stay under ~1e8 multiply-adds per case, so the sweep runs in
 seconds.
@@ -36,7 +42,7 @@ import pytest
 
 from oracle import ref
 from tests._match import assert_codes, assert_fp8_codes, assert_scales, assert_y, say
-from zq_workloads import random_affine
+from zq_workloads import Workload, make_inputs, random_affine
 
 pytestmark = pytest.mark.gpu
 
@@ -199,3 +205,32 @@ def test_layer_sweep_fp8(zq, case):
     assert_y(Y, ref.linear_fp8(X, c.pre, g, b, eps, Wq, s_w, c.G, bias, c.act)[0])
     assert_y(Y, ref.epilogue_f64acc(ref.gemm_fp8(codes, Wq), scales, s_w, c.G, bias, c.act),
              "Y against the oracle's product of the GPU's codes")
+
+
+DECOMP_ALPHAS = (6.0, 6.5, 5.5, 7.0, 5.0, 7.5)
+
+
+@pytest.mark.parametrize("case", CASES[:20], ids=str)
+def test_layer_sweep_decomp(zq, case):
+    say("sweep decomp", case)
+    c = case
+    rng = np.random.default_rng(3000 + c.seed)
+    frac = min(float(rng.choice([0.002, 0.005, 0.01, 0.02])), 64 / c.K)
+    gain = float(rng.choice([8.0, 30.0, 100.0]))
+    w = Workload("sweep_decomp", c.M, c.K, c.N, c.G, "f32" if c.f32 else "f16", c.pre, c.act,
+                 c.bias, 0.3, 0.02, 0.0, max(frac, 1.0 / c.K), gain, False, seed=3000 + c.seed)
+    inp = make_inputs(w)
+    # The outlier test |y| > alpha is decided on fp32 y, whose last bits differ
+    # between the two sides: take the first alpha (6.0 is LLM.int8()'s) that no
+    # column maximum lies within 1e-4 of, so that the set is unambiguous.
+    colmax = np.max(np.abs(ref.preop(inp.X, c.pre).astype(np.float64)), axis=0)
+    alpha = next(a for a in DECOMP_ALPHAS if not np.any(np.abs(colmax - a) <= 1e-4 * a))
+    Wq_r, s_w_r = ref.quantize_groups(inp.W, c.G)
+    want, _, _, cols = ref.linear_decomp(inp.X, c.pre, None, None, 1e-5, alpha, Wq_r,
+                                         s_w_r, c.G, inp.W, inp.bias, c.act)
+    assert cols.size > 0
+    Wd = dev(inp.W)
+    Wq, s_w = zq.quantize_weights_grouped(Wd, c.G)
+    got = zq.linear_w8a8_decomp(dev(inp.X), Wq, s_w, c.G, zq.pack_outlier_weights(Wd),
+                                alpha, c.pre, bias=dev(inp.bias), act=c.act)
+    assert_y(host(got), want)
