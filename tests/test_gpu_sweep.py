@@ -29,6 +29,13 @@ fp16, the rest W8A8) on inputs with a seeded set of amplified channels, with
 alpha = 6.0 or the nearest listed value that no column maximum sits on: Y
 within the output tolerance of the oracle's decomposed layer.
 
+The first 16 cases also run the chained FFN block (the case's K as the model
+width, its N rounded up as the hidden width; bit-identical to two layer calls,
+and against the oracle's chain) and the unfused order (the ZeroQuant reading
+notes' flow before fusion: its codes equal the oracle's quantizer on the GPU's
+own fp16 tensor, its int32 accumulators are exact, its output has the fused
+epilogue's bits for the same codes, and it matches the oracle's unfused layer).
+
 Every case has at least 10^4 activation codes, and the oracle's integer
 products stay under ~1e8 multiply-adds per case, so the sweep runs in
 seconds.
@@ -234,3 +241,73 @@ def test_layer_sweep_decomp(zq, case):
     got = zq.linear_w8a8_decomp(dev(inp.X), Wq, s_w, c.G, zq.pack_outlier_weights(Wd),
                                 alpha, c.pre, bias=dev(inp.bias), act=c.act)
     assert_y(host(got), want)
+
+
+def r256(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("case", CASES[:16], ids=str)
+def test_ffn_sweep(zq, case):
+    say("sweep ffn", case)
+    c = case
+    rng = np.random.default_rng(4000 + c.seed)
+    K = c.K
+    F = -(-c.N // int(np.lcm(c.G, 16))) * int(np.lcm(c.G, 16))   # F % G1 == 0, F % 16 == 0
+    while c.M * F * K > 5e7 and K > 16:
+        K = max(16, K // 2 // 16 * 16)
+    G1, G2 = c.G, 16
+    dt = np.float32 if c.f32 else np.float16
+    X = (rng.standard_normal((c.M, K)) * np.exp(rng.standard_normal((c.M, 1)))).astype(dt)
+    g, b = random_affine(rng, K)
+    W1 = (0.02 * rng.standard_normal((F, K))).astype(np.float32)
+    W2 = (0.02 * rng.standard_normal((K, F))).astype(np.float32)
+    b1 = (0.01 * rng.standard_normal(F)).astype(np.float32)
+    b2 = (0.01 * rng.standard_normal(K)).astype(np.float32)
+    W1q, s1 = zq.quantize_weights_grouped(dev(W1), G1)
+    W2q, s2 = zq.quantize_weights_grouped(dev(W2), G2)
+    Xd, gd, bd, b1d, b2d = dev(X), dev(g), dev(b), dev(b1), dev(b2)
+    ws = torch.zeros(zq.ffn_workspace_bytes(c.M, K, F), dtype=torch.uint8, device="cuda")
+    Y = host(zq.ffn_w8a8(Xd, W1q, s1, G1, W2q, s2, G2, gd, bd, 1e-5, b1d, b2d, workspace=ws))
+    H2 = zq.linear_w8a8(Xd, W1q, s1, G1, zq.PRE_LAYERNORM, gd, bd, 1e-5, b1d, zq.ACT_GELU)
+    Y2 = host(zq.linear_w8a8(H2, W2q, s2, G2, zq.PRE_NONE, None, None, 1e-5, b2d, zq.ACT_NONE))
+    assert np.array_equal(Y.view(np.uint16), Y2.view(np.uint16)), "chain != two layer calls"
+    W1q_h, s1_h, W2q_h, s2_h = host(W1q), host(s1), host(W2q), host(s2)
+    H_ref = ref.linear(X, ref.PRE_LAYERNORM, g, b, 1e-5, W1q_h, s1_h, G1, b1, ref.ACT_GELU)[0]
+    Y_ref = ref.linear(H_ref, ref.PRE_NONE, None, None, 1e-5, W2q_h, s2_h, G2, b2,
+                       ref.ACT_NONE)[0]
+    assert_y(Y, Y_ref)
+
+
+@pytest.mark.parametrize("case", CASES[:16], ids=str)
+def test_unfused_sweep(zq, case):
+    say("sweep unfused", case)
+    c = case
+    rng = np.random.default_rng(5000 + c.seed)
+    dt = np.float32 if c.f32 else np.float16
+    X = (rng.standard_normal((c.M, c.K)) * np.exp(rng.standard_normal((c.M, 1)))).astype(dt)
+    g, b = random_affine(rng, c.K) if c.affine and c.pre == ref.PRE_LAYERNORM else (None, None)
+    W = (0.02 * rng.standard_normal((c.N, c.K))).astype(np.float32)
+    bias = (0.01 * rng.standard_normal(c.N)).astype(np.float32) if c.bias else None
+    Wq, s_w = ref.quantize_groups(W, c.G)
+    M, N, K = c.M, c.N, c.K
+    ws = torch.zeros(zq.linear_unfused_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    Y = host(zq.linear_w8a8_unfused(dev(X), dev(Wq), dev(s_w), c.G, c.pre, dev(g), dev(b), 1e-5,
+                                    dev(bias), c.act, workspace=ws))
+    w = host(ws)
+    o = 0
+    y16 = w[o:o + 2 * M * K].view(np.float16).reshape(M, K)
+    o += r256(2 * M * K)
+    q = w[o:o + M * K].view(np.int8).reshape(M, K)
+    o += r256(M * K)
+    sx = w[o:o + 4 * M].view(np.float32).copy()
+    o += r256(4 * M)
+    acc = w[o:o + 4 * M * N].view(np.int32).reshape(M, N)
+    q_own, s_own = ref.quantize_rows(y16.astype(np.float32))
+    assert_codes(q, q_own, exact=True)
+    assert np.array_equal(sx, s_own)
+    assert np.array_equal(acc, ref.gemm_i32(q, Wq))
+    Yf = host(zq.w8a8_gemm_dequant(dev(q), dev(sx), dev(Wq), dev(s_w), c.G, dev(bias), c.act))
+    assert np.array_equal(Y.view(np.uint16), Yf.view(np.uint16)), "unfused != fused epilogue"
+    q_ref, s_ref = ref.unfused_prologue(X, c.pre, g, b, 1e-5)
+    assert_y(Y, ref.epilogue(ref.gemm_i32(q_ref, Wq), s_ref, s_w, c.G, bias, c.act))
