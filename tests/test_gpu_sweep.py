@@ -51,8 +51,6 @@ from oracle import ref
 from tests._match import assert_codes, assert_fp8_codes, assert_scales, assert_y, say
 from zq_workloads import Workload, make_inputs, random_affine
 
-pytestmark = pytest.mark.gpu
-
 torch = pytest.importorskip("torch")
 
 
@@ -119,7 +117,7 @@ def host(t):
 
 def test_cases_cover_the_argument_space():
     """The drawn cases reach every pre-op, activation, dtype and weight layout,
-    both GEMM paths, every group size, and ragged shapes."""
+    both GEMM paths, every group size, and ragged shapes (no GPU needed)."""
     seen = lambda f: {f(c) for c in CASES}
     assert seen(lambda c: c.pre) == {0, 1, 2}
     assert seen(lambda c: c.act) == {0, 1}
@@ -131,6 +129,7 @@ def test_cases_cover_the_argument_space():
     assert all(c.M * c.K >= 10_000 for c in CASES)
 
 
+@pytest.mark.gpu
 @pytest.mark.parametrize("case", CASES, ids=str)
 def test_layer_sweep(zq, case):
     say("sweep", case)
@@ -179,6 +178,7 @@ def test_layer_sweep(zq, case):
     assert off_ulp.mean() <= 1e-3, f"{off_ulp.sum()} outputs beyond 1 fp16 ulp of the oracle's epilogue"
 
 
+@pytest.mark.gpu
 @pytest.mark.parametrize("case", CASES[:24], ids=str)
 def test_layer_sweep_fp8(zq, case):
     say("sweep fp8", case)
@@ -217,6 +217,7 @@ def test_layer_sweep_fp8(zq, case):
 DECOMP_ALPHAS = (6.0, 6.5, 5.5, 7.0, 5.0, 7.5)
 
 
+@pytest.mark.gpu
 @pytest.mark.parametrize("case", CASES[:20], ids=str)
 def test_layer_sweep_decomp(zq, case):
     say("sweep decomp", case)
@@ -247,6 +248,7 @@ def r256(v):
     return (v + 255) // 256 * 256
 
 
+@pytest.mark.gpu
 @pytest.mark.parametrize("case", CASES[:16], ids=str)
 def test_ffn_sweep(zq, case):
     say("sweep ffn", case)
@@ -279,6 +281,7 @@ def test_ffn_sweep(zq, case):
     assert_y(Y, Y_ref)
 
 
+@pytest.mark.gpu
 @pytest.mark.parametrize("case", CASES[:16], ids=str)
 def test_unfused_sweep(zq, case):
     say("sweep unfused", case)
